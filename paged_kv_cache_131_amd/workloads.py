@@ -1,0 +1,325 @@
+"""Seeded synthetic inputs for paged decode attention.
+
+This module holds no attention arithmetic: it draws random numbers, rounds
+them to the stored element type, places sequences into a shuffled block pool
+and poisons every slot the decode must not read with NaN. The same arrays feed
+both the CPU oracle (in tests) and the device library.
+
+Recipe per workload k (seed 1000 + k): numpy.random.SeedSequence(seed) spawns
+six streams, used in this order: lengths, pool permutation, q, K pool, V pool,
+new-token K/V. Values are float32 standard normals times `value_scale`,
+rounded to nearest-even into the stored type. Pools hold 10% more blocks than
+the sequences need (the tiny workload has a fixed pool of 32) and hand them out
+in the order of a seeded permutation, as on-demand allocation from a shuffled
+free pool would.
+
+Stored element types: "f32" -> float32, "f16" -> float16, "bf16" -> uint16
+holding the raw bfloat16 bits.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from .block_manager import BlockManager
+
+STORED_DTYPE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
+ELEMENT_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+# quiet NaNs with a payload, so that bit-exact copies can be told apart from
+# re-generated NaNs
+POISON_BITS = {"f32": 0x7FC00123, "f16": 0x7E23, "bf16": 0x7FC3}
+_SLICE = 1 << 22  # values drawn per slice (bounds temporary memory)
+
+
+def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (nearest, ties to even); returns raw bits.
+    Inputs are finite."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def round_to(x: np.ndarray, etype: str) -> np.ndarray:
+    if etype == "f32":
+        return np.asarray(x, dtype=np.float32)
+    if etype == "f16":
+        return np.asarray(x, dtype=np.float32).astype(np.float16)
+    if etype == "bf16":
+        return bf16_bits_from_f32(x)
+    raise ValueError(etype)
+
+
+def poison_value(etype: str):
+    bits = POISON_BITS[etype]
+    if etype == "f32":
+        return np.array([bits], dtype=np.uint32).view(np.float32)[0]
+    if etype == "f16":
+        return np.array([bits], dtype=np.uint16).view(np.float16)[0]
+    return np.uint16(bits)
+
+
+def random_stored(rng: np.random.Generator, shape, etype: str, value_scale: float) -> np.ndarray:
+    """Standard normals * value_scale rounded to `etype`, drawn slice by slice."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=STORED_DTYPE[etype])
+    for lo in range(0, n, _SLICE):
+        hi = min(n, lo + _SLICE)
+        x = rng.standard_normal(hi - lo, dtype=np.float32)
+        if value_scale != 1.0:
+            x *= np.float32(value_scale)
+        out[lo:hi] = round_to(x, etype)
+    return out.reshape(shape)
+
+
+@dataclass(frozen=True)
+class DecodeConfig:
+    name: str
+    index: int                 # seed = 1000 + index
+    num_seqs: int
+    num_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    etype: str
+    value_scale: float
+    lengths: tuple             # ("fixed", values) | ("uniform", lo, hi) | ("lognormal", median, sigma, lo, hi)
+    max_len: int               # upper bound of the length law: sizes block tables
+    pool_blocks: int = 0       # 0 = ceil(1.1 * blocks needed)
+    partition_size: int = -1   # -1 = balanced split chosen by the library
+
+    @property
+    def group(self) -> int:
+        return self.num_heads // self.num_kv_heads
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+
+CONFIGS = {
+    "tiny": DecodeConfig("tiny", 1, 4, 2, 2, 64, 16, "f32", 1.0,
+                         ("fixed", (5, 17, 33, 64)), 64, pool_blocks=32),
+    "opt13b": DecodeConfig("opt13b", 2, 64, 40, 40, 128, 16, "f16", 0.5,
+                           ("uniform", 128, 2048), 2048),
+    "llama3_8b": DecodeConfig("llama3_8b", 3, 256, 32, 8, 128, 16, "bf16", 1.0,
+                              ("lognormal", 800.0, 1.0, 16, 8192), 8192),
+    "long_context": DecodeConfig("long_context", 5, 16, 64, 8, 128, 32, "bf16", 1.0,
+                                 ("uniform", 32768, 131072), 131072, partition_size=512),
+}
+
+
+def draw_lengths(cfg: DecodeConfig, rng: np.random.Generator) -> np.ndarray:
+    kind = cfg.lengths[0]
+    if kind == "fixed":
+        lens = np.array(cfg.lengths[1], dtype=np.int64)
+    elif kind == "uniform":
+        lens = rng.integers(cfg.lengths[1], cfg.lengths[2] + 1, size=cfg.num_seqs)
+    elif kind == "lognormal":
+        median, sigma, lo, hi = cfg.lengths[1:]
+        lens = np.rint(np.exp(rng.normal(math.log(median), sigma, size=cfg.num_seqs)))
+        lens = np.clip(lens, lo, hi)
+    else:
+        raise ValueError(kind)
+    return lens.astype(np.int32)
+
+
+@dataclass
+class DecodeWorkload:
+    """One decode step's inputs. `k_cache`/`v_cache` hold the context's first
+    L-1 tokens; the new token (position L-1) arrives in `k_new`/`v_new` and is
+    stored at `slot_mapping` before the decode reads it."""
+    cfg: DecodeConfig
+    q: np.ndarray
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    block_tables: np.ndarray
+    context_lens: np.ndarray
+    k_new: np.ndarray
+    v_new: np.ndarray
+    slot_mapping: np.ndarray
+    num_blocks: int
+    poison_block: int
+    used_blocks: np.ndarray = field(default=None)
+
+    @property
+    def etype(self):
+        return self.cfg.etype
+
+    @property
+    def max_blocks_per_seq(self):
+        return self.block_tables.shape[1]
+
+    @property
+    def max_context_len(self):
+        return int(self.context_lens.max())
+
+    def kv_bytes(self) -> int:
+        c = self.cfg
+        return int(self.context_lens.astype(np.int64).sum()) * c.num_kv_heads * c.head_dim * 2 * ELEMENT_BYTES[c.etype]
+
+
+def make_decode_workload(cfg: DecodeConfig, lengths=None, poison: bool = True,
+                         values: bool = True) -> DecodeWorkload:
+    """Draw one decode step's inputs. With values=False only the integer
+    inputs (lengths, block tables, slot mapping) are produced."""
+    streams = [np.random.default_rng(s) for s in np.random.SeedSequence(1000 + cfg.index).spawn(6)]
+    rng_len, rng_pool, rng_q, rng_k, rng_v, rng_new = streams
+    lens = draw_lengths(cfg, rng_len) if lengths is None else np.asarray(lengths, dtype=np.int32)
+    if lens.shape != (cfg.num_seqs,) or lens.min() < 1:
+        raise ValueError("one positive length per sequence is required")
+    B = cfg.block_size
+    nblk = -(-lens.astype(np.int64) // B)
+    need = int(nblk.sum())
+    num_blocks = cfg.pool_blocks if cfg.pool_blocks else math.ceil(1.1 * need)
+    if num_blocks <= need:
+        raise ValueError("pool too small to leave a spare block for poisoned padding")
+    perm = rng_pool.permutation(num_blocks).astype(np.int32)
+    max_blocks = max(-(-cfg.max_len // B), int(nblk.max()))
+    poison_block = int(perm[need])             # first block never handed out
+    tables = np.full((cfg.num_seqs, max_blocks), poison_block, dtype=np.int32)
+    pos = 0
+    for s in range(cfg.num_seqs):
+        tables[s, :nblk[s]] = perm[pos:pos + nblk[s]]
+        pos += int(nblk[s])
+
+    Hkv, d = cfg.num_kv_heads, cfg.head_dim
+    used = perm[:need]
+    last_pos = lens.astype(np.int64) - 1
+    slots = (tables[np.arange(cfg.num_seqs), last_pos // B].astype(np.int64) * B + last_pos % B).astype(np.int32)
+    if not values:
+        return DecodeWorkload(cfg, None, None, None, tables, lens.copy(), None, None, slots,
+                              num_blocks, poison_block, used)
+    q = random_stored(rng_q, (cfg.num_seqs, cfg.num_heads, d), cfg.etype, cfg.value_scale)
+    k_cache = random_stored(rng_k, (num_blocks, Hkv, B, d), cfg.etype, cfg.value_scale)
+    v_cache = random_stored(rng_v, (num_blocks, Hkv, d, B), cfg.etype, cfg.value_scale)
+    k_new = random_stored(rng_new, (cfg.num_seqs, Hkv, d), cfg.etype, cfg.value_scale)
+    v_new = random_stored(rng_new, (cfg.num_seqs, Hkv, d), cfg.etype, cfg.value_scale)
+
+    if poison:
+        pv = poison_value(cfg.etype)
+        unused = perm[need:]
+        k_cache[unused] = pv
+        v_cache[unused] = pv
+        for s in range(cfg.num_seqs):
+            last = tables[s, nblk[s] - 1]
+            off = (int(lens[s]) - 1) % B          # the new token's slot and the rest
+            k_cache[last, :, off:, :] = pv
+            v_cache[last, :, :, off:] = pv
+    return DecodeWorkload(cfg, q, k_cache, v_cache, tables, lens.copy(), k_new, v_new,
+                          slots, num_blocks, poison_block, used)
+
+
+# --------------------------------------------------------------------------
+# Parallel sampling with a shared prompt (32 prompts x 8 samples).
+# --------------------------------------------------------------------------
+
+PARALLEL_SAMPLING = DecodeConfig("parallel_sampling", 4, 256, 32, 8, 128, 16, "bf16", 1.0,
+                                 ("fixed", ()), 1024 + 256)
+
+
+@dataclass
+class SamplingStep:
+    step: int
+    block_mapping: np.ndarray     # [num_pairs][2] int32 (src, dst), applied before the write
+    slot_mapping: np.ndarray      # [num_seqs] int32
+    k_new: np.ndarray
+    v_new: np.ndarray
+    q: np.ndarray
+    block_tables: np.ndarray      # [num_seqs][max_blocks] int32
+    context_lens: np.ndarray      # [num_seqs] int32 (after this step's token)
+
+
+class ParallelSamplingWorkload:
+    """Prompts are prefilled once, then every prompt is forked into
+    `samples` sequences sharing its blocks; each step appends one token per
+    sample through the block manager (copy-on-write of a shared partial
+    block, on-demand allocation otherwise)."""
+
+    def __init__(self, prompt_len: int = 1024, num_prompts: int = 32, samples: int = 8,
+                 new_tokens: int = 256, cfg: DecodeConfig = PARALLEL_SAMPLING, poison: bool = True,
+                 values: bool = True):
+        self.cfg = cfg
+        self.prompt_len, self.num_prompts, self.samples, self.new_tokens = prompt_len, num_prompts, samples, new_tokens
+        self.values = values
+        streams = [np.random.default_rng(s) for s in np.random.SeedSequence(1000 + cfg.index).spawn(6)]
+        _, rng_pool, self.rng_q, rng_k, rng_v, self.rng_new = streams
+        B = cfg.block_size
+        used = self._dry_run_blocks()
+        self.num_blocks = math.ceil(1.1 * used)
+        perm = rng_pool.permutation(self.num_blocks)
+        self.bm = BlockManager(self.num_blocks, B, free_order=perm)
+        self.max_blocks = -(-(prompt_len + new_tokens) // B)
+        Hkv, d = cfg.num_kv_heads, cfg.head_dim
+        self.k_cache = self.v_cache = None
+        if values:
+            self.k_cache = random_stored(rng_k, (self.num_blocks, Hkv, B, d), cfg.etype, cfg.value_scale)
+            self.v_cache = random_stored(rng_v, (self.num_blocks, Hkv, d, B), cfg.etype, cfg.value_scale)
+        self.seqs = []
+        prompt_blocks = []
+        for _ in range(num_prompts):
+            parent = self.bm.new_sequence()
+            for _ in range(prompt_len):
+                self.bm.append_token(parent)
+            prompt_blocks.extend(parent.block_table)
+            self.seqs.append(parent)
+            for _ in range(samples - 1):
+                self.seqs.append(self.bm.fork(parent))
+        # order: prompt-major, sample index ascending (parent is sample 0)
+        self.seqs = [self.seqs[p * samples + i] for p in range(num_prompts) for i in range(samples)]
+        self.poison_block = int(self.bm.free[-1])   # handed out last, if ever
+        if poison and values:
+            pv = poison_value(cfg.etype)
+            held = np.zeros(self.num_blocks, dtype=bool)
+            held[prompt_blocks] = True
+            self.k_cache[~held] = pv
+            self.v_cache[~held] = pv
+            tail = prompt_len % B
+            if tail:
+                for p in range(num_prompts):
+                    last = self.seqs[p * samples].block_table[-1]
+                    self.k_cache[last, :, tail:, :] = pv
+                    self.v_cache[last, :, :, tail:] = pv
+        self.step_index = 0
+
+    def _dry_run_blocks(self) -> int:
+        B = self.cfg.block_size
+        prompt = -(-self.prompt_len // B)
+        own_tokens_first_block = 0 if self.prompt_len % B == 0 else B - self.prompt_len % B
+        per_sample_new = -(-max(0, self.new_tokens - own_tokens_first_block) // B)
+        copies = (self.samples - 1) if (self.prompt_len % B and self.new_tokens) else 0
+        return self.num_prompts * (prompt + copies + self.samples * per_sample_new)
+
+    @property
+    def num_seqs(self):
+        return self.num_prompts * self.samples
+
+    def step(self) -> SamplingStep:
+        if self.step_index >= self.new_tokens:
+            raise StopIteration
+        self.step_index += 1
+        cfg = self.cfg
+        slots, pairs = [], []
+        for seq in self.seqs:
+            slot, copy = self.bm.append_token(seq)
+            slots.append(slot)
+            if copy is not None:
+                pairs.append(copy)
+        S, Hkv, d = self.num_seqs, cfg.num_kv_heads, cfg.head_dim
+        q = k_new = v_new = None
+        if self.values:
+            q = random_stored(self.rng_q, (S, cfg.num_heads, d), cfg.etype, cfg.value_scale)
+            k_new = random_stored(self.rng_new, (S, Hkv, d), cfg.etype, cfg.value_scale)
+            v_new = random_stored(self.rng_new, (S, Hkv, d), cfg.etype, cfg.value_scale)
+        tables = np.full((S, self.max_blocks), self.poison_block, dtype=np.int32)
+        for i, seq in enumerate(self.seqs):
+            tables[i, :len(seq.block_table)] = seq.block_table
+        lens = np.array([seq.num_tokens for seq in self.seqs], dtype=np.int32)
+        mapping = np.array(pairs, dtype=np.int32).reshape(-1, 2)
+        return SamplingStep(self.step_index, mapping, np.array(slots, dtype=np.int32),
+                            k_new, v_new, q, tables, lens)
+
+    def unique_blocks(self) -> int:
+        return self.num_blocks - self.bm.num_free

@@ -1,0 +1,359 @@
+"""Pins of the CPU oracle to things other than itself: worked examples printed
+on the pages (tests/golden/), a library attention routine on contiguous data,
+closed forms, brute force and invariants. CPU only."""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.paged_attention import translate
+from paged_kv_cache_131_amd.block_manager import BlockManager
+from paged_kv_cache_131_amd import workloads as wl
+
+
+def load(golden_dir, name):
+    with open(os.path.join(golden_dir, name), encoding="utf-8") as f:
+        return json.load(f)
+
+
+def nan_pool(num_blocks, kv_heads, block_size, head_dim, dtype=np.float32):
+    k = np.full((num_blocks, kv_heads, block_size, head_dim), np.nan, dtype=dtype)
+    v = np.full((num_blocks, kv_heads, head_dim, block_size), np.nan, dtype=dtype)
+    return k, v
+
+
+def token_rows(token_indices, kv_heads, head_dim):
+    """Row n carries the value 100*(token+1) + head + dim/1000 everywhere, so
+    any misplaced element is identifiable."""
+    rows = np.empty((len(token_indices), kv_heads, head_dim), dtype=np.float32)
+    for n, t in enumerate(token_indices):
+        for h in range(kv_heads):
+            rows[n, h] = 100.0 * (t + 1) + h + np.arange(head_dim) / 1000.0
+    return rows
+
+
+# ----------------------------------------------------------------------------
+# Worked examples (addressing, allocation, write layout)
+# ----------------------------------------------------------------------------
+
+def test_request_a_translation(golden_dir):
+    g = load(golden_dir, "request_a_block_table.json")
+    B, table = g["block_size"], g["block_table"]
+    assert math.ceil(g["num_tokens"] / B) == g["blocks_needed"]
+    for lb, (lo, hi) in enumerate(g["logical_block_token_ranges"]):
+        for t in range(lo, hi + 1):
+            phys, off = translate(table, t, B)
+            assert phys == table[lb] and off == t - lo
+    for t in g["fifth_token"]["indices"]:
+        assert t // B == g["fifth_token"]["logical_block"]
+        assert translate(table, t, B)[0] == g["fifth_token"]["physical_block"]
+
+
+def test_r1_allocation_and_write_layout(golden_dir):
+    g = load(golden_dir, "r1_allocation.json")
+    B = g["block_size"]
+    pool = g["free_pool"]
+    order = pool + [b for b in range(max(pool) + 1) if b not in pool]
+    bm = BlockManager(len(order), B, free_order=order)
+    seq = bm.new_sequence()
+    slots = [bm.append_token(seq)[0] for _ in range(g["prompt_tokens"])]
+    assert seq.block_table == g["table_after_prefill"]
+    assert [divmod(s, B) for s in slots] == [tuple(x) for x in g["prefill_slots"]]
+    for step in g["decode_tokens"]:
+        before = len(seq.block_table)
+        slot, copy = bm.append_token(seq)
+        assert copy is None
+        assert divmod(slot, B) == (step["physical_block"], step["offset"])
+        assert (len(seq.block_table) > before) == step["new_block"]
+        slots.append(slot)
+    assert seq.block_table == g["table_after_decode"]
+
+    # the write oracle puts each token where the pseudocode's write_kv does,
+    # and the gather reads them back in logical order
+    H, d = 2, 8
+    k, v = nan_pool(len(order), H, B, d)
+    rows = token_rows(range(len(slots)), H, d)
+    k, v = oracle.write_kv(k, v, rows, rows * -1, np.array(slots), B)
+    for t, slot in enumerate(slots):
+        phys, off = divmod(slot, B)
+        np.testing.assert_array_equal(k[phys, :, off, :], rows[t])
+        np.testing.assert_array_equal(v[phys, :, :, off], -rows[t])
+    written = np.zeros(k.shape[:3], dtype=bool)
+    for slot in slots:
+        written[slot // B, :, slot % B] = True
+    assert np.isnan(k[~written]).all() and np.isnan(np.moveaxis(v, 3, 2)[~written]).all()
+    for h in range(H):
+        keys, vals = oracle.gather_sequence(k, v, seq.block_table, len(slots), h, B, "f32")
+        np.testing.assert_array_equal(keys, rows[:, h, :].astype(np.float64))
+        np.testing.assert_array_equal(vals, -rows[:, h, :].astype(np.float64))
+
+    for blk in g["returned_on_finish"]:
+        assert blk not in bm.free
+    bm.free_sequence(seq)
+    assert all(blk in bm.free for blk in g["returned_on_finish"])
+
+
+def test_figure6_decode_sequence(golden_dir):
+    g = load(golden_dir, "figure6_decode.json")
+    B = g["block_size"]
+    order = [7, 1, 3] + [b for b in range(8) if b not in (7, 1, 3)]
+    bm = BlockManager(8, B, free_order=order)
+    seq = bm.new_sequence()
+    slots = [bm.append_token(seq)[0] for _ in range(g["prompt_tokens"])]
+    assert seq.block_table == g["prompt_table"]
+    for blk, toks in g["tokens_in_block"].items():
+        assert [t for t, s in enumerate(slots) if s // B == int(blk)] == toks
+    for key in ("decode_1", "decode_2"):
+        slot, _ = bm.append_token(seq)
+        assert seq.num_tokens - 1 == g[key]["token_index"]
+        assert divmod(slot, B) == (g[key]["physical_block"], g[key]["offset"])
+    assert seq.block_table == g["table_after_decode_2"]
+
+
+def test_block_accounting(golden_dir):
+    g = load(golden_dir, "block_accounting.json")
+    w = g["waste"]
+    bm = BlockManager(64, w["block_size"])
+    seq = bm.new_sequence()
+    for _ in range(w["tokens"]):
+        bm.append_token(seq)
+    assert len(seq.block_table) == w["blocks"]
+    assert w["tokens"] - (w["blocks"] - 1) * w["block_size"] == w["last_block_used"]
+    assert w["blocks"] * w["block_size"] - w["tokens"] == w["last_block_empty"] <= w["max_waste"] == w["block_size"] - 1
+    r = g["reservation"]
+    per = math.ceil(r["avg_len"] / r["block_size"])
+    assert per == r["blocks_per_request"] and per * r["block_size"] == r["units_per_request"]
+    assert r["requests"] * per * r["block_size"] == r["paged_reserved"]
+    assert r["requests"] * r["avg_len"] == r["used"]
+    assert r["requests"] * r["max_len"] == r["contiguous_reserved"]
+    kv = g["kv_size"]
+    assert 2 * kv["hidden"] * kv["layers"] * kv["bytes_per_element"] == kv["bytes_per_token"] == 800 * 1024
+    assert kv["bytes_per_token"] * kv["max_len"] == kv["bytes_per_max_request"]
+
+
+def test_cow_sequence(golden_dir):
+    g = load(golden_dir, "cow_sequence.json")
+    B = g["block_size"]
+    order = g["free_pool"] + [b for b in range(10) if b not in g["free_pool"]]
+    bm = BlockManager(10, B, free_order=order)
+    a1 = bm.new_sequence()
+    for _ in range(g["prompt_tokens"]):
+        bm.append_token(a1)
+    assert a1.block_table == g["prompt_table"]
+    a2 = bm.fork(a1)
+    assert {str(b): bm.refcount[b] for b in a1.block_table} == g["refcounts_after_fork"]
+
+    H, d = 1, 4
+    k, v = nan_pool(10, H, B, d)
+    rows = token_rows(range(g["prompt_tokens"]), H, d)
+    k, v = oracle.write_kv(k, v, rows, rows, np.array([bm.slot_of(a1, t) for t in range(7)]), B)
+
+    slot, copy = bm.append_token(a1)
+    exp = g["a1_write"]
+    assert list(copy) == exp["copy"]
+    assert divmod(slot, B) == (exp["slot_block"], exp["offset"])
+    assert bm.refcount[exp["copy"][0]] == exp["refcount_of_1_after"]
+    k2, v2 = oracle.copy_blocks(k, v, np.array([copy]))
+    np.testing.assert_array_equal(k2[copy[1]], k[copy[0]])
+    np.testing.assert_array_equal(v2[copy[1]], v[copy[0]])
+    untouched = [b for b in range(10) if b != copy[1]]
+    np.testing.assert_array_equal(k2[untouched], k[untouched])
+
+    slot2, copy2 = bm.append_token(a2)
+    assert copy2 is None and divmod(slot2, B) == (g["a2_write"]["slot_block"], g["a2_write"]["offset"])
+    assert a1.block_table == g["a1_table"] and a2.block_table == g["a2_table"]
+
+    # shared prefix: three tables naming one physical block hold one copy
+    sp = g["shared_prefix"]
+    bm3 = BlockManager(40, 4, free_order=[sp["physical_block"]] + [b for b in range(40) if b != sp["physical_block"]])
+    a = bm3.new_sequence()
+    for _ in range(4):
+        bm3.append_token(a)
+    others = [bm3.fork(a) for _ in sp["requests"][1:]]
+    assert all(o.block_table[sp["logical_block"]] == sp["physical_block"] for o in [a] + others)
+    assert bm3.refcount[sp["physical_block"]] == len(sp["requests"])
+
+
+# ----------------------------------------------------------------------------
+# Decode: library routine on contiguous data, closed forms, brute force
+# ----------------------------------------------------------------------------
+
+def paged_from_contiguous(keys, values, block_size, rng, num_blocks=None):
+    """Scatter per-sequence contiguous [L][Hkv][d] K/V into a randomly permuted
+    pool (test-side construction, independent of the oracle's gather)."""
+    Hkv, d = keys[0].shape[1], keys[0].shape[2]
+    need = [-(-k.shape[0] // block_size) for k in keys]
+    nb = num_blocks or sum(need) + 3
+    perm = rng.permutation(nb)
+    kc, vc = nan_pool(nb, Hkv, block_size, d, dtype=np.float64)
+    tables = np.full((len(keys), max(need)), perm[-1], dtype=np.int32)
+    pos = 0
+    for s, (K, V) in enumerate(zip(keys, values)):
+        blocks = perm[pos:pos + need[s]]
+        pos += need[s]
+        tables[s, :need[s]] = blocks
+        for t in range(K.shape[0]):
+            kc[blocks[t // block_size], :, t % block_size, :] = K[t]
+            vc[blocks[t // block_size], :, :, t % block_size] = V[t]
+    return kc.astype(np.float32), vc.astype(np.float32), tables
+
+
+def random_case(seed, lens, Hq, Hkv, d):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((len(lens), Hq, d)).astype(np.float32)
+    keys = [rng.standard_normal((L, Hkv, d)).astype(np.float32) for L in lens]
+    values = [rng.standard_normal((L, Hkv, d)).astype(np.float32) for L in lens]
+    return rng, q, keys, values
+
+
+@pytest.mark.parametrize("Hq,Hkv,B", [(2, 2, 16), (8, 2, 4), (12, 4, 8)])
+def test_decode_matches_torch_sdpa_on_contiguous(Hq, Hkv, B):
+    lens = [1, 5, 17, 40]
+    d = 16
+    rng, q, keys, values = random_case(7 + Hq, lens, Hq, Hkv, d)
+    kc, vc, tables = paged_from_contiguous(keys, values, B, rng)
+    scale = 0.3
+    got = oracle.decode(q, kc, vc, tables, np.array(lens), scale, B, "f32")
+    for s, L in enumerate(lens):
+        qq = torch.from_numpy(q[s].astype(np.float64))[None, :, None, :]             # [1][Hq][1][d]
+        kk = torch.from_numpy(keys[s].astype(np.float64)).permute(1, 0, 2)[None]      # [1][Hkv][L][d]
+        vv = torch.from_numpy(values[s].astype(np.float64)).permute(1, 0, 2)[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, scale=scale, enable_gqa=True)
+        np.testing.assert_allclose(got[s], ref[0, :, 0, :].numpy(), rtol=0, atol=1e-12)
+
+
+def test_permutation_invariance_and_blockwise_forms():
+    lens = [3, 16, 33, 50]
+    rng, q, keys, values = random_case(11, lens, 4, 2, 8)
+    ref = None
+    for trial in range(4):
+        kc, vc, tables = paged_from_contiguous(keys, values, 8, np.random.default_rng(100 + trial), num_blocks=40)
+        out = oracle.decode(q, kc, vc, tables, np.array(lens), 0.5, 8, "f32")
+        if ref is None:
+            ref = out
+        np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(oracle.decode_blockwise(q, kc, vc, tables, np.array(lens), 0.5, 8, "f32"),
+                                   ref, rtol=0, atol=1e-12)
+        for P in (8, 16, 24, 512):
+            part, partials = oracle.decode_partitioned(q, kc, vc, tables, np.array(lens), 0.5, 8, "f32", P)
+            np.testing.assert_allclose(part, ref, rtol=0, atol=1e-12)
+            assert [len(p) for p in partials[2]] == [-(-33 // P)] * 4
+
+
+def test_bruteforce_tiny_config_and_all_pool_permutations():
+    w = wl.make_decode_workload(wl.CONFIGS["tiny"], poison=False)
+    args = (w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens, w.cfg.scale, 16, "f32")
+    np.testing.assert_allclose(oracle.decode(*args), oracle.bruteforce_decode(*args), rtol=0, atol=1e-12)
+
+    # a 4-block pool under all 24 placements of its blocks
+    rng, q, keys, values = random_case(3, [13], 2, 1, 4)
+    base_k, base_v, base_t = paged_from_contiguous(keys, values, 4, rng, num_blocks=4)
+    ref = oracle.bruteforce_decode(q, base_k, base_v, base_t, np.array([13]), 0.7, 4, "f32")
+    for perm in itertools.permutations(range(4)):
+        kc = np.empty_like(base_k)
+        vc = np.empty_like(base_v)
+        kc[list(perm)] = base_k
+        vc[list(perm)] = base_v
+        tables = np.array([[perm[b] for b in base_t[0]]], dtype=np.int32)
+        out = oracle.decode(q, kc, vc, tables, np.array([13]), 0.7, 4, "f32")
+        np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def test_closed_forms():
+    lens = [1, 7, 20]
+    rng, q, keys, values = random_case(5, lens, 4, 2, 8)
+    kc, vc, tables = paged_from_contiguous(keys, values, 4, rng)
+    L = np.array(lens)
+    mean = [v.astype(np.float64).mean(axis=0) for v in values]      # [Hkv][d]
+    # q = 0 and scale = 0: uniform weights -> mean of the values
+    for qq, sc in ((np.zeros_like(q), 1.0), (q, 0.0)):
+        out = oracle.decode(qq, kc, vc, tables, L, sc, 4, "f32")
+        for s in range(3):
+            for h in range(4):
+                np.testing.assert_allclose(out[s, h], mean[s][h // 2], rtol=0, atol=1e-12)
+    # L = 1: the only value
+    out = oracle.decode(q, kc, vc, tables, L, 0.9, 4, "f32")
+    for h in range(4):
+        np.testing.assert_array_equal(out[0, h], values[0][0, h // 2].astype(np.float64))
+    # identical keys: uniform weights whatever q is
+    same = [np.repeat(k[:1], k.shape[0], axis=0) for k in keys]
+    kc2, vc2, t2 = paged_from_contiguous(same, values, 4, np.random.default_rng(1))
+    out = oracle.decode(q, kc2, vc2, t2, L, 0.9, 4, "f32")
+    for s in range(3):
+        np.testing.assert_allclose(out[s, 1], mean[s][0], rtol=0, atol=1e-12)
+
+
+def test_two_token_logistic_weights():
+    # scores ln3 and 0 -> weights 3/4 and 1/4 (logistic form, not the exp/sum form)
+    d = 4
+    x = np.float32(math.log(3.0))
+    q = np.zeros((1, 1, d), np.float32)
+    q[0, 0, 0] = x
+    k = [np.zeros((2, 1, d), np.float32)]
+    k[0][0, 0, 0] = 1.0
+    v = [np.array([[[1.0, 2.0, -4.0, 8.0]], [[5.0, -6.0, 0.0, 2.0]]], np.float32)]
+    kc, vc, t = paged_from_contiguous(k, v, 4, np.random.default_rng(0))
+    out = oracle.decode(q, kc, vc, t, np.array([2]), 1.0, 4, "f32")
+    w0 = 1.0 / (1.0 + math.exp(-float(x)))
+    v64 = v[0].astype(np.float64)
+    np.testing.assert_allclose(out[0, 0], w0 * v64[0, 0] + (1 - w0) * v64[1, 0], rtol=0, atol=1e-14)
+    assert abs(w0 - 0.75) < 1e-7
+
+
+def test_one_hot_values_return_the_weights_and_rows_sum_to_one():
+    # v_t = e_t (d = 64 >= L): the output is the weight vector itself
+    d, L = 64, 64
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((1, 2, d)).astype(np.float32)
+    keys = [rng.standard_normal((L, 1, d)).astype(np.float32)]
+    eye = np.zeros((L, 1, d), np.float32)
+    eye[np.arange(L), 0, np.arange(L)] = 1.0
+    kc, vc, t = paged_from_contiguous(keys, [eye], 16, rng)
+    out = oracle.decode(q, kc, vc, t, np.array([L]), 0.125, 16, "f32")
+    kk, _ = oracle.gather_sequence(kc, vc, t[0], L, 0, 16, "f32")
+    for h in range(2):
+        a = oracle.decode_probabilities(q[0, h].astype(np.float64), kk, 0.125)
+        assert abs(a.sum() - 1.0) < 1e-12 and (a > 0).all()
+        np.testing.assert_allclose(out[0, h], a, rtol=0, atol=1e-15)
+    # V == 1 everywhere: every output element is 1
+    ones = [np.ones((L, 1, d), np.float32)]
+    kc, vc, t = paged_from_contiguous(keys, ones, 16, rng)
+    out = oracle.decode(q, kc, vc, t, np.array([L]), 0.125, 16, "f32")
+    np.testing.assert_allclose(out, 1.0, rtol=0, atol=1e-12)
+
+
+def test_gqa_head_mapping():
+    # KV head j holds the constant j+1 in every V element: query head h must see h // g + 1
+    Hq, Hkv, d = 8, 2, 4
+    rng = np.random.default_rng(2)
+    q = rng.standard_normal((1, Hq, d)).astype(np.float32)
+    keys = [rng.standard_normal((9, Hkv, d)).astype(np.float32)]
+    vals = [np.broadcast_to(np.arange(1, Hkv + 1, dtype=np.float32)[None, :, None], (9, Hkv, d)).copy()]
+    kc, vc, t = paged_from_contiguous(keys, vals, 4, rng)
+    out = oracle.decode(q, kc, vc, t, np.array([9]), 0.5, 4, "f32")
+    for h in range(Hq):
+        np.testing.assert_allclose(out[0, h], h // (Hq // Hkv) + 1, rtol=0, atol=1e-12)
+
+
+def test_element_widening():
+    bf = np.array([0x3F80, 0xC000, 0x3F81, 0x0001, 0x7F80], dtype=np.uint16)
+    np.testing.assert_array_equal(oracle.to_float64(bf, "bf16"),
+                                  [1.0, -2.0, 1.0 + 2.0 ** -7, 2.0 ** -133, np.inf])
+    f16 = np.array([1.0, -0.5, 65504.0, 2.0 ** -24], dtype=np.float16)
+    np.testing.assert_array_equal(oracle.to_float64(f16, "f16"), [1.0, -0.5, 65504.0, 2.0 ** -24])
+    # torch agrees on the bf16 bit patterns
+    t = torch.tensor(bf.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(oracle.to_float64(bf, "bf16"), t)
+
+
+def test_empty_context_is_rejected():
+    rng, q, keys, values = random_case(1, [3], 1, 1, 4)
+    kc, vc, t = paged_from_contiguous(keys, values, 4, rng)
+    with pytest.raises(ValueError):
+        oracle.decode(q, kc, vc, t, np.array([0]), 1.0, 4, "f32")
