@@ -1,0 +1,180 @@
+/*
+ * pagedattn.h -- C ABI of libpagedattn.so: paged decode attention, the
+ * slot-mapped KV write and the copy-on-write block copy on MI355X (gfx950).
+ *
+ * Sources (web pages on the SOSP'23 PagedAttention paper):
+ *   [notes-zh]  "PagedAttention 论文精读笔记" (pagedattention-sosp23-notes)
+ *   [deep-dive] "paged-attention은 도대체 뭘 최적화 하는 것일까" (hrletsgo.me)
+ *   [review-en] "PagedAttention paper review" (junupark.xyz)
+ *   [review-kr] "Efficient Memory Management for Large Language Model Serving
+ *                with PagedAttention Review" (dimensionstp.github.io)
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Pointers named *_cache, q, out, k_new, v_new, slot_mapping, block_tables,
+ * context_lens, block_mapping and workspace are DEVICE pointers owned by the
+ * caller; every one must be 16-byte aligned. The library allocates no memory
+ * and keeps no state between calls apart from a per-device cache of device
+ * properties. `stream` is a hipStream_t passed as void* (NULL = the default
+ * stream); every call only enqueues work on it and returns without
+ * synchronising. The status covers host-side argument checks and launch
+ * errors; device-side faults surface on a later synchronisation.
+ *
+ * KV block pool layout (one contiguous chunk cut into fixed-size physical
+ * blocks, each holding K and V for block_size tokens, [notes-zh] §5.1-§5.2;
+ * the in-block order is this library's choice):
+ *   k_cache: [num_blocks][num_kv_heads][block_size][head_dim]  (token rows)
+ *   v_cache: [num_blocks][num_kv_heads][head_dim][block_size]  (token columns)
+ * Token t of a sequence lives in physical block block_tables[s][t / block_size]
+ * at offset t % block_size ([deep-dive] §14 and §17), i.e. slot
+ * physical_block * block_size + offset.
+ *
+ * Element types: PA_F32 (IEEE binary32), PA_F16 (IEEE binary16) and PA_BF16
+ * (bfloat16). All attention arithmetic is fp32.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, negative or inconsistent size */
+  PA_ERR_UNSUPPORTED = -2,  /* valid request this build does not implement */
+  PA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required */
+  PA_ERR_LAUNCH = -4        /* the HIP runtime reported an error at launch */
+} pa_status;
+
+/* Decode kernel family. AUTO picks MFMA for 16-bit elements when
+ * num_heads / num_kv_heads >= 3 (grouped query heads make QK and PV a dense
+ * contraction), the vector kernel otherwise. */
+typedef enum pa_algo { PA_ALGO_AUTO = 0, PA_ALGO_VECTOR = 1, PA_ALGO_MFMA = 2 } pa_algo;
+
+/* partition_size values for pa_decode besides a positive multiple of 32:
+ *  PA_PARTITION_AUTO: the context of every (sequence, KV head) is cut so that
+ *                     every worker wave gets the same number of 32-token
+ *                     chunks (split points fall anywhere in the batch);
+ *  PA_PARTITION_NONE: one wave per (sequence, KV head), no split. */
+#define PA_PARTITION_AUTO (-1)
+#define PA_PARTITION_NONE 0
+
+/*
+ * pa_write_kv -- store new K/V rows into their slots ("fused reshape and
+ * block write", [review-kr] §3-2(5); new KV goes into its physical block,
+ * [notes-zh] §5.3).
+ *   k_new, v_new : [num_tokens][num_kv_heads][head_dim] of `dtype`.
+ *   slot_mapping : [num_tokens] int32, slot = physical_block*block_size + offset.
+ *                  A negative slot or one >= num_blocks*block_size is skipped.
+ *   For every written token n and head h:
+ *     k_cache[slot/B][h][slot%B][:] = k_new[n][h][:]
+ *     v_cache[slot/B][h][:][slot%B] = v_new[n][h][:]
+ *   Bit-exact data movement (NaN payloads included). Two tokens naming the
+ *   same slot in one call is a precondition violation (the winner is
+ *   unspecified). num_tokens == 0 is a no-op. Any head_dim >= 1 and
+ *   block_size >= 1 are accepted.
+ */
+pa_status pa_write_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                      const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int32_t num_blocks, pa_dtype dtype,
+                      void* stream);
+
+/*
+ * pa_decode -- exact single-query attention of every sequence's newest token
+ * over its paged context ([notes-zh] §2.1 attention equation and §4.2
+ * block-wise form; [deep-dive] §8 and §14):
+ *   for sequence s, query head h, KV head j = h / (num_heads/num_kv_heads),
+ *   L = context_lens[s] (the new token included, so write first):
+ *     a_t = exp(scale*q[s][h].k_t) / sum_{u<L} exp(scale*q[s][h].k_u),
+ *     out[s][h][:] = sum_{t<L} a_t * v_t,
+ *   with k_t, v_t read through block_tables[s].
+ *   out          : [num_seqs][num_heads][head_dim] of out_dtype (F32, F16 or
+ *                  BF16; the value is rounded once at the end).
+ *   q            : [num_seqs][num_heads][head_dim] of dtype.
+ *   block_tables : [num_seqs][max_blocks_per_seq] int32; only entries below
+ *                  ceil(L/block_size) are read. Ids outside [0, num_blocks)
+ *                  are clamped into range (the result is then unspecified,
+ *                  but no memory outside the pools is read).
+ *   context_lens : [num_seqs] int32. L is clamped to
+ *                  max_blocks_per_seq*block_size; L <= 0 writes zeros.
+ *   max_context_len : host-side upper bound of context_lens (sizes the work).
+ *   partition_size  : PA_PARTITION_AUTO, PA_PARTITION_NONE, or a positive
+ *                  multiple of 32: fixed partitions of that many tokens per
+ *                  (sequence, KV head), merged by their max and sum of
+ *                  exponentials ([review-en] "How does this work?": compute
+ *                  per block, then combine the partial results).
+ *   workspace    : device scratch of at least pa_decode_workspace_bytes(...)
+ *                  bytes (may be NULL when that is 0). Its first
+ *                  num_seqs*num_kv_heads int32 are arrival counters that
+ *                  must be zero when a call starts; every call leaves them
+ *                  zero, and leaves partial results in the bytes after them.
+ *                  So zero the buffer after allocating it (e.g. with
+ *                  pa_decode_workspace_init), and again before a call whose
+ *                  num_seqs*num_kv_heads exceeds that of the previous call on
+ *                  the same buffer. Calls that overlap in time must not share
+ *                  a workspace.
+ *   Requirements: head_dim in {64, 128}; block_size in {8, 16, 32, 64, 128};
+ *   num_heads % num_kv_heads == 0 and num_heads/num_kv_heads <= 8;
+ *   PA_ALGO_MFMA needs dtype F16 or BF16.
+ *   The reduction order depends only on logical token positions (no atomics
+ *   in the arithmetic), so the result does not change under any permutation
+ *   of the physical blocks.
+ */
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                    int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                    float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
+                    pa_dtype dtype, pa_dtype out_dtype, void* stream);
+
+/* pa_decode with an explicit kernel family (pa_algo). Same contract. */
+pa_status pa_decode_ex(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                       int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                       int32_t max_context_len, float scale, int32_t partition_size,
+                       void* workspace, size_t workspace_bytes, pa_dtype dtype,
+                       pa_dtype out_dtype, pa_algo algo, void* stream);
+
+/* Workspace bytes pa_decode needs for these sizes (0 when it needs none).
+ * Returns 0 as well for arguments pa_decode would reject. Pure host function. */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_context_len,
+                                 int32_t partition_size);
+
+/* Zero a decode workspace on `stream` (a fill kernel, so it may be captured
+ * in a HIP graph). */
+pa_status pa_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_copy_blocks -- batched whole-block copy for copy-on-write ([notes-zh]
+ * §6.1: a write into a shared block first copies it to a new block; the
+ * copies of a step are fused into one launch, [review-kr] §3-2(5)).
+ *   block_mapping: [num_pairs][2] int32 (src, dst). For every pair:
+ *     k_cache[dst][:][:][:] = k_cache[src][:][:][:] and the same for v_cache
+ *   (all KV heads, all slots). Bit-exact. Pairs with an id outside
+ *   [0, num_blocks) are skipped. Preconditions: destinations are distinct and
+ *   no destination is also a source in the same call (otherwise the result
+ *   depends on scheduling). num_pairs == 0 is a no-op.
+ */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping,
+                         int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks, pa_dtype dtype, void* stream);
+
+/* Static, human-readable name of a status. */
+const char* pa_status_string(pa_status status);
+
+/* ABI version of this header (incremented on incompatible change). */
+int32_t pa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

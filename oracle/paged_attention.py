@@ -63,17 +63,18 @@ def translate(block_table_row, token_index: int, block_size: int):
     return int(block_table_row[logical_block]), offset
 
 
-def write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, block_size):
+def write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, block_size, inplace=False):
     """Slot-mapped store of new K/V rows ("fused reshape and block write",
     [review-kr] §3-2(5); new KV goes into its physical block, [notes-zh] §5.3).
 
     k_new, v_new: [num_tokens][num_kv_heads][head_dim] raw stored elements.
     slot_mapping[n] = physical_block * block_size + offset; a negative slot
-    means "no write" (padding token). Returns new pools; inputs untouched.
-    This is pure data movement, so the result is compared bit for bit.
+    means "no write" (padding token). Returns new pools (the given ones,
+    modified, when inplace=True). This is pure data movement, so the result is
+    compared bit for bit.
     """
-    k_out = np.array(k_cache, copy=True)
-    v_out = np.array(v_cache, copy=True)
+    k_out = k_cache if inplace else np.array(k_cache, copy=True)
+    v_out = v_cache if inplace else np.array(v_cache, copy=True)
     for n, slot in enumerate(np.asarray(slot_mapping).tolist()):
         if slot < 0:
             continue
@@ -84,14 +85,15 @@ def write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, block_size):
     return k_out, v_out
 
 
-def copy_blocks(k_cache, v_cache, block_mapping):
+def copy_blocks(k_cache, v_cache, block_mapping, inplace=False):
     """Copy-on-write block copy ([notes-zh] §6.1: allocate a new physical
     block and copy the original block's data into it; batched as one fused
     copy, [review-kr] §3-2(5)). Whole blocks: every KV head, every slot, K and
-    V. Pairs are applied in list order. Returns new pools.
+    V. Pairs are applied in list order. Returns new pools (the given ones when
+    inplace=True).
     """
-    k_out = np.array(k_cache, copy=True)
-    v_out = np.array(v_cache, copy=True)
+    k_out = k_cache if inplace else np.array(k_cache, copy=True)
+    v_out = v_cache if inplace else np.array(v_cache, copy=True)
     for src, dst in np.asarray(block_mapping).reshape(-1, 2).tolist():
         k_out[dst] = k_out[src]
         v_out[dst] = v_out[src]

@@ -1,0 +1,276 @@
+// extern "C" entry points of libpagedattn.so: argument checks, choice of
+// kernel family and split mode, workspace layout, launch. Declarations and
+// the contract of every call are in include/pagedattn.h.
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+
+#include "pa_internal.h"
+#include "pagedattn.h"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+constexpr size_t kAlign = 256;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+bool valid_dtype(int d) { return d == PA_F32 || d == PA_F16 || d == PA_BF16; }
+int elem_bytes(int d) { return d == PA_F32 ? 4 : 2; }
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int log2_exact(int v) {
+  int l = 0;
+  while ((1 << l) < v) ++l;
+  return (1 << l) == v ? l : -1;
+}
+
+// How a decode call splits its work.
+struct Plan {
+  int mode;         // pa::kModeBalanced / pa::kModeFixed
+  int part_chunks;  // fixed: chunks per partition
+  int max_parts;    // fixed: partitions per sequence
+  int max_workers;  // balanced: upper bound of workers per KV head
+  size_t slots;     // partial-result slots (0 = never split)
+};
+
+Plan make_plan(int num_seqs, int num_kv_heads, int max_context_len, int partition_size) {
+  Plan pl{pa::kModeFixed, 1, 1, 0, 0};
+  const long long max_chunks = ((long long)max_context_len + pa::kChunk - 1) / pa::kChunk;
+  if (partition_size == PA_PARTITION_AUTO && num_seqs <= pa::kMaxBalancedSeqs) {
+    pl.mode = pa::kModeBalanced;
+    const long long wmax = (pa::kMaxWorkersTotal + num_kv_heads - 1) / num_kv_heads;
+    const long long cap = (long long)num_seqs * max_chunks;
+    pl.max_workers = (int)(wmax < cap ? wmax : cap);
+    if (pl.max_workers < 1) pl.max_workers = 1;
+    pl.slots = (size_t)pl.max_workers + (size_t)num_seqs;
+    return pl;
+  }
+  if (partition_size > 0) {
+    pl.part_chunks = partition_size / pa::kChunk;
+    pl.max_parts = (int)((max_chunks + pl.part_chunks - 1) / pl.part_chunks);
+  } else {  // NONE, or AUTO with too many sequences: one wave per (sequence, KV head)
+    pl.part_chunks = (int)(max_chunks < INT_MAX ? max_chunks : INT_MAX);
+    pl.max_parts = 1;
+  }
+  if (pl.max_parts < 1) pl.max_parts = 1;
+  pl.slots = pl.max_parts > 1 ? (size_t)num_seqs * pl.max_parts : 0;
+  return pl;
+}
+
+struct WorkspaceLayout {
+  size_t counters, ml, acc, total;
+};
+
+WorkspaceLayout layout(const Plan& pl, int num_seqs, int num_heads, int num_kv_heads, int head_dim) {
+  WorkspaceLayout w{0, 0, 0, 0};
+  if (pl.slots == 0) return w;
+  const size_t counters = round_up((size_t)num_seqs * num_kv_heads * sizeof(int32_t));
+  const size_t ml = round_up(pl.slots * (size_t)num_heads * 2 * sizeof(float));
+  const size_t acc = round_up(pl.slots * (size_t)num_heads * head_dim * sizeof(float));
+  w.counters = 0;
+  w.ml = counters;
+  w.acc = counters + ml;
+  w.total = counters + ml + acc;
+  return w;
+}
+
+bool decode_shape_ok(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int max_context_len,
+                     int partition_size) {
+  if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads) return false;
+  if (head_dim != 64 && head_dim != 128) return false;
+  if (max_context_len < 1) return false;
+  if (partition_size < PA_PARTITION_AUTO) return false;
+  if (partition_size > 0 && partition_size % pa::kChunk) return false;
+  return true;
+}
+
+// Resident 64-thread waves per CU for each kernel, and CU counts, per device.
+constexpr int kMaxDevices = 64;
+std::mutex g_mutex;
+int g_cus[kMaxDevices];
+int g_waves[kMaxDevices][3][2][3][9];  // [device][elem][head_dim 64/128][algo][G]
+
+int workers_target(int elem, int head_dim, int algo, int G) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 2048;
+  std::lock_guard<std::mutex> lock(g_mutex);
+  if (g_cus[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+    g_cus[dev] = cus;
+  }
+  int& waves = g_waves[dev][elem][head_dim == 128][algo][G];
+  if (waves == 0) {
+    waves = pa::decode_waves_per_cu(elem, head_dim, algo, G);
+    if (waves < 1) waves = 8;
+  }
+  return g_cus[dev] * waves;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(pa_status status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t pa_abi_version(void) { return kAbiVersion; }
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t partition_size) {
+  if (!decode_shape_ok(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, partition_size)) return 0;
+  const Plan pl = make_plan(num_seqs, num_kv_heads, max_context_len, partition_size);
+  return layout(pl, num_seqs, num_heads, num_kv_heads, head_dim).total;
+}
+
+pa_status pa_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (workspace_bytes == 0) return PA_OK;
+  if (!workspace || !aligned(workspace, 4)) return PA_ERR_INVALID_ARG;
+  return pa::launch_fill_zero(workspace, workspace_bytes, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? PA_OK
+             : PA_ERR_LAUNCH;
+}
+
+pa_status pa_write_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                      const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int32_t num_blocks, pa_dtype dtype, void* stream) {
+  if (!valid_dtype(dtype)) return PA_ERR_INVALID_ARG;
+  if (num_tokens < 0 || num_kv_heads < 1 || num_kv_heads > 65535 || head_dim < 1 || block_size < 1 ||
+      num_blocks < 1)
+    return PA_ERR_INVALID_ARG;
+  if ((long long)num_blocks * block_size > INT_MAX) return PA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PA_OK;
+  const uintptr_t a = (uintptr_t)elem_bytes(dtype);
+  if (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping) return PA_ERR_INVALID_ARG;
+  if (!aligned(k_new, a) || !aligned(v_new, a) || !aligned(k_cache, a) || !aligned(v_cache, a) ||
+      !aligned(slot_mapping, 4))
+    return PA_ERR_INVALID_ARG;
+  const hipError_t e = pa::launch_write_kv(k_new, v_new, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads,
+                                           head_dim, block_size, num_blocks, elem_bytes(dtype),
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping, int32_t num_pairs,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                         pa_dtype dtype, void* stream) {
+  if (!valid_dtype(dtype)) return PA_ERR_INVALID_ARG;
+  if (num_pairs < 0 || num_kv_heads < 1 || head_dim < 1 || block_size < 1 || num_blocks < 1)
+    return PA_ERR_INVALID_ARG;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !block_mapping) return PA_ERR_INVALID_ARG;
+  const size_t block_bytes = (size_t)num_kv_heads * block_size * head_dim * elem_bytes(dtype);
+  const uintptr_t a = block_bytes % 16 == 0 ? 16 : 1;
+  if (!aligned(k_cache, a) || !aligned(v_cache, a) || !aligned(block_mapping, 4)) return PA_ERR_INVALID_ARG;
+  const hipError_t e = pa::launch_copy_blocks(k_cache, v_cache, block_mapping, num_pairs, num_blocks, block_bytes,
+                                              static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+pa_status pa_decode_ex(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                       int32_t max_blocks_per_seq, int32_t max_context_len, float scale, int32_t partition_size,
+                       void* workspace, size_t workspace_bytes, pa_dtype dtype, pa_dtype out_dtype, pa_algo algo,
+                       void* stream) {
+  if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return PA_ERR_INVALID_ARG;
+  if (algo != PA_ALGO_AUTO && algo != PA_ALGO_VECTOR && algo != PA_ALGO_MFMA) return PA_ERR_INVALID_ARG;
+  if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads) return PA_ERR_INVALID_ARG;
+  if (num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
+  if (max_context_len < 1 || num_blocks < 1 || max_blocks_per_seq < 1) return PA_ERR_INVALID_ARG;
+  if (partition_size < PA_PARTITION_AUTO || (partition_size > 0 && partition_size % pa::kChunk))
+    return PA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
+  const int log2b = log2_exact(block_size);
+  if (block_size < 8 || block_size > 128 || log2b < 0) return PA_ERR_UNSUPPORTED;
+  if ((long long)max_blocks_per_seq * block_size > INT_MAX) return PA_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  const int group = num_heads / num_kv_heads;
+  if (group > pa::kMaxGroup) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 4) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return PA_ERR_INVALID_ARG;
+
+  int kernel_algo;
+  if (algo == PA_ALGO_MFMA) {
+    if (dtype == PA_F32) return PA_ERR_UNSUPPORTED;
+    kernel_algo = pa::kAlgoMfma;
+  } else if (algo == PA_ALGO_VECTOR) {
+    kernel_algo = pa::kAlgoVector;
+  } else {
+    kernel_algo = (dtype != PA_F32 && group >= 3) ? pa::kAlgoMfma : pa::kAlgoVector;
+  }
+  const int G = kernel_algo == pa::kAlgoMfma ? 0 : (group <= 1 ? 1 : group <= 2 ? 2 : group <= 4 ? 4 : 8);
+
+  const Plan pl = make_plan(num_seqs, num_kv_heads, max_context_len, partition_size);
+  const WorkspaceLayout wl = layout(pl, num_seqs, num_heads, num_kv_heads, head_dim);
+  if (wl.total > 0) {
+    if (!workspace || workspace_bytes < wl.total) return PA_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return PA_ERR_INVALID_ARG;
+  }
+
+  pa::DecodeParams p{};
+  p.out = out;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  char* ws = static_cast<char*>(workspace);
+  p.counters = wl.total ? reinterpret_cast<int32_t*>(ws + wl.counters) : nullptr;
+  p.ws_ml = wl.total ? reinterpret_cast<float*>(ws + wl.ml) : nullptr;
+  p.ws_acc = wl.total ? reinterpret_cast<float*>(ws + wl.acc) : nullptr;
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = group;
+  p.block_size = block_size;
+  p.log2_block = log2b;
+  p.num_blocks = num_blocks;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.mode = pl.mode;
+  p.part_chunks = pl.part_chunks;
+  p.max_parts = pl.max_parts;
+  p.out_dtype = out_dtype;
+
+  const int elem = dtype == PA_F32 ? pa::kF32 : (dtype == PA_F16 ? pa::kF16 : pa::kBF16);
+  long long workers;
+  if (pl.mode == pa::kModeBalanced) {
+    const int target = workers_target(elem, head_dim, kernel_algo, G);
+    workers = (target + num_kv_heads - 1) / num_kv_heads;
+    if (workers > pl.max_workers) workers = pl.max_workers;
+    if (workers < 1) workers = 1;
+  } else {
+    workers = (long long)num_seqs * pl.max_parts;
+    if (workers > INT_MAX) return PA_ERR_UNSUPPORTED;
+  }
+  const hipError_t e = pa::launch_decode(p, elem, head_dim, kernel_algo, G, (unsigned)workers,
+                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                    int32_t max_context_len, float scale, int32_t partition_size, void* workspace,
+                    size_t workspace_bytes, pa_dtype dtype, pa_dtype out_dtype, void* stream) {
+  return pa_decode_ex(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads, num_kv_heads,
+                      head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len, scale, partition_size,
+                      workspace, workspace_bytes, dtype, out_dtype, PA_ALGO_AUTO, stream);
+}
+
+}  // extern "C"

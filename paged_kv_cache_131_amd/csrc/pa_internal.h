@@ -1,0 +1,67 @@
+// Internal interface between the C ABI (pa_api.cpp) and the HIP kernels
+// (pa_kernels.hip). Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Tokens one wave consumes per step of the decode loop. Balanced splits and
+// fixed partitions both fall on multiples of it.
+constexpr int kChunk = 32;
+// Upper bound on balanced-split workers summed over KV heads; sizes workspaces.
+constexpr int kMaxWorkersTotal = 8192;
+// Largest query-head group (num_heads / num_kv_heads) any kernel handles.
+constexpr int kMaxGroup = 8;
+// Balanced splits scan every sequence length in every worker; above this
+// many sequences the automatic mode falls back to one wave per sequence.
+constexpr int kMaxBalancedSeqs = 4096;
+
+enum Elem : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+enum Mode : int { kModeBalanced = 0, kModeFixed = 1 };
+enum Algo : int { kAlgoVector = 1, kAlgoMfma = 2 };
+
+struct DecodeParams {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int32_t* counters;  // [num_seqs][num_kv_heads] arrival counters (split modes)
+  float* ws_ml;       // [slots][num_heads][2]  (running max in log2 units, sum)
+  float* ws_acc;      // [slots][num_heads][head_dim] (unnormalised output)
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t group;        // num_heads / num_kv_heads
+  int32_t block_size;
+  int32_t log2_block;
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  float scale_log2;     // scale * log2(e): scores live in base-2 exponent units
+  int32_t mode;         // kModeBalanced or kModeFixed
+  int32_t part_chunks;  // fixed mode: chunks per partition
+  int32_t max_parts;    // fixed mode: partitions per sequence (grid.x = num_seqs*max_parts)
+  int32_t out_dtype;    // Elem of `out`
+};
+
+// Launch the decode kernel for (elem, head_dim, algo, group bucket G).
+// grid = (workers per KV head, num_kv_heads), 64 threads per workgroup.
+hipError_t launch_decode(const DecodeParams& p, int elem, int head_dim, int algo, int G,
+                         unsigned workers, hipStream_t stream);
+// Resident waves per CU of that kernel (0 if unknown).
+int decode_waves_per_cu(int elem, int head_dim, int algo, int G);
+
+hipError_t launch_write_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                           const int32_t* slots, int num_tokens, int num_kv_heads, int head_dim,
+                           int block_size, int num_blocks, int elem_bytes, hipStream_t stream);
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* mapping, int num_pairs,
+                              int num_blocks, size_t block_bytes, hipStream_t stream);
+
+hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream);
+
+}  // namespace pa

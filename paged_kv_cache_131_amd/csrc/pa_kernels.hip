@@ -1,0 +1,793 @@
+// HIP kernels for gfx950 (CDNA4): paged decode attention, slot-mapped KV
+// write, copy-on-write block copy, workspace fill.
+//
+// Method: exact single-query attention over a KV cache cut into fixed-size
+// physical blocks that a per-sequence block table maps from logical order
+// ("PagedAttention 论文精读笔记" §2.1 attention equation, §4.2 block-wise
+// form; "paged-attention은 도대체 뭘 최적화 하는 것일까" §14 address
+// translation). Blocks are consumed 32 tokens at a time with an fp32 online
+// softmax, partial results of split contexts are combined by their maxima and
+// exponential sums ("PagedAttention paper review", "How does this work?").
+//
+// Pool layout (per physical block and KV head, one contiguous tile):
+//   K tile [block_size][head_dim]  -- token rows
+//   V tile [head_dim][block_size]  -- token columns
+// so that both MFMA operands of the two contractions (QK over head_dim, PV
+// over tokens) are 16-byte contiguous loads straight from HBM.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <mutex>
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ u32x4 load16(const void* ptr) {
+  return *reinterpret_cast<const u32x4*>(ptr);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// Element types
+// ---------------------------------------------------------------------------
+template <int E>
+struct ElemT;
+
+template <>
+struct ElemT<kF32> {
+  using raw = uint32_t;
+  static constexpr int kVec = 4;  // elements per 16 bytes
+  __device__ static void widen(u32x4 w, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(w[i]);
+  }
+  // zero the elements of tokens >= nvalid (one token per element)
+  __device__ static u32x4 keep_first(u32x4 w, int nvalid) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = i < nvalid ? w[i] : 0u;
+    return w;
+  }
+};
+
+template <>
+struct ElemT<kF16> {
+  using raw = uint16_t;
+  using op8 = f16x8;
+  using scalar = _Float16;
+  static constexpr int kVec = 8;
+  __device__ static void widen(u32x4 w, float* f) {
+    const f16x8 h = __builtin_bit_cast(f16x8, w);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = static_cast<float>(h[i]);
+  }
+  __device__ static u32x4 keep_first(u32x4 w, int nvalid) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t m = 2 * i + 1 < nvalid ? 0xffffffffu : (2 * i < nvalid ? 0x0000ffffu : 0u);
+      w[i] &= m;
+    }
+    return w;
+  }
+};
+
+template <>
+struct ElemT<kBF16> {
+  using raw = uint16_t;
+  using op8 = bf16x8;
+  using scalar = __bf16;
+  static constexpr int kVec = 8;
+  __device__ static void widen(u32x4 w, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ static u32x4 keep_first(u32x4 w, int nvalid) { return ElemT<kF16>::keep_first(w, nvalid); }
+};
+
+__device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_16x16x32(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void store_out(void* out, size_t idx, float v, int out_dtype) {
+  if (out_dtype == kF32) {
+    static_cast<float*>(out)[idx] = v;
+  } else if (out_dtype == kF16) {
+    static_cast<_Float16*>(out)[idx] = static_cast<_Float16>(v);
+  } else {
+    static_cast<__bf16*>(out)[idx] = static_cast<__bf16>(v);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Block-table lookups for one 32-token chunk. A chunk spans at most four
+// blocks (block_size >= 8); ids are read with wave-uniform addresses and the
+// logical block is clamped to the segment's last block, so tokens past the
+// context never index past the table's valid entries. Ids are clamped into
+// the pool.
+// ---------------------------------------------------------------------------
+struct ChunkIds {
+  int lb0;
+  int id0, id1, id2, id3;
+};
+
+__device__ __forceinline__ int table_entry(const int32_t* __restrict__ tbl, int lb, int lbl, int num_blocks) {
+  const int v = tbl[min(lb, lbl)];
+  return min(max(v, 0), num_blocks - 1);
+}
+
+__device__ __forceinline__ ChunkIds load_chunk_ids(const int32_t* __restrict__ tbl, int cs, int lbl,
+                                                   const DecodeParams& p) {
+  ChunkIds c;
+  c.lb0 = cs >> p.log2_block;
+  const int nid = p.log2_block >= 5 ? 1 : (kChunk >> p.log2_block);
+  c.id0 = table_entry(tbl, c.lb0, lbl, p.num_blocks);
+  c.id1 = nid > 1 ? table_entry(tbl, c.lb0 + 1, lbl, p.num_blocks) : c.id0;
+  c.id2 = nid > 2 ? table_entry(tbl, c.lb0 + 2, lbl, p.num_blocks) : c.id1;
+  c.id3 = nid > 3 ? table_entry(tbl, c.lb0 + 3, lbl, p.num_blocks) : c.id2;
+  return c;
+}
+
+__device__ __forceinline__ int pick_block(ChunkIds c, int tok, int log2_block, int lbl) {
+  const int k = min(tok >> log2_block, lbl) - c.lb0;
+  int id = c.id0;
+  id = k >= 1 ? c.id1 : id;
+  id = k >= 2 ? c.id2 : id;
+  id = k >= 3 ? c.id3 : id;
+  return id;
+}
+
+__device__ __forceinline__ int eff_len(const DecodeParams& p, int s) {
+  const int cap = p.max_blocks_per_seq << p.log2_block;
+  return min(p.context_lens[s], cap);
+}
+
+__device__ __forceinline__ int num_chunks(int L) { return L > 0 ? (L + kChunk - 1) / kChunk : 0; }
+
+// ---------------------------------------------------------------------------
+// MFMA engine (16-bit elements, group g in [1, 8]).
+//
+// One wave runs v_mfma_f32_16x16x32 on each chunk of 32 tokens:
+//   QK: D[token slot][head slot] = K rows (A, 16 x 32) x q^T (B, 32 x 16),
+//       two row groups of 16 tokens, head_dim/32 k-steps each;
+//   PV: D[head slot][dd] = P (A, 16 x 32 tokens) x V (B, 32 tokens x 16),
+//       head_dim/16 column tiles.
+// Lane l feeds A row / B column l%16 and k-slots 8*(l/16)..+7; D[4*(l/16)+i]
+// [l%16] comes back in register i. Token slots are arranged so that the QK
+// result of lane l (tokens 8*(l/16)+0..7 of its head slot) is exactly the P
+// operand lane l must supply, and V's token-minor tile makes each lane's
+// eight tokens at one dd a single 16-byte load.
+// Head slots: c < g carry head c with P rounded to 16 bits ("hi"), g <= c <
+// 2g carry head c-g with the rounding residual ("lo"), the rest are zero; the
+// two PV results are added at the end, so P enters the product with ~16
+// significant bits instead of 8.
+// ---------------------------------------------------------------------------
+template <int E, int D>
+struct MfmaEngine {
+  using Tr = ElemT<E>;
+  using op8 = typename Tr::op8;
+  using scalar = typename Tr::scalar;
+  using raw = typename Tr::raw;
+  static constexpr int MQ = D / 32;  // QK k-steps
+  static constexpr int NT = D / 16;  // PV column tiles
+  static constexpr int kPad = 4;
+  struct Smem {
+    float o[16][D + kPad];
+    float ml[16][2];
+  };
+
+  op8 qop[MQ];
+  f32x4 o[NT];
+  float m_run;
+  float l_run;
+
+  __device__ void begin(const DecodeParams& p, int s, int kvh, int lane) {
+    const int col = lane & 15, grp = lane >> 4, g = p.group;
+    const int hs = col < g ? col : (col < 2 * g ? col - g : -1);
+    const raw* qb = static_cast<const raw*>(p.q) + ((size_t)s * p.num_heads + (size_t)kvh * g) * D;
+#pragma unroll
+    for (int m = 0; m < MQ; ++m) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (hs >= 0) w = load16(qb + (size_t)hs * D + 32 * m + 8 * grp);
+      qop[m] = __builtin_bit_cast(op8, w);
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run = kNegInf;
+    l_run = 0.f;
+  }
+
+  __device__ void chunk(const DecodeParams& p, Smem&, int kvh, int lane, int cs, int t1,
+                        ChunkIds ids, int lbl) {
+    const int col = lane & 15, grp = lane >> 4, g = p.group;
+    const int B = p.block_size, lg = p.log2_block, Hkv = p.num_kv_heads;
+    const raw* __restrict__ kc = static_cast<const raw*>(p.k_cache);
+    const raw* __restrict__ vc = static_cast<const raw*>(p.v_cache);
+
+    // K rows: A-operand row `col` of row group c holds token 8*(col/4)+4c+col%4
+    u32x4 ka[2][MQ];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int tok = cs + 8 * (col >> 2) + 4 * c + (col & 3);
+      const int phys = pick_block(ids, tok, lg, lbl);
+      const raw* row = kc + (((size_t)phys * Hkv + kvh) * B + (tok & (B - 1))) * D + 8 * grp;
+#pragma unroll
+      for (int m = 0; m < MQ; ++m) ka[c][m] = load16(row + 32 * m);
+    }
+    // V: B operand, tokens 8*grp..+7 of the chunk at dd = 16j + col
+    const int tv = cs + 8 * grp;
+    const int physv = pick_block(ids, tv, lg, lbl);
+    const raw* vb = vc + (((size_t)physv * Hkv + kvh) * D + col) * B + (tv & (B - 1));
+    u32x4 vr[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) vr[j] = load16(vb + (size_t)16 * j * B);
+
+    // scores: lane holds tokens tv+0..7 of head slot `col`
+    f32x4 sc0 = {0.f, 0.f, 0.f, 0.f}, sc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < MQ; ++m) {
+      sc0 = mfma_16x16x32(__builtin_bit_cast(op8, ka[0][m]), qop[m], sc0);
+      sc1 = mfma_16x16x32(__builtin_bit_cast(op8, ka[1][m]), qop[m], sc1);
+    }
+    float sv[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sv[i] = sc0[i] * p.scale_log2;
+      sv[4 + i] = sc1[i] * p.scale_log2;
+    }
+    const bool partial = cs + kChunk > t1;
+    if (partial) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sv[e] = (tv + e < t1) ? sv[e] : kNegInf;
+    }
+
+    // online softmax (base 2), per head slot
+    float cmax = sv[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) cmax = fmaxf(cmax, sv[e]);
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+    const float m_new = fmaxf(m_run, cmax);
+    const float alpha = fast_exp2(m_run - m_new);
+    float pe[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pe[e] = fast_exp2(sv[e] - m_new);
+      psum += pe[e];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    if (__any(alpha != 1.f)) {
+      // output rows of this lane are head slots 4*grp+i; their factor lives in lane 4*grp+i
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ai = __shfl(alpha, 4 * grp + i);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) o[j][i] *= ai;
+      }
+    }
+
+    // P operand: hi part, lo residual or zero depending on the head slot
+    op8 pa;
+    const int part = col < g ? 0 : (col < 2 * g ? 1 : 2);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const scalar hi = static_cast<scalar>(pe[e]);
+      const scalar lo = static_cast<scalar>(pe[e] - static_cast<float>(hi));
+      pa[e] = part == 0 ? hi : (part == 1 ? lo : static_cast<scalar>(0.f));
+    }
+    if (partial) {
+      const int nvalid = t1 - tv;
+#pragma unroll
+      for (int j = 0; j < NT; ++j) vr[j] = Tr::keep_first(vr[j], nvalid);
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) o[j] = mfma_16x16x32(pa, __builtin_bit_cast(op8, vr[j]), o[j]);
+  }
+
+  __device__ void finish(Smem& sm, int lane) {
+    const int col = lane & 15, grp = lane >> 4;
+    float l_tot = l_run + __shfl_xor(l_run, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm.o[4 * grp + i][16 * j + col] = o[j][i];
+    if (grp == 0) {
+      sm.ml[col][0] = m_run;
+      sm.ml[col][1] = l_tot;
+    }
+    __syncthreads();
+  }
+
+  __device__ static float o_val(const Smem& sm, int h, int dd, int g) { return sm.o[h][dd] + sm.o[h + g][dd]; }
+  __device__ static float m_val(const Smem& sm, int h) { return sm.ml[h][0]; }
+  __device__ static float l_val(const Smem& sm, int h) { return sm.ml[h][1]; }
+};
+
+// ---------------------------------------------------------------------------
+// Vector engine (any element type, group bucket G >= g).
+//
+// QK: 16-byte coalesced loads of token rows, LPR lanes per row, partial dot
+// products reduced across those lanes. Softmax over the chunk's 32 scores
+// through LDS. PV: 16-byte loads of VEC consecutive tokens at one dd from the
+// token-minor V tile, fp32 FMAs, accumulators reduced across lanes at the end.
+// ---------------------------------------------------------------------------
+template <int E, int D, int G>
+struct VecEngine {
+  using Tr = ElemT<E>;
+  using raw = typename Tr::raw;
+  static constexpr int VEC = Tr::kVec;
+  static constexpr int LPR = D / VEC;           // lanes per K row
+  static constexpr int RPS = 64 / LPR;          // K rows per load step
+  static constexpr int KSTEPS = kChunk / RPS;   // K load steps per chunk
+  static constexpr int LPD = kChunk / VEC;      // lanes per V dd-row of a chunk
+  static constexpr int DPS = 64 / LPD;          // dd rows per V load step
+  static constexpr int VSTEPS = D / DPS;        // V load steps per chunk
+  struct Smem {
+    float sc[G][kChunk];
+    float pl[G][kChunk];
+    float o[G][D];
+    float ml[G][2];
+  };
+
+  float qv[G][VEC];
+  float acc[G][VSTEPS];
+  float m_run[G];
+  float l_run[G];
+
+  __device__ void begin(const DecodeParams& p, int s, int kvh, int lane) {
+    const int piece = lane % LPR, g = p.group;
+    const raw* qb = static_cast<const raw*>(p.q) + ((size_t)s * p.num_heads + (size_t)kvh * g) * D;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (h < g) w = load16(qb + (size_t)h * D + piece * VEC);
+      Tr::widen(w, qv[h]);
+#pragma unroll
+      for (int st = 0; st < VSTEPS; ++st) acc[h][st] = 0.f;
+      m_run[h] = kNegInf;
+      l_run[h] = 0.f;
+    }
+  }
+
+  __device__ void chunk(const DecodeParams& p, Smem& sm, int kvh, int lane, int cs, int t1,
+                        ChunkIds ids, int lbl) {
+    const int B = p.block_size, lg = p.log2_block, Hkv = p.num_kv_heads;
+    const raw* __restrict__ kc = static_cast<const raw*>(p.k_cache);
+    const raw* __restrict__ vc = static_cast<const raw*>(p.v_cache);
+    const int piece = lane % LPR;
+    const int tg = lane % LPD, ddl = lane / LPD;
+
+    u32x4 kr[KSTEPS];
+#pragma unroll
+    for (int st = 0; st < KSTEPS; ++st) {
+      const int tok = cs + st * RPS + lane / LPR;
+      const int phys = pick_block(ids, tok, lg, lbl);
+      kr[st] = load16(kc + (((size_t)phys * Hkv + kvh) * B + (tok & (B - 1))) * D + piece * VEC);
+    }
+    const int tv = cs + tg * VEC;
+    const int physv = pick_block(ids, tv, lg, lbl);
+    const raw* vb = vc + (((size_t)physv * Hkv + kvh) * D + ddl) * B + (tv & (B - 1));
+    u32x4 vr[VSTEPS];
+#pragma unroll
+    for (int st = 0; st < VSTEPS; ++st) vr[st] = load16(vb + (size_t)st * DPS * B);
+
+    // QK
+#pragma unroll
+    for (int st = 0; st < KSTEPS; ++st) {
+      float kf[VEC];
+      Tr::widen(kr[st], kf);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) d = fmaf(qv[h][e], kf[e], d);
+#pragma unroll
+        for (int off = LPR / 2; off >= 1; off >>= 1) d += __shfl_xor(d, off);
+        if (piece == 0) sm.sc[h][st * RPS + lane / LPR] = d;
+      }
+    }
+    __syncthreads();
+
+    // softmax over the chunk's 32 tokens
+    const bool partial = cs + kChunk > t1;
+    float alpha[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const bool valid = lane < kChunk && cs + lane < t1;
+      const float sv = valid ? sm.sc[h][lane] * p.scale_log2 : kNegInf;
+      float cmax = sv;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) cmax = fmaxf(cmax, __shfl_xor(cmax, off));
+      const float m_new = fmaxf(m_run[h], cmax);
+      alpha[h] = fast_exp2(m_run[h] - m_new);
+      const float pv = fast_exp2(sv - m_new);
+      l_run[h] = l_run[h] * alpha[h] + pv;
+      m_run[h] = m_new;
+      if (lane < kChunk) sm.pl[h][lane] = pv;
+    }
+    __syncthreads();
+
+    // PV
+    float pw[G][VEC];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) pw[h][e] = sm.pl[h][tg * VEC + e];
+#pragma unroll
+    for (int st = 0; st < VSTEPS; ++st) {
+      u32x4 w = vr[st];
+      if (partial) w = Tr::keep_first(w, t1 - tv);
+      float vf[VEC];
+      Tr::widen(w, vf);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float a = acc[h][st] * alpha[h];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) a = fmaf(pw[h][e], vf[e], a);
+        acc[h][st] = a;
+      }
+    }
+    __syncthreads();  // sc/pl are rewritten by the next chunk
+  }
+
+  __device__ void finish(Smem& sm, int lane) {
+    const int tg = lane % LPD, ddl = lane / LPD;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int st = 0; st < VSTEPS; ++st) {
+        float v = acc[h][st];
+#pragma unroll
+        for (int off = LPD / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+        if (tg == 0) sm.o[h][st * DPS + ddl] = v;
+      }
+      float l = l_run[h];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
+      if (lane == 0) {
+        sm.ml[h][0] = m_run[h];
+        sm.ml[h][1] = l;
+      }
+    }
+    __syncthreads();
+  }
+
+  __device__ static float o_val(const Smem& sm, int h, int dd, int) { return sm.o[h][dd]; }
+  __device__ static float m_val(const Smem& sm, int h) { return sm.ml[h][0]; }
+  __device__ static float l_val(const Smem& sm, int h) { return sm.ml[h][1]; }
+};
+
+// ---------------------------------------------------------------------------
+// Segment driver, epilogue and merge (shared by both engines)
+// ---------------------------------------------------------------------------
+template <class Eng, int D>
+__device__ void write_zero_rows(const DecodeParams& p, int s, int kvh, int lane) {
+  const int g = p.group;
+  const size_t base = ((size_t)s * p.num_heads + (size_t)kvh * g) * D;
+  for (int idx = lane; idx < g * D; idx += 64) store_out(p.out, base + idx, 0.f, p.out_dtype);
+}
+
+template <int D>
+__device__ void merge_pieces(const DecodeParams& p, int s, int kvh, int lane, int first_slot, int npieces) {
+  const int g = p.group, Hq = p.num_heads;
+  for (int idx = lane; idx < g * D; idx += 64) {
+    const int h = idx / D, dd = idx % D;
+    const int head = kvh * g + h;
+    float M = kNegInf;
+    for (int k = 0; k < npieces; ++k)
+      M = fmaxf(M, p.ws_ml[((size_t)(first_slot + k) * Hq + head) * 2]);
+    float num = 0.f, den = 0.f;
+    for (int k = 0; k < npieces; ++k) {
+      const size_t r = (size_t)(first_slot + k) * Hq + head;
+      const float wgt = fast_exp2(p.ws_ml[r * 2] - M);
+      den = fmaf(wgt, p.ws_ml[r * 2 + 1], den);
+      num = fmaf(wgt, p.ws_acc[r * D + dd], num);
+    }
+    store_out(p.out, ((size_t)s * Hq + head) * D + dd, num / den, p.out_dtype);
+  }
+}
+
+template <class Eng, int D>
+__device__ void process_piece(const DecodeParams& p, typename Eng::Smem& sm, int s, int kvh, int lane,
+                              int t0, int t1, int npieces, int slot, int first_slot) {
+  const int32_t* __restrict__ tbl = p.block_tables + (size_t)s * p.max_blocks_per_seq;
+  const int lbl = (t1 - 1) >> p.log2_block;
+  Eng eng;
+  eng.begin(p, s, kvh, lane);
+  ChunkIds ids = load_chunk_ids(tbl, t0, lbl, p);
+  for (int cs = t0; cs < t1; cs += kChunk) {
+    ChunkIds next = ids;
+    if (cs + kChunk < t1) next = load_chunk_ids(tbl, cs + kChunk, lbl, p);
+    eng.chunk(p, sm, kvh, lane, cs, t1, ids, lbl);
+    ids = next;
+  }
+  eng.finish(sm, lane);
+
+  const int g = p.group, Hq = p.num_heads;
+  const size_t head0 = (size_t)kvh * g;
+  if (npieces == 1) {
+    const size_t base = ((size_t)s * Hq + head0) * D;
+    for (int idx = lane; idx < g * D; idx += 64) {
+      const int h = idx / D, dd = idx % D;
+      store_out(p.out, base + idx, Eng::o_val(sm, h, dd, g) / Eng::l_val(sm, h), p.out_dtype);
+    }
+    __syncthreads();
+    return;
+  }
+  const size_t row0 = (size_t)slot * Hq + head0;
+  for (int idx = lane; idx < g * D; idx += 64) {
+    const int h = idx / D, dd = idx % D;
+    p.ws_acc[row0 * D + idx] = Eng::o_val(sm, h, dd, g);
+  }
+  for (int h = lane; h < g; h += 64) {
+    p.ws_ml[(row0 + h) * 2] = Eng::m_val(sm, h);
+    p.ws_ml[(row0 + h) * 2 + 1] = Eng::l_val(sm, h);
+  }
+  __syncthreads();
+  // publish the partial, count arrivals; the last piece to arrive merges
+  __threadfence();
+  int* counter = p.counters + (size_t)s * p.num_kv_heads + kvh;
+  int arrived = 0;
+  if (lane == 0) arrived = atomicAdd(counter, 1);
+  arrived = __shfl(arrived, 0);
+  if (arrived == npieces - 1) {
+    __threadfence();
+    merge_pieces<D>(p, s, kvh, lane, first_slot, npieces);
+    if (lane == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+__device__ __forceinline__ long long owner_of(long long c, long long W, long long T) {
+  return ((c + 1) * W - 1) / T;
+}
+
+template <class Eng, int D>
+__global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
+  __shared__ typename Eng::Smem sm;
+  const int lane = threadIdx.x;
+  const int kvh = blockIdx.y;
+  const int w = blockIdx.x;
+  const int W = gridDim.x;
+
+  if (p.mode == kModeFixed) {
+    const int s = w / p.max_parts, part = w % p.max_parts;
+    const int P = p.part_chunks * kChunk;
+    // a context longer than max_parts partitions (longer than the host's
+    // bound) is cut there rather than left without a merging piece
+    const long long cap = (long long)p.max_parts * P;
+    const int L = (int)min((long long)eff_len(p, s), cap);
+    if (L <= 0) {
+      if (part == 0) write_zero_rows<Eng, D>(p, s, kvh, lane);
+      return;
+    }
+    const int t0 = part * P;
+    if (t0 >= L) return;
+    const int t1 = min(t0 + P, L);
+    const int np = (L + P - 1) / P;
+    process_piece<Eng, D>(p, sm, s, kvh, lane, t0, t1, np, s * p.max_parts + part, s * p.max_parts);
+    return;
+  }
+
+  // Balanced split: the chunks of all sequences (per KV head) are laid end
+  // to end; worker w takes chunks [w*T/W, (w+1)*T/W). Every worker scans the
+  // lengths itself (S <= kMaxBalancedSeqs), so no planning launch is needed.
+  const int S = p.num_seqs;
+  const int per = (S + 63) >> 6;
+  const int s_lo = min(lane * per, S), s_hi = min(s_lo + per, S);
+  long long mine = 0;
+  for (int s = s_lo; s < s_hi; ++s) mine += num_chunks(eff_len(p, s));
+  long long incl = mine;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const long long t = __shfl_up(incl, d);
+    if (lane >= d) incl += t;
+  }
+  const long long T = __shfl(incl, 63);
+  const long long excl = incl - mine;
+
+  for (int s = w; s < S; s += W)
+    if (eff_len(p, s) <= 0) write_zero_rows<Eng, D>(p, s, kvh, lane);
+  if (T == 0) return;
+  // with no more workers than chunks every range is non-empty, so the pieces
+  // of a sequence are exactly the workers owner_of(first chunk)..owner_of(last)
+  const long long Wn = (long long)W < T ? (long long)W : T;
+  if (w >= Wn) return;
+  const long long start = (long long)w * T / Wn, end = (long long)(w + 1) * T / Wn;
+
+  const unsigned long long ball = __ballot(start >= excl && start < incl);
+  if (ball == 0ull) return;  // unreachable while 0 <= start < T
+  const int owner = __builtin_ctzll(ball);
+  int s_first = 0;
+  long long c_first = 0;
+  if (lane == owner) {
+    long long c = excl;
+    for (int s = s_lo; s < s_hi; ++s) {
+      const int n = num_chunks(eff_len(p, s));
+      if (start < c + n) {
+        s_first = s;
+        c_first = c;
+        break;
+      }
+      c += n;
+    }
+  }
+  s_first = __shfl(s_first, owner);
+  c_first = __shfl(c_first, owner);
+
+  long long c = c_first;
+  for (int s = s_first; s < S && c < end; ++s) {
+    const int L = eff_len(p, s);
+    const int n = num_chunks(L);
+    if (n == 0) continue;
+    const long long c0 = start > c ? start : c;
+    const long long c1 = end < c + n ? end : c + n;
+    const int t0 = (int)(c0 - c) * kChunk;
+    const int t1 = min((int)(c1 - c) * kChunk, L);
+    const int first = (int)owner_of(c, Wn, T);
+    const int last = (int)owner_of(c + n - 1, Wn, T);
+    process_piece<Eng, D>(p, sm, s, kvh, lane, t0, t1, last - first + 1, w + s, first + s);
+    c += n;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// KV write, block copy, fill
+// ---------------------------------------------------------------------------
+template <typename U>
+__global__ __launch_bounds__(64) void write_kv_kernel(const U* __restrict__ k_new, const U* __restrict__ v_new,
+                                                      U* __restrict__ k_cache, U* __restrict__ v_cache,
+                                                      const int32_t* __restrict__ slots, int Hkv, int D, int B,
+                                                      long long total_slots) {
+  const int n = blockIdx.x, h = blockIdx.y;
+  const int slot = slots[n];
+  if (slot < 0 || (long long)slot >= total_slots) return;
+  const int phys = slot / B, off = slot % B;
+  const U* kr = k_new + ((size_t)n * Hkv + h) * D;
+  const U* vr = v_new + ((size_t)n * Hkv + h) * D;
+  U* kd = k_cache + (((size_t)phys * Hkv + h) * B + off) * D;
+  U* vd = v_cache + ((size_t)phys * Hkv + h) * D * B + off;
+  for (int i = threadIdx.x; i < D; i += 64) {
+    kd[i] = kr[i];
+    vd[(size_t)i * B] = vr[i];
+  }
+}
+
+template <typename U>
+__global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* k_cache, uint8_t* v_cache,
+                                                          const int32_t* __restrict__ mapping, int num_blocks,
+                                                          size_t block_bytes) {
+  const int pair = blockIdx.x;
+  const int src = mapping[2 * pair], dst = mapping[2 * pair + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  uint8_t* base = blockIdx.y ? v_cache : k_cache;
+  const U* s = reinterpret_cast<const U*>(base + (size_t)src * block_bytes);
+  U* d = reinterpret_cast<U*>(base + (size_t)dst * block_bytes);
+  const size_t n = block_bytes / sizeof(U);
+  for (size_t i = (size_t)blockIdx.z * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.z * blockDim.x)
+    d[i] = s[i];
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* ptr, size_t words) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (size_t)gridDim.x * blockDim.x)
+    ptr[i] = 0u;
+}
+
+// ---------------------------------------------------------------------------
+// Host-side dispatch
+// ---------------------------------------------------------------------------
+template <class Eng, int D>
+const void* kernel_of() {
+  return reinterpret_cast<const void*>(&decode_kernel<Eng, D>);
+}
+
+template <int E, int D>
+const void* vec_kernel(int G) {
+  switch (G) {
+    case 1: return kernel_of<VecEngine<E, D, 1>, D>();
+    case 2: return kernel_of<VecEngine<E, D, 2>, D>();
+    case 4: return kernel_of<VecEngine<E, D, 4>, D>();
+    case 8: return kernel_of<VecEngine<E, D, 8>, D>();
+    default: return nullptr;
+  }
+}
+
+template <int E>
+const void* vec_kernel_d(int D, int G) {
+  return D == 64 ? vec_kernel<E, 64>(G) : (D == 128 ? vec_kernel<E, 128>(G) : nullptr);
+}
+
+const void* decode_fn(int elem, int head_dim, int algo, int G) {
+  if (algo == kAlgoMfma) {
+    if (elem == kBF16) return head_dim == 64 ? kernel_of<MfmaEngine<kBF16, 64>, 64>()
+                                             : (head_dim == 128 ? kernel_of<MfmaEngine<kBF16, 128>, 128>() : nullptr);
+    if (elem == kF16) return head_dim == 64 ? kernel_of<MfmaEngine<kF16, 64>, 64>()
+                                            : (head_dim == 128 ? kernel_of<MfmaEngine<kF16, 128>, 128>() : nullptr);
+    return nullptr;
+  }
+  if (elem == kF32) return vec_kernel_d<kF32>(head_dim, G);
+  if (elem == kF16) return vec_kernel_d<kF16>(head_dim, G);
+  if (elem == kBF16) return vec_kernel_d<kBF16>(head_dim, G);
+  return nullptr;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeParams& p, int elem, int head_dim, int algo, int G, unsigned workers,
+                         hipStream_t stream) {
+  const void* fn = decode_fn(elem, head_dim, algo, G);
+  if (!fn) return hipErrorInvalidDeviceFunction;
+  DecodeParams args = p;
+  void* kargs[] = {&args};
+  return hipLaunchKernel(fn, dim3(workers, (unsigned)p.num_kv_heads, 1), dim3(64, 1, 1), kargs, 0, stream);
+}
+
+int decode_waves_per_cu(int elem, int head_dim, int algo, int G) {
+  const void* fn = decode_fn(elem, head_dim, algo, G);
+  if (!fn) return 0;
+  int blocks = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, 64, 0) != hipSuccess) return 0;
+  return blocks;
+}
+
+hipError_t launch_write_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cache, const int32_t* slots,
+                           int num_tokens, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                           int elem_bytes, hipStream_t stream) {
+  const dim3 grid((unsigned)num_tokens, (unsigned)num_kv_heads), block(64);
+  const long long total = (long long)num_blocks * block_size;
+  if (elem_bytes == 4) {
+    hipLaunchKernelGGL(write_kv_kernel<uint32_t>, grid, block, 0, stream, static_cast<const uint32_t*>(k_new),
+                       static_cast<const uint32_t*>(v_new), static_cast<uint32_t*>(k_cache),
+                       static_cast<uint32_t*>(v_cache), slots, num_kv_heads, head_dim, block_size, total);
+  } else {
+    hipLaunchKernelGGL(write_kv_kernel<uint16_t>, grid, block, 0, stream, static_cast<const uint16_t*>(k_new),
+                       static_cast<const uint16_t*>(v_new), static_cast<uint16_t*>(k_cache),
+                       static_cast<uint16_t*>(v_cache), slots, num_kv_heads, head_dim, block_size, total);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* mapping, int num_pairs, int num_blocks,
+                              size_t block_bytes, hipStream_t stream) {
+  uint8_t* k = static_cast<uint8_t*>(k_cache);
+  uint8_t* v = static_cast<uint8_t*>(v_cache);
+  if (block_bytes % 16 == 0) {
+    const size_t n = block_bytes / 16;
+    const unsigned slices = (unsigned)((n + 255) / 256 < 64 ? (n + 255) / 256 : 64);
+    hipLaunchKernelGGL(copy_blocks_kernel<u32x4>, dim3((unsigned)num_pairs, 2, slices), dim3(256), 0, stream, k, v,
+                       mapping, num_blocks, block_bytes);
+  } else {
+    const unsigned slices = (unsigned)((block_bytes + 255) / 256 < 64 ? (block_bytes + 255) / 256 : 64);
+    hipLaunchKernelGGL(copy_blocks_kernel<uint8_t>, dim3((unsigned)num_pairs, 2, slices), dim3(256), 0, stream, k, v,
+                       mapping, num_blocks, block_bytes);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream) {
+  const size_t words = bytes / 4;
+  if (words == 0) return hipSuccess;
+  const size_t want = (words + 255) / 256;
+  const unsigned blocks = (unsigned)(want < 1024 ? want : 1024);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, stream, static_cast<uint32_t*>(ptr), words);
+  return hipGetLastError();
+}
+
+}  // namespace pa

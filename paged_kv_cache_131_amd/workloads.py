@@ -8,7 +8,9 @@ both the CPU oracle (in tests) and the device library.
 Recipe per workload k (seed 1000 + k): numpy.random.SeedSequence(seed) spawns
 six streams, used in this order: lengths, pool permutation, q, K pool, V pool,
 new-token K/V. Values are float32 standard normals times `value_scale`,
-rounded to nearest-even into the stored type. Pools hold 10% more blocks than
+rounded to nearest-even into the stored type; an array is drawn in slices of
+2**22 elements, slice i from the i-th child of its stream (so slices can be
+drawn in parallel and the values do not depend on the thread count). Pools hold 10% more blocks than
 the sequences need (the tiny workload has a fixed pool of 32) and hand them out
 in the order of a seeded permutation, as on-demand allocation from a shuffled
 free pool would.
@@ -20,6 +22,8 @@ holding the raw bfloat16 bits.
 from __future__ import annotations
 
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -61,16 +65,35 @@ def poison_value(etype: str):
     return np.uint16(bits)
 
 
-def random_stored(rng: np.random.Generator, shape, etype: str, value_scale: float) -> np.ndarray:
-    """Standard normals * value_scale rounded to `etype`, drawn slice by slice."""
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def random_stored(seq: np.random.SeedSequence, shape, etype: str, value_scale: float) -> np.ndarray:
+    """Standard normals * value_scale rounded to `etype`; slice i of 2**22
+    values comes from the i-th child of `seq`."""
     n = int(np.prod(shape))
     out = np.empty(n, dtype=STORED_DTYPE[etype])
-    for lo in range(0, n, _SLICE):
-        hi = min(n, lo + _SLICE)
-        x = rng.standard_normal(hi - lo, dtype=np.float32)
+    nslices = -(-n // _SLICE)
+    children = seq.spawn(nslices)
+
+    def fill(i):
+        lo, hi = i * _SLICE, min(n, (i + 1) * _SLICE)
+        x = np.random.default_rng(children[i]).standard_normal(hi - lo, dtype=np.float32)
         if value_scale != 1.0:
             x *= np.float32(value_scale)
         out[lo:hi] = round_to(x, etype)
+
+    if nslices <= 1:
+        for i in range(nslices):
+            fill(i)
+    else:
+        with ThreadPoolExecutor(_threads()) as pool:
+            list(pool.map(fill, range(nslices)))
     return out.reshape(shape)
 
 
@@ -165,8 +188,9 @@ def make_decode_workload(cfg: DecodeConfig, lengths=None, poison: bool = True,
                          values: bool = True) -> DecodeWorkload:
     """Draw one decode step's inputs. With values=False only the integer
     inputs (lengths, block tables, slot mapping) are produced."""
-    streams = [np.random.default_rng(s) for s in np.random.SeedSequence(1000 + cfg.index).spawn(6)]
-    rng_len, rng_pool, rng_q, rng_k, rng_v, rng_new = streams
+    seqs = np.random.SeedSequence(1000 + cfg.index).spawn(6)
+    rng_len, rng_pool = np.random.default_rng(seqs[0]), np.random.default_rng(seqs[1])
+    ss_q, ss_k, ss_v, ss_new = seqs[2:]
     lens = draw_lengths(cfg, rng_len) if lengths is None else np.asarray(lengths, dtype=np.int32)
     if lens.shape != (cfg.num_seqs,) or lens.min() < 1:
         raise ValueError("one positive length per sequence is required")
@@ -192,11 +216,12 @@ def make_decode_workload(cfg: DecodeConfig, lengths=None, poison: bool = True,
     if not values:
         return DecodeWorkload(cfg, None, None, None, tables, lens.copy(), None, None, slots,
                               num_blocks, poison_block, used)
-    q = random_stored(rng_q, (cfg.num_seqs, cfg.num_heads, d), cfg.etype, cfg.value_scale)
-    k_cache = random_stored(rng_k, (num_blocks, Hkv, B, d), cfg.etype, cfg.value_scale)
-    v_cache = random_stored(rng_v, (num_blocks, Hkv, d, B), cfg.etype, cfg.value_scale)
-    k_new = random_stored(rng_new, (cfg.num_seqs, Hkv, d), cfg.etype, cfg.value_scale)
-    v_new = random_stored(rng_new, (cfg.num_seqs, Hkv, d), cfg.etype, cfg.value_scale)
+    q = random_stored(ss_q, (cfg.num_seqs, cfg.num_heads, d), cfg.etype, cfg.value_scale)
+    k_cache = random_stored(ss_k, (num_blocks, Hkv, B, d), cfg.etype, cfg.value_scale)
+    v_cache = random_stored(ss_v, (num_blocks, Hkv, d, B), cfg.etype, cfg.value_scale)
+    kn_ss, vn_ss = ss_new.spawn(2)
+    k_new = random_stored(kn_ss, (cfg.num_seqs, Hkv, d), cfg.etype, cfg.value_scale)
+    v_new = random_stored(vn_ss, (cfg.num_seqs, Hkv, d), cfg.etype, cfg.value_scale)
 
     if poison:
         pv = poison_value(cfg.etype)
@@ -244,8 +269,10 @@ class ParallelSamplingWorkload:
         self.cfg = cfg
         self.prompt_len, self.num_prompts, self.samples, self.new_tokens = prompt_len, num_prompts, samples, new_tokens
         self.values = values
-        streams = [np.random.default_rng(s) for s in np.random.SeedSequence(1000 + cfg.index).spawn(6)]
-        _, rng_pool, self.rng_q, rng_k, rng_v, self.rng_new = streams
+        seqs = np.random.SeedSequence(1000 + cfg.index).spawn(6)
+        rng_pool = np.random.default_rng(seqs[1])
+        ss_k, ss_v = seqs[3], seqs[4]
+        self.ss_q, self.ss_new = seqs[2], seqs[5]
         B = cfg.block_size
         used = self._dry_run_blocks()
         self.num_blocks = math.ceil(1.1 * used)
@@ -255,8 +282,8 @@ class ParallelSamplingWorkload:
         Hkv, d = cfg.num_kv_heads, cfg.head_dim
         self.k_cache = self.v_cache = None
         if values:
-            self.k_cache = random_stored(rng_k, (self.num_blocks, Hkv, B, d), cfg.etype, cfg.value_scale)
-            self.v_cache = random_stored(rng_v, (self.num_blocks, Hkv, d, B), cfg.etype, cfg.value_scale)
+            self.k_cache = random_stored(ss_k, (self.num_blocks, Hkv, B, d), cfg.etype, cfg.value_scale)
+            self.v_cache = random_stored(ss_v, (self.num_blocks, Hkv, d, B), cfg.etype, cfg.value_scale)
         self.seqs = []
         prompt_blocks = []
         for _ in range(num_prompts):
@@ -310,9 +337,12 @@ class ParallelSamplingWorkload:
         S, Hkv, d = self.num_seqs, cfg.num_kv_heads, cfg.head_dim
         q = k_new = v_new = None
         if self.values:
-            q = random_stored(self.rng_q, (S, cfg.num_heads, d), cfg.etype, cfg.value_scale)
-            k_new = random_stored(self.rng_new, (S, Hkv, d), cfg.etype, cfg.value_scale)
-            v_new = random_stored(self.rng_new, (S, Hkv, d), cfg.etype, cfg.value_scale)
+            # step t draws from child t-1 of the q and new-token streams
+            q_ss = self.ss_q.spawn(1)[0]
+            kn_ss, vn_ss = self.ss_new.spawn(1)[0].spawn(2)
+            q = random_stored(q_ss, (S, cfg.num_heads, d), cfg.etype, cfg.value_scale)
+            k_new = random_stored(kn_ss, (S, Hkv, d), cfg.etype, cfg.value_scale)
+            v_new = random_stored(vn_ss, (S, Hkv, d), cfg.etype, cfg.value_scale)
         tables = np.full((S, self.max_blocks), self.poison_block, dtype=np.int32)
         for i, seq in enumerate(self.seqs):
             tables[i, :len(seq.block_table)] = seq.block_table

@@ -1,0 +1,78 @@
+"""Model of the decode kernel's balanced split, checked exhaustively on small
+cases on the CPU: every 32-token chunk is covered by exactly one worker, the
+pieces the merge waits for are exactly the workers that contribute to the
+sequence, and partial-result slots are unique and inside the workspace the
+host sizes (workers + sequences). Fixed partitions likewise."""
+
+import itertools
+
+import numpy as np
+import pytest
+
+CHUNK = 32
+
+
+def balanced_plan(lengths, W):
+    n = [(L + CHUNK - 1) // CHUNK if L > 0 else 0 for L in lengths]
+    pref = np.concatenate([[0], np.cumsum(n)]).astype(np.int64)
+    T = int(pref[-1])
+    if T == 0:
+        return {}, {}
+    Wn = min(W, T)
+    owner = lambda c: ((c + 1) * Wn - 1) // T  # noqa: E731
+    pieces, expected = {}, {}
+    for w in range(Wn):
+        start, end = w * T // Wn, (w + 1) * T // Wn
+        assert start < end
+        # first sequence whose chunk range contains `start`
+        s = int(np.searchsorted(pref, start, side="right") - 1)
+        c = int(pref[s])
+        while s < len(lengths) and c < end:
+            if n[s] == 0:
+                s += 1
+                continue
+            c0, c1 = max(start, c), min(end, c + n[s])
+            first, last = owner(c), owner(c + n[s] - 1)
+            pieces.setdefault(s, []).append((w, c0, c1, w + s))
+            expected[s] = (first, last)
+            c += n[s]
+            s += 1
+    return pieces, expected
+
+
+@pytest.mark.parametrize("W", [1, 2, 3, 5, 8, 13, 64, 1000])
+def test_balanced_split_covers_each_chunk_once(W):
+    rng = np.random.default_rng(W)
+    for trial in range(60):
+        S = int(rng.integers(1, 12))
+        lengths = rng.integers(0, 300, size=S).tolist()
+        if trial % 7 == 0:
+            lengths[0] = 0
+        pieces, expected = balanced_plan(lengths, W)
+        slots = set()
+        for s, L in enumerate(lengths):
+            n = (L + CHUNK - 1) // CHUNK
+            if n == 0:
+                assert s not in pieces
+                continue
+            got = sorted(pieces[s])
+            covered = [c for (_, c0, c1, _) in got for c in range(c0, c1)]
+            base = min(c0 for (_, c0, _, _) in got)
+            assert covered == list(range(base, base + n))
+            first, last = expected[s]
+            workers = [w for (w, _, _, _) in got]
+            assert workers == list(range(first, last + 1)), (lengths, W)
+            for (_, _, _, slot) in got:
+                assert slot not in slots and 0 <= slot < W + S
+                slots.add(slot)
+
+
+def test_fixed_partitions_cover_each_token_once():
+    for L, P in itertools.product([1, 31, 32, 33, 511, 512, 513, 5000], [32, 64, 512]):
+        max_parts = (L + P - 1) // P
+        covered = []
+        for part in range(max_parts):
+            t0, t1 = part * P, min((part + 1) * P, L)
+            if t0 < L:
+                covered.extend(range(t0, t1))
+        assert covered == list(range(L))
