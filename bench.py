@@ -1,0 +1,224 @@
+"""Throughput of one decode step of the paged-KV hot path on one MI355X.
+
+A step = this step's copy-on-write block copies (none in this workload) +
+pa_write_kv of every sequence's new token + pa_decode over the paged cache,
+on seeded synthetic inputs already resident in HBM. Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload llama3_8b]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, vendor figure
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_131_amd", "csrc", f)
+                  for f in ("pa_kernels.hip", "pa_api.cpp", "pa_internal.h")]
+
+WORKLOAD_TEXT = {
+    "llama3_8b": "Llama-3-8B-shaped GQA decode: 256 seqs, 32 q / 8 kv heads, head_dim 128, block 16, bf16, "
+                 "lengths lognormal(median 800, sigma 1) clipped to [16, 8192], shuffled pool",
+    "opt13b": "OPT-13B-shaped decode: 64 seqs, 40 heads (MHA), head_dim 128, block 16, fp16, lengths U[128, 2048]",
+    "long_context": "long-context split decode: 16 seqs, 64 q / 8 kv heads, head_dim 128, block 32, bf16, "
+                    "lengths U[32768, 131072], 512-token partitions",
+}
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def decode_bytes(w) -> dict:
+    """Algorithmic bytes of one pa_decode call: K and V of every context token,
+    q, the fp32 output, the block ids read and the lengths."""
+    c = w.cfg
+    es = {"f32": 4, "f16": 2, "bf16": 2}[c.etype]
+    L = w.context_lens.astype(np.int64)
+    kv = int(L.sum()) * c.num_kv_heads * c.head_dim * 2 * es
+    q = c.num_seqs * c.num_heads * c.head_dim * es
+    out = c.num_seqs * c.num_heads * c.head_dim * 4
+    ids = 4 * int((-(-L // c.block_size)).sum())
+    lens = 4 * c.num_seqs
+    return {"kv": kv, "q": q, "out": out, "ids": ids, "lens": lens, "total": kv + q + out + ids + lens}
+
+
+def write_bytes(w) -> int:
+    c = w.cfg
+    es = {"f32": 4, "f16": 2, "bf16": 2}[c.etype]
+    T = len(w.slot_mapping)
+    return 2 * T * c.num_kv_heads * c.head_dim * es * 2 + 4 * T
+
+
+def cpu_baseline(w, budget_s: float) -> dict:
+    """The oracle, as it stands, on the first sequences of the same workload
+    until the time budget is spent (at least one sequence), BLAS pinned to one
+    thread."""
+    import oracle
+
+    from threadpoolctl import threadpool_limits
+
+    c = w.cfg
+    kr, vr = oracle.write_kv(w.k_cache, w.v_cache, w.k_new, w.v_new, w.slot_mapping, c.block_size)
+    done = 0
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        while done < c.num_seqs:
+            oracle.decode(w.q, kr, vr, w.block_tables, w.context_lens, c.scale, c.block_size, c.etype, seqs=[done])
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = time.perf_counter() - t0
+    es = {"f32": 4, "f16": 2, "bf16": 2}[c.etype]
+    kv = int(w.context_lens[:done].astype(np.int64).sum()) * c.num_kv_heads * c.head_dim * 2 * es
+    return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {done} of {c.num_seqs} sequences, all heads, {dt:.1f} s, "
+                      f"{done / dt:.2f} seq/s, float64 NumPy oracle"}
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(workload, {}).get(kernel)
+    if not entry or entry.get("kernel_hash") != kernel_hash():
+        return None
+    return entry.get("traffic_bytes")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama3_8b", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--algo", default="auto", choices=["auto", "vector", "mfma"])
+    ap.add_argument("--partition", type=int, default=None, help="partition size (-1 balanced, 0 none)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="run one plain device copy of this size first (traffic counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the decode path here has no "
+              "multi-GPU mode: per-GPU work is the single-GPU kernel on that GPU's share", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from paged_kv_cache_131_amd import binding as pb
+    from paged_kv_cache_131_amd import workloads as wl
+
+    pb.load_library()
+    dev = torch.device("cuda:0")
+    cfg = wl.CONFIGS[args.workload]
+    part = cfg.partition_size if args.partition is None else args.partition
+    t_gen = time.perf_counter()
+    w = wl.make_decode_workload(cfg)
+    gen_s = time.perf_counter() - t_gen
+    et = cfg.etype
+    kc, vc = pb.to_device(w.k_cache, et, dev), pb.to_device(w.v_cache, et, dev)
+    q = pb.to_device(w.q, et, dev)
+    k_new, v_new = pb.to_device(w.k_new, et, dev), pb.to_device(w.v_new, et, dev)
+    slots = pb.int32_to_device(w.slot_mapping, dev)
+    bt, cl = pb.int32_to_device(w.block_tables, dev), pb.int32_to_device(w.context_lens, dev)
+    copies = torch.empty((0, 2), dtype=torch.int32, device=dev)   # no shared blocks in this workload
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    max_len = w.max_context_len
+
+    if args.calibration_copy_mib:
+        n = args.calibration_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    def step(ev=None):
+        pb.pa_copy_blocks(kc, vc, copies)
+        pb.pa_write_kv(k_new, v_new, kc, vc, slots)
+        if ev is not None:
+            ev[0].record()
+        pb.pa_decode(out, q, kc, vc, bt, cl, cfg.scale, max_len, partition_size=part, algo=args.algo)
+        if ev is not None:
+            ev[1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    decode_ms = [a.elapsed_time(b) for a, b in events]
+
+    db = decode_bytes(w)
+    wb = write_bytes(w)
+    step_bytes = db["total"] + wb
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    decode_avg_ms = float(np.mean(decode_ms))
+    achieved = db["total"] / (decode_avg_ms * 1e-3) / 1e9
+    kernel = "decode_kernel"
+    traffic = traffic_for(kernel, args.workload)
+    result = {
+        "metric": "paged decode attention: achieved HBM GB/s (% of peak) + sequences/s at 1 GPU",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": et,
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD_TEXT[args.workload],
+            "num_seqs": cfg.num_seqs,
+            "context_tokens": int(w.context_lens.astype(np.int64).sum()),
+            "max_context_len": max_len,
+            "partition_size": part,
+            "algo": args.algo,
+            "step": "copy blocks (0 pairs) + write 1 token/seq + decode",
+        },
+        "sequences_per_s": round(cfg.num_seqs / (ms_per_step * 1e-3), 1),
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "step_bytes": step_bytes,
+        "decode": {"bytes": db, "avg_ms": round(decode_avg_ms, 5), "min_ms": round(float(np.min(decode_ms)), 5),
+                   "GBps": round(achieved, 1), "seq_per_s": round(cfg.num_seqs / (decode_avg_ms * 1e-3), 1)},
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "input_generation_s": round(gen_s, 2),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
