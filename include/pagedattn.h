@@ -110,15 +110,10 @@ pa_status pa_write_kv(const void* k_new, const void* v_new, void* k_cache, void*
  *                  exponentials ([review-en] "How does this work?": compute
  *                  per block, then combine the partial results).
  *   workspace    : device scratch of at least pa_decode_workspace_bytes(...)
- *                  bytes (may be NULL when that is 0). Its first
- *                  num_seqs*num_kv_heads int32 are arrival counters that
- *                  must be zero when a call starts; every call leaves them
- *                  zero, and leaves partial results in the bytes after them.
- *                  So zero the buffer after allocating it (e.g. with
- *                  pa_decode_workspace_init), and again before a call whose
- *                  num_seqs*num_kv_heads exceeds that of the previous call on
- *                  the same buffer. Calls that overlap in time must not share
- *                  a workspace.
+ *                  bytes (may be NULL when that is 0); no initial contents
+ *                  are required. Split sequences leave their partial results
+ *                  there and a second kernel on `stream` combines them, so
+ *                  calls that overlap in time must not share a workspace.
  *   Requirements: head_dim in {64, 128}; block_size in {8, 16, 32, 64, 128};
  *   num_heads % num_kv_heads == 0 and num_heads/num_kv_heads <= 8;
  *   PA_ALGO_MFMA needs dtype F16 or BF16.
@@ -147,10 +142,6 @@ pa_status pa_decode_ex(void* out, const void* q, const void* k_cache, const void
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_context_len,
                                  int32_t partition_size);
-
-/* Zero a decode workspace on `stream` (a fill kernel, so it may be captured
- * in a HIP graph). */
-pa_status pa_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * pa_copy_blocks -- batched whole-block copy for copy-on-write ([notes-zh]

@@ -32,7 +32,6 @@ SIGNATURES = {
     "pa_decode_ex": (_i32, [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                             _p, _sz, _i32, _i32, _i32, _p]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
-    "pa_decode_workspace_init": (_i32, [_p, _sz, _p]),
     "pa_copy_blocks": (_i32, [_p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p]),
     "pa_status_string": (ctypes.c_char_p, [_i32]),
     "pa_abi_version": (_i32, []),
@@ -120,42 +119,19 @@ def pa_decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_c
                                                         max_context_len, partition_size))
 
 
-def pa_decode_workspace_init(workspace: torch.Tensor, stream=None) -> None:
-    _check("pa_decode_workspace_init",
-           load_library().pa_decode_workspace_init(_dev(workspace, "workspace"), workspace.numel() *
-                                                   workspace.element_size(), _stream(stream)))
-
-
-class _Workspace:
-    """A decode workspace and the length of its prefix known to be zero.
-
-    A call needs its counter region (the first num_seqs*num_kv_heads int32)
-    zero at entry and leaves it zero; the bytes after it hold partial results
-    afterwards. A later call with a larger counter region would start on
-    those bytes, so the buffer is zeroed again first."""
-
-    def __init__(self, device, nbytes):
-        self.buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
-        self.clean = self.buf.numel()
-
-    def prepare(self, counter_bytes, stream=None):
-        if counter_bytes > self.clean:
-            pa_decode_workspace_init(self.buf, stream)
-        self.clean = counter_bytes
-
-
 _workspaces = {}
 
 
-def workspace_for(device, nbytes: int, counter_bytes: int, stream=None) -> torch.Tensor:
-    """A workspace of at least nbytes on `device` whose first counter_bytes
-    are zero, reused across calls on that device."""
+def workspace_for(device, nbytes: int) -> torch.Tensor:
+    """A workspace of at least nbytes on `device`, reused by calls on that
+    device (calls on one device through this binding are stream-ordered on
+    the current stream)."""
     key = torch.device(device)
     ws = _workspaces.get(key)
-    if ws is None or ws.buf.numel() < nbytes:
-        ws = _workspaces[key] = _Workspace(key, nbytes)
-    ws.prepare(counter_bytes, stream)
-    return ws.buf
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=key)
+        _workspaces[key] = ws
+    return ws
 
 
 def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
@@ -171,7 +147,7 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_c
     dt = k_cache.dtype
     need = int(lib.pa_decode_workspace_bytes(S, Hq, Hkv, d, int(max_context_len), int(partition_size)))
     if workspace is None and need:
-        workspace = workspace_for(q.device, need, S * Hkv * 4, stream)
+        workspace = workspace_for(q.device, need)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     status = lib.pa_decode_ex(

@@ -14,7 +14,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 constexpr size_t kAlign = 256;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -61,19 +61,19 @@ Plan make_plan(int num_seqs, int num_kv_heads, int max_context_len, int partitio
 }
 
 struct WorkspaceLayout {
-  size_t counters, ml, acc, total;
+  size_t meta, ml, acc, total;
 };
 
 WorkspaceLayout layout(const Plan& pl, int num_seqs, int num_heads, int num_kv_heads, int head_dim) {
   WorkspaceLayout w{0, 0, 0, 0};
   if (pl.slots == 0) return w;
-  const size_t counters = round_up((size_t)num_seqs * num_kv_heads * sizeof(int32_t));
+  const size_t meta = round_up((size_t)num_seqs * 2 * sizeof(int32_t));
   const size_t ml = round_up(pl.slots * (size_t)num_heads * 2 * sizeof(float));
   const size_t acc = round_up(pl.slots * (size_t)num_heads * head_dim * sizeof(float));
-  w.counters = 0;
-  w.ml = counters;
-  w.acc = counters + ml;
-  w.total = counters + ml + acc;
+  w.meta = 0;
+  w.ml = meta;
+  w.acc = meta + ml;
+  w.total = meta + ml + acc;
   return w;
 }
 
@@ -89,10 +89,15 @@ bool decode_shape_ok(int num_seqs, int num_heads, int num_kv_heads, int head_dim
 
 // Resident 64-thread waves per CU for each kernel, and CU counts, per device.
 constexpr int kMaxDevices = 64;
+constexpr int kMfmaWavesPerCu = 4;
 std::mutex g_mutex;
 int g_cus[kMaxDevices];
 int g_waves[kMaxDevices][3][2][3][9];  // [device][elem][head_dim 64/128][algo][G]
 
+// Balanced-split workers for one launch (all KV heads). The MFMA engine runs
+// one wave per SIMD: measured on MI355X, more resident waves of it split the
+// same bytes-in-flight over more pieces and lose bandwidth; the vector engine,
+// with more VALU work per byte, wants every resident wave.
 int workers_target(int elem, int head_dim, int algo, int G) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 2048;
@@ -106,6 +111,7 @@ int workers_target(int elem, int head_dim, int algo, int G) {
   if (waves == 0) {
     waves = pa::decode_waves_per_cu(elem, head_dim, algo, G);
     if (waves < 1) waves = 8;
+    if (algo == pa::kAlgoMfma && waves > kMfmaWavesPerCu) waves = kMfmaWavesPerCu;
   }
   return g_cus[dev] * waves;
 }
@@ -132,14 +138,6 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t nu
   if (!decode_shape_ok(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, partition_size)) return 0;
   const Plan pl = make_plan(num_seqs, num_kv_heads, max_context_len, partition_size);
   return layout(pl, num_seqs, num_heads, num_kv_heads, head_dim).total;
-}
-
-pa_status pa_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
-  if (workspace_bytes == 0) return PA_OK;
-  if (!workspace || !aligned(workspace, 4)) return PA_ERR_INVALID_ARG;
-  return pa::launch_fill_zero(workspace, workspace_bytes, static_cast<hipStream_t>(stream)) == hipSuccess
-             ? PA_OK
-             : PA_ERR_LAUNCH;
 }
 
 pa_status pa_write_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
@@ -230,7 +228,7 @@ pa_status pa_decode_ex(void* out, const void* q, const void* k_cache, const void
   p.block_tables = block_tables;
   p.context_lens = context_lens;
   char* ws = static_cast<char*>(workspace);
-  p.counters = wl.total ? reinterpret_cast<int32_t*>(ws + wl.counters) : nullptr;
+  p.ws_meta = wl.total ? reinterpret_cast<int32_t*>(ws + wl.meta) : nullptr;
   p.ws_ml = wl.total ? reinterpret_cast<float*>(ws + wl.ml) : nullptr;
   p.ws_acc = wl.total ? reinterpret_cast<float*>(ws + wl.acc) : nullptr;
   p.num_seqs = num_seqs;
@@ -258,7 +256,7 @@ pa_status pa_decode_ex(void* out, const void* q, const void* k_cache, const void
     workers = (long long)num_seqs * pl.max_parts;
     if (workers > INT_MAX) return PA_ERR_UNSUPPORTED;
   }
-  const hipError_t e = pa::launch_decode(p, elem, head_dim, kernel_algo, G, (unsigned)workers,
+  const hipError_t e = pa::launch_decode(p, elem, head_dim, kernel_algo, G, (unsigned)workers, pl.slots > 0,
                                          static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }

@@ -30,7 +30,7 @@ struct DecodeParams {
   const void* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  int32_t* counters;  // [num_seqs][num_kv_heads] arrival counters (split modes)
+  int32_t* ws_meta;   // [num_seqs][2] balanced split: (first slot, pieces) of each sequence
   float* ws_ml;       // [slots][num_heads][2]  (running max in log2 units, sum)
   float* ws_acc;      // [slots][num_heads][head_dim] (unnormalised output)
   int32_t num_seqs;
@@ -48,10 +48,12 @@ struct DecodeParams {
   int32_t out_dtype;    // Elem of `out`
 };
 
-// Launch the decode kernel for (elem, head_dim, algo, group bucket G).
-// grid = (workers per KV head, num_kv_heads), 64 threads per workgroup.
+// Launch the decode kernel for (elem, head_dim, algo, group bucket G),
+// grid = (workers per KV head, num_kv_heads), 64 threads per workgroup, then,
+// when `merge` is set, the kernel that combines the partial results of split
+// sequences (grid = (num_seqs, num_kv_heads)).
 hipError_t launch_decode(const DecodeParams& p, int elem, int head_dim, int algo, int G,
-                         unsigned workers, hipStream_t stream);
+                         unsigned workers, bool merge, hipStream_t stream);
 // Resident waves per CU of that kernel (0 if unknown).
 int decode_waves_per_cu(int elem, int head_dim, int algo, int G);
 
@@ -62,6 +64,5 @@ hipError_t launch_write_kv(const void* k_new, const void* v_new, void* k_cache, 
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* mapping, int num_pairs,
                               int num_blocks, size_t block_bytes, hipStream_t stream);
 
-hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream);
 
 }  // namespace pa

@@ -36,6 +36,11 @@ __device__ __forceinline__ u32x4 load16(const void* ptr) {
   return *reinterpret_cast<const u32x4*>(ptr);
 }
 
+// K/V tiles are read exactly once per launch: stream them past the caches.
+__device__ __forceinline__ u32x4 load16_stream(const void* ptr) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------
@@ -126,30 +131,36 @@ struct ChunkIds {
   int id0, id1, id2, id3;
 };
 
-__device__ __forceinline__ int table_entry(const int32_t* __restrict__ tbl, int lb, int lbl, int num_blocks) {
-  const int v = tbl[min(lb, lbl)];
-  return min(max(v, 0), num_blocks - 1);
+// The block table is read-only for the whole launch; reading it through the
+// constant address space lets wave-uniform reads use scalar loads, which are
+// counted apart from the K/V vector loads in flight.
+typedef const __attribute__((address_space(4))) int32_t const_i32;
+
+__device__ __forceinline__ int table_entry(const int32_t* tbl, int lb, int lbl) {
+  const const_i32* t = (const const_i32*)tbl;
+  return t[min(lb, lbl)];
 }
 
-__device__ __forceinline__ ChunkIds load_chunk_ids(const int32_t* __restrict__ tbl, int cs, int lbl,
-                                                   const DecodeParams& p) {
+// Raw entries of the (up to four) blocks of the chunk starting at `cs`,
+// loaded unconditionally and used (clamped) only when picked, so the loads
+// stay in flight until then.
+__device__ __forceinline__ ChunkIds load_chunk_ids(const int32_t* tbl, int cs, int lbl, const DecodeParams& p) {
   ChunkIds c;
   c.lb0 = cs >> p.log2_block;
-  const int nid = p.log2_block >= 5 ? 1 : (kChunk >> p.log2_block);
-  c.id0 = table_entry(tbl, c.lb0, lbl, p.num_blocks);
-  c.id1 = nid > 1 ? table_entry(tbl, c.lb0 + 1, lbl, p.num_blocks) : c.id0;
-  c.id2 = nid > 2 ? table_entry(tbl, c.lb0 + 2, lbl, p.num_blocks) : c.id1;
-  c.id3 = nid > 3 ? table_entry(tbl, c.lb0 + 3, lbl, p.num_blocks) : c.id2;
+  c.id0 = table_entry(tbl, c.lb0, lbl);
+  c.id1 = table_entry(tbl, c.lb0 + 1, lbl);
+  c.id2 = table_entry(tbl, c.lb0 + 2, lbl);
+  c.id3 = table_entry(tbl, c.lb0 + 3, lbl);
   return c;
 }
 
-__device__ __forceinline__ int pick_block(ChunkIds c, int tok, int log2_block, int lbl) {
+__device__ __forceinline__ int pick_block(ChunkIds c, int tok, int log2_block, int lbl, int num_blocks) {
   const int k = min(tok >> log2_block, lbl) - c.lb0;
   int id = c.id0;
   id = k >= 1 ? c.id1 : id;
   id = k >= 2 ? c.id2 : id;
   id = k >= 3 ? c.id3 : id;
-  return id;
+  return min(max(id, 0), num_blocks - 1);
 }
 
 __device__ __forceinline__ int eff_len(const DecodeParams& p, int s) {
@@ -177,12 +188,13 @@ __device__ __forceinline__ int num_chunks(int L) { return L > 0 ? (L + kChunk - 
 // two PV results are added at the end, so P enters the product with ~16
 // significant bits instead of 8.
 // ---------------------------------------------------------------------------
-template <int E, int D>
+template <int E, int D, int SUB>
 struct MfmaEngine {
   using Tr = ElemT<E>;
   using op8 = typename Tr::op8;
   using scalar = typename Tr::scalar;
   using raw = typename Tr::raw;
+  static constexpr int kSub = SUB;   // 32-token sub-chunks per step
   static constexpr int MQ = D / 32;  // QK k-steps
   static constexpr int NT = D / 16;  // PV column tiles
   static constexpr int kPad = 4;
@@ -212,65 +224,105 @@ struct MfmaEngine {
     l_run = 0.f;
   }
 
-  __device__ void chunk(const DecodeParams& p, Smem&, int kvh, int lane, int cs, int t1,
-                        ChunkIds ids, int lbl) {
-    const int col = lane & 15, grp = lane >> 4, g = p.group;
+  // registers of one step: K rows (A operands) and V columns (B operands)
+  // of SUB sub-chunks
+  struct Frag {
+    u32x4 ka[SUB][2][MQ];
+    u32x4 vr[SUB][NT];
+  };
+
+  __device__ void load_k(Frag& f, const DecodeParams& p, int kvh, int lane, int cs, const ChunkIds* ids,
+                         int lbl) const {
+    const int col = lane & 15, grp = lane >> 4;
     const int B = p.block_size, lg = p.log2_block, Hkv = p.num_kv_heads;
     const raw* __restrict__ kc = static_cast<const raw*>(p.k_cache);
-    const raw* __restrict__ vc = static_cast<const raw*>(p.v_cache);
-
     // K rows: A-operand row `col` of row group c holds token 8*(col/4)+4c+col%4
-    u32x4 ka[2][MQ];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int tok = cs + 8 * (col >> 2) + 4 * c + (col & 3);
-      const int phys = pick_block(ids, tok, lg, lbl);
-      const raw* row = kc + (((size_t)phys * Hkv + kvh) * B + (tok & (B - 1))) * D + 8 * grp;
+    for (int u = 0; u < SUB; ++u)
 #pragma unroll
-      for (int m = 0; m < MQ; ++m) ka[c][m] = load16(row + 32 * m);
-    }
-    // V: B operand, tokens 8*grp..+7 of the chunk at dd = 16j + col
-    const int tv = cs + 8 * grp;
-    const int physv = pick_block(ids, tv, lg, lbl);
-    const raw* vb = vc + (((size_t)physv * Hkv + kvh) * D + col) * B + (tv & (B - 1));
-    u32x4 vr[NT];
+      for (int c = 0; c < 2; ++c) {
+        const int tok = cs + kChunk * u + 8 * (col >> 2) + 4 * c + (col & 3);
+        const int phys = pick_block(ids[u], tok, lg, lbl, p.num_blocks);
+        const raw* row = kc + (((size_t)phys * Hkv + kvh) * B + (tok & (B - 1))) * D + 8 * grp;
 #pragma unroll
-    for (int j = 0; j < NT; ++j) vr[j] = load16(vb + (size_t)16 * j * B);
+        for (int m = 0; m < MQ; ++m) f.ka[u][c][m] = load16_stream(row + 32 * m);
+      }
+  }
 
-    // scores: lane holds tokens tv+0..7 of head slot `col`
-    f32x4 sc0 = {0.f, 0.f, 0.f, 0.f}, sc1 = {0.f, 0.f, 0.f, 0.f};
+  __device__ void load_v(Frag& f, const DecodeParams& p, int kvh, int lane, int cs, const ChunkIds* ids,
+                         int lbl) const {
+    const int col = lane & 15, grp = lane >> 4;
+    const int B = p.block_size, lg = p.log2_block, Hkv = p.num_kv_heads;
+    const raw* __restrict__ vc = static_cast<const raw*>(p.v_cache);
+    // V: B operand, tokens 8*grp..+7 of each sub-chunk at dd = 16j + col
 #pragma unroll
-    for (int m = 0; m < MQ; ++m) {
-      sc0 = mfma_16x16x32(__builtin_bit_cast(op8, ka[0][m]), qop[m], sc0);
-      sc1 = mfma_16x16x32(__builtin_bit_cast(op8, ka[1][m]), qop[m], sc1);
-    }
-    float sv[8];
+    for (int u = 0; u < SUB; ++u) {
+      const int tv = cs + kChunk * u + 8 * grp;
+      const int physv = pick_block(ids[u], tv, lg, lbl, p.num_blocks);
+      const raw* vb = vc + (((size_t)physv * Hkv + kvh) * D + col) * B + (tv & (B - 1));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sv[i] = sc0[i] * p.scale_log2;
-      sv[4 + i] = sc1[i] * p.scale_log2;
+      for (int j = 0; j < NT; ++j) f.vr[u][j] = load16_stream(vb + (size_t)16 * j * B);
     }
-    const bool partial = cs + kChunk > t1;
+  }
+
+  // Compute the step at `cs` from `f`; as soon as a register set is
+  // consumed it is refilled with the next step (K after QK, V after PV), so
+  // one step's loads are always in flight behind the math.
+  __device__ void step(Frag& f, const DecodeParams& p, Smem&, int kvh, int lane, int cs, int t1, bool has_next,
+                       const ChunkIds* ids_next, int lbl) {
+    const int col = lane & 15, grp = lane >> 4, g = p.group;
+    // scores: in sub-chunk u the lane holds tokens cs+32u+8*grp+0..7 of head slot `col`
+    f32x4 sc[SUB][2];
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) {
+      sc[u][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sc[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < MQ; ++m) {
+        sc[u][0] = mfma_16x16x32(__builtin_bit_cast(op8, f.ka[u][0][m]), qop[m], sc[u][0]);
+        sc[u][1] = mfma_16x16x32(__builtin_bit_cast(op8, f.ka[u][1][m]), qop[m], sc[u][1]);
+      }
+    }
+    // unconditional refill (the last step re-reads itself from L2) keeps the
+    // count of loads in flight the same on every path, so the PV wait below
+    // never has to drain the next step's K loads
+    const int cs_next = has_next ? cs + SUB * kChunk : cs;
+    load_k(f, p, kvh, lane, cs_next, ids_next, lbl);
+    float sv[SUB][8];
+#pragma unroll
+    for (int u = 0; u < SUB; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sv[u][i] = sc[u][0][i] * p.scale_log2;
+        sv[u][4 + i] = sc[u][1][i] * p.scale_log2;
+      }
+    const bool partial = cs + SUB * kChunk > t1;
     if (partial) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sv[e] = (tv + e < t1) ? sv[e] : kNegInf;
+      for (int u = 0; u < SUB; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sv[u][e] = (cs + kChunk * u + 8 * grp + e < t1) ? sv[u][e] : kNegInf;
     }
 
     // online softmax (base 2), per head slot
-    float cmax = sv[0];
+    float cmax = kNegInf;
 #pragma unroll
-    for (int e = 1; e < 8; ++e) cmax = fmaxf(cmax, sv[e]);
+    for (int u = 0; u < SUB; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) cmax = fmaxf(cmax, sv[u][e]);
     cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
     cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
     const float m_new = fmaxf(m_run, cmax);
     const float alpha = fast_exp2(m_run - m_new);
-    float pe[8];
+    float pe[SUB][8];
     float psum = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pe[e] = fast_exp2(sv[e] - m_new);
-      psum += pe[e];
-    }
+    for (int u = 0; u < SUB; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pe[u][e] = fast_exp2(sv[u][e] - m_new);
+        psum += pe[u][e];
+      }
     l_run = l_run * alpha + psum;
     m_run = m_new;
     if (__any(alpha != 1.f)) {
@@ -283,22 +335,26 @@ struct MfmaEngine {
       }
     }
 
-    // P operand: hi part, lo residual or zero depending on the head slot
-    op8 pa;
+    // P operands: hi part, lo residual or zero depending on the head slot
     const int part = col < g ? 0 : (col < 2 * g ? 1 : 2);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const scalar hi = static_cast<scalar>(pe[e]);
-      const scalar lo = static_cast<scalar>(pe[e] - static_cast<float>(hi));
-      pa[e] = part == 0 ? hi : (part == 1 ? lo : static_cast<scalar>(0.f));
-    }
-    if (partial) {
-      const int nvalid = t1 - tv;
+    for (int u = 0; u < SUB; ++u) {
+      op8 pa;
 #pragma unroll
-      for (int j = 0; j < NT; ++j) vr[j] = Tr::keep_first(vr[j], nvalid);
-    }
+      for (int e = 0; e < 8; ++e) {
+        const scalar hi = static_cast<scalar>(pe[u][e]);
+        const scalar lo = static_cast<scalar>(pe[u][e] - static_cast<float>(hi));
+        pa[e] = part == 0 ? hi : (part == 1 ? lo : static_cast<scalar>(0.f));
+      }
+      if (partial) {
+        const int nvalid = t1 - (cs + kChunk * u + 8 * grp);
 #pragma unroll
-    for (int j = 0; j < NT; ++j) o[j] = mfma_16x16x32(pa, __builtin_bit_cast(op8, vr[j]), o[j]);
+        for (int j = 0; j < NT; ++j) f.vr[u][j] = Tr::keep_first(f.vr[u][j], nvalid);
+      }
+#pragma unroll
+      for (int j = 0; j < NT; ++j) o[j] = mfma_16x16x32(pa, __builtin_bit_cast(op8, f.vr[u][j]), o[j]);
+    }
+    load_v(f, p, kvh, lane, cs_next, ids_next, lbl);
   }
 
   __device__ void finish(Smem& sm, int lane) {
@@ -340,6 +396,7 @@ struct VecEngine {
   static constexpr int LPD = kChunk / VEC;      // lanes per V dd-row of a chunk
   static constexpr int DPS = 64 / LPD;          // dd rows per V load step
   static constexpr int VSTEPS = D / DPS;        // V load steps per chunk
+  static constexpr int kSub = 1;
   struct Smem {
     float sc[G][kChunk];
     float pl[G][kChunk];
@@ -367,33 +424,49 @@ struct VecEngine {
     }
   }
 
-  __device__ void chunk(const DecodeParams& p, Smem& sm, int kvh, int lane, int cs, int t1,
-                        ChunkIds ids, int lbl) {
+  struct Frag {
+    u32x4 kr[KSTEPS];
+    u32x4 vr[VSTEPS];
+  };
+
+  __device__ void load_k(Frag& f, const DecodeParams& p, int kvh, int lane, int cs, const ChunkIds* idp,
+                         int lbl) const {
+    const ChunkIds ids = idp[0];
     const int B = p.block_size, lg = p.log2_block, Hkv = p.num_kv_heads;
     const raw* __restrict__ kc = static_cast<const raw*>(p.k_cache);
-    const raw* __restrict__ vc = static_cast<const raw*>(p.v_cache);
     const int piece = lane % LPR;
-    const int tg = lane % LPD, ddl = lane / LPD;
-
-    u32x4 kr[KSTEPS];
 #pragma unroll
     for (int st = 0; st < KSTEPS; ++st) {
       const int tok = cs + st * RPS + lane / LPR;
-      const int phys = pick_block(ids, tok, lg, lbl);
-      kr[st] = load16(kc + (((size_t)phys * Hkv + kvh) * B + (tok & (B - 1))) * D + piece * VEC);
+      const int phys = pick_block(ids, tok, lg, lbl, p.num_blocks);
+      f.kr[st] = load16_stream(kc + (((size_t)phys * Hkv + kvh) * B + (tok & (B - 1))) * D + piece * VEC);
     }
+  }
+
+  __device__ void load_v(Frag& f, const DecodeParams& p, int kvh, int lane, int cs, const ChunkIds* idp,
+                         int lbl) const {
+    const ChunkIds ids = idp[0];
+    const int B = p.block_size, lg = p.log2_block, Hkv = p.num_kv_heads;
+    const raw* __restrict__ vc = static_cast<const raw*>(p.v_cache);
+    const int tg = lane % LPD, ddl = lane / LPD;
     const int tv = cs + tg * VEC;
-    const int physv = pick_block(ids, tv, lg, lbl);
+    const int physv = pick_block(ids, tv, lg, lbl, p.num_blocks);
     const raw* vb = vc + (((size_t)physv * Hkv + kvh) * D + ddl) * B + (tv & (B - 1));
-    u32x4 vr[VSTEPS];
 #pragma unroll
-    for (int st = 0; st < VSTEPS; ++st) vr[st] = load16(vb + (size_t)st * DPS * B);
+    for (int st = 0; st < VSTEPS; ++st) f.vr[st] = load16_stream(vb + (size_t)st * DPS * B);
+  }
+
+  __device__ void step(Frag& f, const DecodeParams& p, Smem& sm, int kvh, int lane, int cs, int t1, bool has_next,
+                       const ChunkIds* ids_next, int lbl) {
+    const int piece = lane % LPR;
+    const int tg = lane % LPD;
+    const int tv = cs + tg * VEC;
 
     // QK
 #pragma unroll
     for (int st = 0; st < KSTEPS; ++st) {
       float kf[VEC];
-      Tr::widen(kr[st], kf);
+      Tr::widen(f.kr[st], kf);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float d = 0.f;
@@ -404,6 +477,7 @@ struct VecEngine {
         if (piece == 0) sm.sc[h][st * RPS + lane / LPR] = d;
       }
     }
+    load_k(f, p, kvh, lane, has_next ? cs + kChunk : cs, ids_next, lbl);
     __syncthreads();
 
     // softmax over the chunk's 32 tokens
@@ -433,7 +507,7 @@ struct VecEngine {
       for (int e = 0; e < VEC; ++e) pw[h][e] = sm.pl[h][tg * VEC + e];
 #pragma unroll
     for (int st = 0; st < VSTEPS; ++st) {
-      u32x4 w = vr[st];
+      u32x4 w = f.vr[st];
       if (partial) w = Tr::keep_first(w, t1 - tv);
       float vf[VEC];
       Tr::widen(w, vf);
@@ -445,6 +519,7 @@ struct VecEngine {
         acc[h][st] = a;
       }
     }
+    load_v(f, p, kvh, lane, has_next ? cs + kChunk : cs, ids_next, lbl);
     __syncthreads();  // sc/pl are rewritten by the next chunk
   }
 
@@ -508,16 +583,45 @@ __device__ void merge_pieces(const DecodeParams& p, int s, int kvh, int lane, in
 template <class Eng, int D>
 __device__ void process_piece(const DecodeParams& p, typename Eng::Smem& sm, int s, int kvh, int lane,
                               int t0, int t1, int npieces, int slot, int first_slot) {
+  // every argument is the same in all lanes; saying so lets table reads be
+  // scalar loads, counted apart from the K/V loads in flight
+  s = __builtin_amdgcn_readfirstlane(s);
+  t0 = __builtin_amdgcn_readfirstlane(t0);
+  t1 = __builtin_amdgcn_readfirstlane(t1);
+  npieces = __builtin_amdgcn_readfirstlane(npieces);
+  slot = __builtin_amdgcn_readfirstlane(slot);
+  first_slot = __builtin_amdgcn_readfirstlane(first_slot);
+  // the piece holding a sequence's first token records where its pieces are
+  // (single pieces too, so the merge kernel never reads a stale record)
+  if (p.mode == kModeBalanced && t0 == 0 && kvh == 0 && lane == 0) {
+    p.ws_meta[2 * s] = first_slot;
+    p.ws_meta[2 * s + 1] = npieces;
+  }
   const int32_t* __restrict__ tbl = p.block_tables + (size_t)s * p.max_blocks_per_seq;
   const int lbl = (t1 - 1) >> p.log2_block;
   Eng eng;
   eng.begin(p, s, kvh, lane);
-  ChunkIds ids = load_chunk_ids(tbl, t0, lbl, p);
-  for (int cs = t0; cs < t1; cs += kChunk) {
-    ChunkIds next = ids;
-    if (cs + kChunk < t1) next = load_chunk_ids(tbl, cs + kChunk, lbl, p);
-    eng.chunk(p, sm, kvh, lane, cs, t1, ids, lbl);
-    ids = next;
+  // One register set per step (kSub chunks), refilled inside step() as it
+  // is consumed; block ids are read two steps ahead with scalar loads.
+  constexpr int SUB = Eng::kSub;
+  constexpr int STEP = SUB * kChunk;
+  typename Eng::Frag f;
+  ChunkIds ids0[SUB], ids1[SUB], ids2[SUB];
+#pragma unroll
+  for (int u = 0; u < SUB; ++u) {
+    ids0[u] = load_chunk_ids(tbl, t0 + kChunk * u, lbl, p);
+    ids1[u] = t0 + STEP < t1 ? load_chunk_ids(tbl, t0 + STEP + kChunk * u, lbl, p) : ids0[u];
+  }
+  eng.load_k(f, p, kvh, lane, t0, ids0, lbl);
+  eng.load_v(f, p, kvh, lane, t0, ids0, lbl);
+  for (int cs = t0; cs < t1; cs += STEP) {
+    const bool has1 = cs + STEP < t1;
+#pragma unroll
+    for (int u = 0; u < SUB; ++u)
+      ids2[u] = cs + 2 * STEP < t1 ? load_chunk_ids(tbl, cs + 2 * STEP + kChunk * u, lbl, p) : ids1[u];
+    eng.step(f, p, sm, kvh, lane, cs, t1, has1, ids1, lbl);
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) ids1[u] = ids2[u];
   }
   eng.finish(sm, lane);
 
@@ -542,17 +646,6 @@ __device__ void process_piece(const DecodeParams& p, typename Eng::Smem& sm, int
     p.ws_ml[(row0 + h) * 2 + 1] = Eng::l_val(sm, h);
   }
   __syncthreads();
-  // publish the partial, count arrivals; the last piece to arrive merges
-  __threadfence();
-  int* counter = p.counters + (size_t)s * p.num_kv_heads + kvh;
-  int arrived = 0;
-  if (lane == 0) arrived = atomicAdd(counter, 1);
-  arrived = __shfl(arrived, 0);
-  if (arrived == npieces - 1) {
-    __threadfence();
-    merge_pieces<D>(p, s, kvh, lane, first_slot, npieces);
-    if (lane == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
 }
 
 __device__ __forceinline__ long long owner_of(long long c, long long W, long long T) {
@@ -648,8 +741,81 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
   }
 }
 
+// Combine the partial results of every split (sequence, KV head): the
+// pieces' maxima and exponential sums give piece k of head h the weight
+// w_k = 2^(m_k - M) / sum_j 2^(m_j - M) l_j with M = max_j m_j (base-2 units),
+// and out = sum_k w_k acc_k. Up to kMergeTile pieces the (m, l) pairs are
+// staged in LDS with one parallel load pass and every partial output is
+// loaded independently; longer piece lists take a plain per-output loop.
+constexpr int kMergeTile = 256;
+
+template <int D>
+__global__ __launch_bounds__(64) void merge_kernel(DecodeParams p) {
+  __shared__ float wgt[kMaxGroup][kMergeTile];
+  const int s = blockIdx.x, kvh = blockIdx.y, lane = threadIdx.x;
+  int L = eff_len(p, s);
+  int first_slot, npieces;
+  if (p.mode == kModeFixed) {
+    const int P = p.part_chunks * kChunk;
+    L = (int)min((long long)L, (long long)p.max_parts * P);
+    if (L <= 0) return;
+    npieces = (L + P - 1) / P;
+    first_slot = s * p.max_parts;
+  } else {
+    if (L <= 0) return;
+    first_slot = p.ws_meta[2 * s];
+    npieces = p.ws_meta[2 * s + 1];
+  }
+  if (npieces <= 1) return;
+  if (npieces > kMergeTile) {
+    merge_pieces<D>(p, s, kvh, lane, first_slot, npieces);
+    return;
+  }
+  const int g = p.group, Hq = p.num_heads;
+  const size_t head0 = (size_t)kvh * g;
+  // (m, l) of every (head, piece): m into wgt, l kept in the same slot's pair
+  __shared__ float ls[kMaxGroup][kMergeTile];
+  for (int i = lane; i < g * npieces; i += 64) {
+    const int h = i / npieces, k = i % npieces;
+    const size_t r = ((size_t)(first_slot + k) * Hq + head0 + h) * 2;
+    wgt[h][k] = p.ws_ml[r];
+    ls[h][k] = p.ws_ml[r + 1];
+  }
+  __syncthreads();
+  if (lane < g) {
+    float M = kNegInf;
+    for (int k = 0; k < npieces; ++k) M = fmaxf(M, wgt[lane][k]);
+    float den = 0.f;
+    for (int k = 0; k < npieces; ++k) {
+      const float e = fast_exp2(wgt[lane][k] - M);
+      wgt[lane][k] = e;
+      den = fmaf(e, ls[lane][k], den);
+    }
+    const float inv = 1.f / den;
+    for (int k = 0; k < npieces; ++k) wgt[lane][k] *= inv;
+  }
+  __syncthreads();
+  constexpr int PER = D / 64;
+  for (int h = 0; h < g; ++h) {
+    float acc[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+    const float* base = p.ws_acc + ((size_t)first_slot * Hq + head0 + h) * D + lane;
+    const size_t step = (size_t)Hq * D;
+#pragma unroll 4
+    for (int k = 0; k < npieces; ++k) {
+      const float w = wgt[h][k];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, base[k * step + 64 * i], acc[i]);
+    }
+    const size_t o = ((size_t)s * Hq + head0 + h) * D + lane;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) store_out(p.out, o + 64 * i, acc[i], p.out_dtype);
+  }
+}
+
 // ---------------------------------------------------------------------------
-// KV write, block copy, fill
+// KV write, block copy
 // ---------------------------------------------------------------------------
 template <typename U>
 __global__ __launch_bounds__(64) void write_kv_kernel(const U* __restrict__ k_new, const U* __restrict__ v_new,
@@ -685,14 +851,13 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* k_cache, uint
     d[i] = s[i];
 }
 
-__global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* ptr, size_t words) {
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (size_t)gridDim.x * blockDim.x)
-    ptr[i] = 0u;
-}
-
 // ---------------------------------------------------------------------------
 // Host-side dispatch
 // ---------------------------------------------------------------------------
+// 32-token sub-chunks per MFMA step. Two (32 KiB of K/V in flight per wave)
+// measured slower on MI355X than one: bytes in flight are not the limit.
+constexpr int kMfmaSub = 1;
+
 template <class Eng, int D>
 const void* kernel_of() {
   return reinterpret_cast<const void*>(&decode_kernel<Eng, D>);
@@ -716,10 +881,10 @@ const void* vec_kernel_d(int D, int G) {
 
 const void* decode_fn(int elem, int head_dim, int algo, int G) {
   if (algo == kAlgoMfma) {
-    if (elem == kBF16) return head_dim == 64 ? kernel_of<MfmaEngine<kBF16, 64>, 64>()
-                                             : (head_dim == 128 ? kernel_of<MfmaEngine<kBF16, 128>, 128>() : nullptr);
-    if (elem == kF16) return head_dim == 64 ? kernel_of<MfmaEngine<kF16, 64>, 64>()
-                                            : (head_dim == 128 ? kernel_of<MfmaEngine<kF16, 128>, 128>() : nullptr);
+    if (elem == kBF16) return head_dim == 64 ? kernel_of<MfmaEngine<kBF16, 64, kMfmaSub>, 64>()
+                                             : (head_dim == 128 ? kernel_of<MfmaEngine<kBF16, 128, kMfmaSub>, 128>() : nullptr);
+    if (elem == kF16) return head_dim == 64 ? kernel_of<MfmaEngine<kF16, 64, kMfmaSub>, 64>()
+                                            : (head_dim == 128 ? kernel_of<MfmaEngine<kF16, 128, kMfmaSub>, 128>() : nullptr);
     return nullptr;
   }
   if (elem == kF32) return vec_kernel_d<kF32>(head_dim, G);
@@ -731,12 +896,17 @@ const void* decode_fn(int elem, int head_dim, int algo, int G) {
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams& p, int elem, int head_dim, int algo, int G, unsigned workers,
-                         hipStream_t stream) {
+                         bool merge, hipStream_t stream) {
   const void* fn = decode_fn(elem, head_dim, algo, G);
   if (!fn) return hipErrorInvalidDeviceFunction;
   DecodeParams args = p;
   void* kargs[] = {&args};
-  return hipLaunchKernel(fn, dim3(workers, (unsigned)p.num_kv_heads, 1), dim3(64, 1, 1), kargs, 0, stream);
+  hipError_t e = hipLaunchKernel(fn, dim3(workers, (unsigned)p.num_kv_heads, 1), dim3(64, 1, 1), kargs, 0, stream);
+  if (e != hipSuccess || !merge) return e;
+  const void* mf = head_dim == 64 ? reinterpret_cast<const void*>(&merge_kernel<64>)
+                                  : reinterpret_cast<const void*>(&merge_kernel<128>);
+  return hipLaunchKernel(mf, dim3((unsigned)p.num_seqs, (unsigned)p.num_kv_heads, 1), dim3(64, 1, 1), kargs, 0,
+                         stream);
 }
 
 int decode_waves_per_cu(int elem, int head_dim, int algo, int G) {
@@ -778,15 +948,6 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* mappi
     hipLaunchKernelGGL(copy_blocks_kernel<uint8_t>, dim3((unsigned)num_pairs, 2, slices), dim3(256), 0, stream, k, v,
                        mapping, num_blocks, block_bytes);
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream) {
-  const size_t words = bytes / 4;
-  if (words == 0) return hipSuccess;
-  const size_t want = (words + 255) / 256;
-  const unsigned blocks = (unsigned)(want < 1024 ? want : 1024);
-  hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, stream, static_cast<uint32_t*>(ptr), words);
   return hipGetLastError();
 }
 

@@ -43,7 +43,7 @@ def test_exports_match_header(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.pa_abi_version() == 1
+    assert lib.pa_abi_version() == 2
     assert lib.pa_status_string(OK) == b"ok"
     assert lib.pa_status_string(WORKSPACE) == b"workspace missing or too small"
     assert lib.pa_status_string(123) == b"unknown status"
@@ -88,7 +88,7 @@ def test_decode_workspace_sizes(lib):
     assert f(4, 32, 8, 128, 1024, 0) == 0                  # single pass never splits
     assert f(4, 32, 8, 128, 512, 512) == 0                 # one partition per sequence
     two = f(4, 32, 8, 128, 1024, 512)                      # 2 partitions x 4 seqs = 8 slots
-    assert two == 256 + 8 * 32 * 2 * 4 + 8 * 32 * 128 * 4   # counters, (m, l), partial outputs
+    assert two == 256 + 8 * 32 * 2 * 4 + 8 * 32 * 128 * 4   # split records, (m, l), partial outputs
     auto = f(256, 32, 8, 128, 8192, -1)
     assert auto >= (1024 + 256) * 32 * 130 * 4             # balanced: workers + sequences slots
     assert f(4, 30, 8, 128, 1024, -1) == 0                 # rejected shape
@@ -108,8 +108,6 @@ def test_write_and_copy_argument_checks(lib):
     assert c(FAKE, FAKE, None, 2, 8, 128, 16, 10, 2, None) == INVALID
     assert c(FAKE, FAKE, FAKE, -2, 8, 128, 16, 10, 2, None) == INVALID
     assert c(FAKE + 4, FAKE, FAKE, 2, 8, 128, 16, 10, 2, None) == INVALID
-    assert lib.pa_decode_workspace_init(None, 0, None) == OK
-    assert lib.pa_decode_workspace_init(None, 64, None) == INVALID
 
 
 def test_binding_refuses_host_tensors(lib):
