@@ -168,6 +168,14 @@ __device__ __forceinline__ int eff_len(const DecodeParams& p, int s) {
   return min(p.context_lens[s], cap);
 }
 
+// The same for a wave-uniform s, read with a scalar load so that it never
+// waits behind the K/V vector loads in flight.
+__device__ __forceinline__ int eff_len_uniform(const DecodeParams& p, int s) {
+  const int cap = p.max_blocks_per_seq << p.log2_block;
+  const const_i32* lens = (const const_i32*)p.context_lens;
+  return min(lens[__builtin_amdgcn_readfirstlane(s)], cap);
+}
+
 __device__ __forceinline__ int num_chunks(int L) { return L > 0 ? (L + kChunk - 1) / kChunk : 0; }
 
 // ---------------------------------------------------------------------------
@@ -208,7 +216,12 @@ struct MfmaEngine {
   float m_run;
   float l_run;
 
-  __device__ void begin(const DecodeParams& p, int s, int kvh, int lane) {
+  // q of one sequence as the QK B operand (columns = head slots)
+  struct Q {
+    u32x4 w[MQ];
+  };
+
+  __device__ void load_q(Q& q, const DecodeParams& p, int s, int kvh, int lane) const {
     const int col = lane & 15, grp = lane >> 4, g = p.group;
     const int hs = col < g ? col : (col < 2 * g ? col - g : -1);
     const raw* qb = static_cast<const raw*>(p.q) + ((size_t)s * p.num_heads + (size_t)kvh * g) * D;
@@ -216,8 +229,13 @@ struct MfmaEngine {
     for (int m = 0; m < MQ; ++m) {
       u32x4 w = {0u, 0u, 0u, 0u};
       if (hs >= 0) w = load16(qb + (size_t)hs * D + 32 * m + 8 * grp);
-      qop[m] = __builtin_bit_cast(op8, w);
+      q.w[m] = w;
     }
+  }
+
+  __device__ void reset(const Q& q) {
+#pragma unroll
+    for (int m = 0; m < MQ; ++m) qop[m] = __builtin_bit_cast(op8, q.w[m]);
 #pragma unroll
     for (int j = 0; j < NT; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_run = kNegInf;
@@ -268,8 +286,8 @@ struct MfmaEngine {
   // Compute the step at `cs` from `f`; as soon as a register set is
   // consumed it is refilled with the next step (K after QK, V after PV), so
   // one step's loads are always in flight behind the math.
-  __device__ void step(Frag& f, const DecodeParams& p, Smem&, int kvh, int lane, int cs, int t1, bool has_next,
-                       const ChunkIds* ids_next, int lbl) {
+  __device__ void step(Frag& f, const DecodeParams& p, Smem&, int kvh, int lane, int cs, int t1, int cs_next,
+                       const ChunkIds* ids_next, int lbl_next) {
     const int col = lane & 15, grp = lane >> 4, g = p.group;
     // scores: in sub-chunk u the lane holds tokens cs+32u+8*grp+0..7 of head slot `col`
     f32x4 sc[SUB][2];
@@ -283,11 +301,10 @@ struct MfmaEngine {
         sc[u][1] = mfma_16x16x32(__builtin_bit_cast(op8, f.ka[u][1][m]), qop[m], sc[u][1]);
       }
     }
-    // unconditional refill (the last step re-reads itself from L2) keeps the
-    // count of loads in flight the same on every path, so the PV wait below
-    // never has to drain the next step's K loads
-    const int cs_next = has_next ? cs + SUB * kChunk : cs;
-    load_k(f, p, kvh, lane, cs_next, ids_next, lbl);
+    // unconditional refill (at the end of the stream the last step re-reads
+    // itself from L2) keeps the count of loads in flight the same on every
+    // path, so the PV wait below never has to drain the next step's K loads
+    load_k(f, p, kvh, lane, cs_next, ids_next, lbl_next);
     float sv[SUB][8];
 #pragma unroll
     for (int u = 0; u < SUB; ++u)
@@ -354,7 +371,7 @@ struct MfmaEngine {
 #pragma unroll
       for (int j = 0; j < NT; ++j) o[j] = mfma_16x16x32(pa, __builtin_bit_cast(op8, f.vr[u][j]), o[j]);
     }
-    load_v(f, p, kvh, lane, cs_next, ids_next, lbl);
+    load_v(f, p, kvh, lane, cs_next, ids_next, lbl_next);
   }
 
   __device__ void finish(Smem& sm, int lane) {
@@ -409,14 +426,25 @@ struct VecEngine {
   float m_run[G];
   float l_run[G];
 
-  __device__ void begin(const DecodeParams& p, int s, int kvh, int lane) {
+  struct Q {
+    u32x4 w[G];
+  };
+
+  __device__ void load_q(Q& q, const DecodeParams& p, int s, int kvh, int lane) const {
     const int piece = lane % LPR, g = p.group;
     const raw* qb = static_cast<const raw*>(p.q) + ((size_t)s * p.num_heads + (size_t)kvh * g) * D;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       u32x4 w = {0u, 0u, 0u, 0u};
       if (h < g) w = load16(qb + (size_t)h * D + piece * VEC);
-      Tr::widen(w, qv[h]);
+      q.w[h] = w;
+    }
+  }
+
+  __device__ void reset(const Q& q) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      Tr::widen(q.w[h], qv[h]);
 #pragma unroll
       for (int st = 0; st < VSTEPS; ++st) acc[h][st] = 0.f;
       m_run[h] = kNegInf;
@@ -456,8 +484,8 @@ struct VecEngine {
     for (int st = 0; st < VSTEPS; ++st) f.vr[st] = load16_stream(vb + (size_t)st * DPS * B);
   }
 
-  __device__ void step(Frag& f, const DecodeParams& p, Smem& sm, int kvh, int lane, int cs, int t1, bool has_next,
-                       const ChunkIds* ids_next, int lbl) {
+  __device__ void step(Frag& f, const DecodeParams& p, Smem& sm, int kvh, int lane, int cs, int t1, int cs_next,
+                       const ChunkIds* ids_next, int lbl_next) {
     const int piece = lane % LPR;
     const int tg = lane % LPD;
     const int tv = cs + tg * VEC;
@@ -477,7 +505,7 @@ struct VecEngine {
         if (piece == 0) sm.sc[h][st * RPS + lane / LPR] = d;
       }
     }
-    load_k(f, p, kvh, lane, has_next ? cs + kChunk : cs, ids_next, lbl);
+    load_k(f, p, kvh, lane, cs_next, ids_next, lbl_next);
     __syncthreads();
 
     // softmax over the chunk's 32 tokens
@@ -519,7 +547,7 @@ struct VecEngine {
         acc[h][st] = a;
       }
     }
-    load_v(f, p, kvh, lane, has_next ? cs + kChunk : cs, ids_next, lbl);
+    load_v(f, p, kvh, lane, cs_next, ids_next, lbl_next);
     __syncthreads();  // sc/pl are rewritten by the next chunk
   }
 
@@ -580,76 +608,187 @@ __device__ void merge_pieces(const DecodeParams& p, int s, int kvh, int lane, in
   }
 }
 
-template <class Eng, int D>
-__device__ void process_piece(const DecodeParams& p, typename Eng::Smem& sm, int s, int kvh, int lane,
-                              int t0, int t1, int npieces, int slot, int first_slot) {
-  // every argument is the same in all lanes; saying so lets table reads be
-  // scalar loads, counted apart from the K/V loads in flight
-  s = __builtin_amdgcn_readfirstlane(s);
-  t0 = __builtin_amdgcn_readfirstlane(t0);
-  t1 = __builtin_amdgcn_readfirstlane(t1);
-  npieces = __builtin_amdgcn_readfirstlane(npieces);
-  slot = __builtin_amdgcn_readfirstlane(slot);
-  first_slot = __builtin_amdgcn_readfirstlane(first_slot);
-  // the piece holding a sequence's first token records where its pieces are
-  // (single pieces too, so the merge kernel never reads a stale record)
-  if (p.mode == kModeBalanced && t0 == 0 && kvh == 0 && lane == 0) {
-    p.ws_meta[2 * s] = first_slot;
-    p.ws_meta[2 * s + 1] = npieces;
-  }
-  const int32_t* __restrict__ tbl = p.block_tables + (size_t)s * p.max_blocks_per_seq;
-  const int lbl = (t1 - 1) >> p.log2_block;
-  Eng eng;
-  eng.begin(p, s, kvh, lane);
-  // One register set per step (kSub chunks), refilled inside step() as it
-  // is consumed; block ids are read two steps ahead with scalar loads.
-  constexpr int SUB = Eng::kSub;
-  constexpr int STEP = SUB * kChunk;
-  typename Eng::Frag f;
-  ChunkIds ids0[SUB], ids1[SUB], ids2[SUB];
-#pragma unroll
-  for (int u = 0; u < SUB; ++u) {
-    ids0[u] = load_chunk_ids(tbl, t0 + kChunk * u, lbl, p);
-    ids1[u] = t0 + STEP < t1 ? load_chunk_ids(tbl, t0 + STEP + kChunk * u, lbl, p) : ids0[u];
-  }
-  eng.load_k(f, p, kvh, lane, t0, ids0, lbl);
-  eng.load_v(f, p, kvh, lane, t0, ids0, lbl);
-  for (int cs = t0; cs < t1; cs += STEP) {
-    const bool has1 = cs + STEP < t1;
-#pragma unroll
-    for (int u = 0; u < SUB; ++u)
-      ids2[u] = cs + 2 * STEP < t1 ? load_chunk_ids(tbl, cs + 2 * STEP + kChunk * u, lbl, p) : ids1[u];
-    eng.step(f, p, sm, kvh, lane, cs, t1, has1, ids1, lbl);
-#pragma unroll
-    for (int u = 0; u < SUB; ++u) ids1[u] = ids2[u];
-  }
-  eng.finish(sm, lane);
+// One worker's share of one sequence (all values wave-uniform).
+struct Segment {
+  int s, t0, t1, lbl, npieces, slot, first_slot;
+  int valid;
+};
 
-  const int g = p.group, Hq = p.num_heads;
-  const size_t head0 = (size_t)kvh * g;
-  if (npieces == 1) {
-    const size_t base = ((size_t)s * Hq + head0) * D;
-    for (int idx = lane; idx < g * D; idx += 64) {
-      const int h = idx / D, dd = idx % D;
-      store_out(p.out, base + idx, Eng::o_val(sm, h, dd, g) / Eng::l_val(sm, h), p.out_dtype);
-    }
-    __syncthreads();
-    return;
-  }
-  const size_t row0 = (size_t)slot * Hq + head0;
-  for (int idx = lane; idx < g * D; idx += 64) {
-    const int h = idx / D, dd = idx % D;
-    p.ws_acc[row0 * D + idx] = Eng::o_val(sm, h, dd, g);
-  }
-  for (int h = lane; h < g; h += 64) {
-    p.ws_ml[(row0 + h) * 2] = Eng::m_val(sm, h);
-    p.ws_ml[(row0 + h) * 2 + 1] = Eng::l_val(sm, h);
-  }
-  __syncthreads();
+__device__ __forceinline__ Segment invalid_segment() {
+  Segment g;
+  g.s = g.t0 = g.t1 = g.lbl = g.npieces = g.slot = g.first_slot = 0;
+  g.valid = 0;
+  return g;
+}
+
+__device__ __forceinline__ Segment uniform(Segment g) {
+  g.s = __builtin_amdgcn_readfirstlane(g.s);
+  g.t0 = __builtin_amdgcn_readfirstlane(g.t0);
+  g.t1 = __builtin_amdgcn_readfirstlane(g.t1);
+  g.lbl = __builtin_amdgcn_readfirstlane(g.lbl);
+  g.npieces = __builtin_amdgcn_readfirstlane(g.npieces);
+  g.slot = __builtin_amdgcn_readfirstlane(g.slot);
+  g.first_slot = __builtin_amdgcn_readfirstlane(g.first_slot);
+  g.valid = __builtin_amdgcn_readfirstlane(g.valid);
+  return g;
 }
 
 __device__ __forceinline__ long long owner_of(long long c, long long W, long long T) {
   return ((c + 1) * W - 1) / T;
+}
+
+// Yields a worker's segments in order. Balanced mode: the chunks of all
+// sequences (per KV head) are laid end to end and worker w owns chunks
+// [start, end); fixed mode: a single partition.
+struct SegmentSource {
+  int mode;
+  int s;          // next sequence to look at (balanced) / the sequence (fixed)
+  long long c;    // first chunk of sequence s in the laid-out order
+  long long start, end, W, T;
+  int w;
+  Segment fixed;  // fixed mode's only segment
+
+  __device__ Segment next(const DecodeParams& p) {
+    if (mode == kModeFixed) {
+      const Segment g = fixed;
+      fixed.valid = 0;
+      return g;
+    }
+    while (s < p.num_seqs && c < end) {
+      const int L = eff_len_uniform(p, s);
+      const int n = num_chunks(L);
+      if (n == 0) {
+        ++s;
+        continue;
+      }
+      const long long c0 = start > c ? start : c;
+      const long long c1 = end < c + n ? end : c + n;
+      Segment g;
+      g.s = s;
+      g.t0 = (int)(c0 - c) * kChunk;
+      g.t1 = min((int)(c1 - c) * kChunk, L);
+      g.lbl = (g.t1 - 1) >> p.log2_block;
+      const int first = (int)owner_of(c, W, T);
+      const int last = (int)owner_of(c + n - 1, W, T);
+      g.npieces = last - first + 1;
+      g.slot = w + s;
+      g.first_slot = first + s;
+      g.valid = 1;
+      c += n;
+      ++s;
+      return uniform(g);
+    }
+    return invalid_segment();
+  }
+};
+
+// A position in the worker's chunk stream: segment rel (0 = current, 1 =
+// next, 2 = the one after) and the chunk's first token.
+struct Pos {
+  int rel;
+  int cs;
+};
+
+__device__ __forceinline__ Segment seg_at(int rel, const Segment& a, const Segment& b, const Segment& c) {
+  return rel == 0 ? a : (rel == 1 ? b : c);
+}
+
+// The chunk after x; at the end of the stream x itself (its refill then
+// re-reads data already in L2).
+__device__ __forceinline__ Pos advance(Pos x, const Segment& a, const Segment& b, const Segment& c) {
+  const Segment g = seg_at(x.rel, a, b, c);
+  if (x.cs + kChunk < g.t1) return Pos{x.rel, x.cs + kChunk};
+  if (x.rel < 2) {
+    const Segment n = seg_at(x.rel + 1, a, b, c);
+    if (n.valid) return Pos{x.rel + 1, n.t0};
+  }
+  return x;
+}
+
+__device__ __forceinline__ ChunkIds ids_at(const DecodeParams& p, Pos x, const Segment& a, const Segment& b,
+                                           const Segment& c) {
+  const Segment g = seg_at(x.rel, a, b, c);
+  return load_chunk_ids(p.block_tables + (size_t)g.s * p.max_blocks_per_seq, x.cs, g.lbl, p);
+}
+
+template <class Eng, int D>
+__device__ void segment_epilogue(const DecodeParams& p, const typename Eng::Smem& sm, const Segment& g, int kvh,
+                                 int lane) {
+  const int gq = p.group, Hq = p.num_heads;
+  const size_t head0 = (size_t)kvh * gq;
+  // the piece holding a sequence's first token records where its pieces are
+  // (single pieces too, so the merge kernel never reads a stale record)
+  if (p.mode == kModeBalanced && g.t0 == 0 && kvh == 0 && lane == 0) {
+    p.ws_meta[2 * g.s] = g.first_slot;
+    p.ws_meta[2 * g.s + 1] = g.npieces;
+  }
+  if (g.npieces == 1) {
+    const size_t base = ((size_t)g.s * Hq + head0) * D;
+    for (int idx = lane; idx < gq * D; idx += 64) {
+      const int h = idx / D, dd = idx % D;
+      store_out(p.out, base + idx, Eng::o_val(sm, h, dd, gq) / Eng::l_val(sm, h), p.out_dtype);
+    }
+  } else {
+    const size_t row0 = (size_t)g.slot * Hq + head0;
+    for (int idx = lane; idx < gq * D; idx += 64) {
+      const int h = idx / D, dd = idx % D;
+      p.ws_acc[row0 * D + idx] = Eng::o_val(sm, h, dd, gq);
+    }
+    for (int h = lane; h < gq; h += 64) {
+      p.ws_ml[(row0 + h) * 2] = Eng::m_val(sm, h);
+      p.ws_ml[(row0 + h) * 2 + 1] = Eng::l_val(sm, h);
+    }
+  }
+  __syncthreads();
+}
+
+// Runs all of a worker's segments as one stream of 32-token chunks: the
+// register set of a chunk is refilled with the next chunk of the stream,
+// which may already belong to the next segment, whose q is fetched at the
+// same time; block ids are read two chunks ahead. A segment's epilogue
+// therefore overlaps the next segment's first loads.
+template <class Eng, int D>
+__device__ void run_stream(const DecodeParams& p, typename Eng::Smem& sm, SegmentSource& src, int kvh, int lane) {
+  static_assert(Eng::kSub == 1, "the chunk stream assumes one 32-token chunk per step");
+  Segment A = src.next(p);
+  if (!A.valid) return;
+  Segment B = src.next(p);
+  Segment C = B.valid ? src.next(p) : invalid_segment();
+  Eng eng;
+  typename Eng::Q q, qn;
+  eng.load_q(q, p, A.s, kvh, lane);
+  eng.reset(q);
+  Pos p0{0, A.t0};
+  Pos p1 = advance(p0, A, B, C);
+  Pos p2 = advance(p1, A, B, C);
+  const ChunkIds ids0 = ids_at(p, p0, A, B, C);
+  ChunkIds ids1 = ids_at(p, p1, A, B, C);
+  typename Eng::Frag f;
+  eng.load_k(f, p, kvh, lane, p0.cs, &ids0, A.lbl);
+  eng.load_v(f, p, kvh, lane, p0.cs, &ids0, A.lbl);
+  for (;;) {
+    const ChunkIds ids2 = ids_at(p, p2, A, B, C);
+    const bool leaving = p1.rel != 0;                       // p0 is the current segment's last chunk
+    const bool at_end = !leaving && p1.cs == p0.cs;         // and there is no next segment
+    const Segment n1 = seg_at(p1.rel, A, B, C);
+    if (leaving) eng.load_q(qn, p, n1.s, kvh, lane);
+    eng.step(f, p, sm, kvh, lane, p0.cs, A.t1, p1.cs, &ids1, n1.lbl);
+    if (leaving || at_end) {
+      eng.finish(sm, lane);
+      segment_epilogue<Eng, D>(p, sm, A, kvh, lane);
+      if (at_end) break;
+      A = B;
+      B = C;
+      C = B.valid ? src.next(p) : invalid_segment();
+      p1.rel -= 1;
+      p2.rel -= 1;
+      eng.reset(qn);
+    }
+    p0 = p1;
+    p1 = p2;
+    p2 = advance(p2, A, B, C);
+    ids1 = ids2;
+  }
 }
 
 template <class Eng, int D>
@@ -659,6 +798,9 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
   const int kvh = blockIdx.y;
   const int w = blockIdx.x;
   const int W = gridDim.x;
+  SegmentSource src;
+  src.mode = p.mode;
+  src.w = w;
 
   if (p.mode == kModeFixed) {
     const int s = w / p.max_parts, part = w % p.max_parts;
@@ -666,22 +808,29 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
     // a context longer than max_parts partitions (longer than the host's
     // bound) is cut there rather than left without a merging piece
     const long long cap = (long long)p.max_parts * P;
-    const int L = (int)min((long long)eff_len(p, s), cap);
+    const int L = (int)min((long long)eff_len_uniform(p, s), cap);
     if (L <= 0) {
       if (part == 0) write_zero_rows<Eng, D>(p, s, kvh, lane);
       return;
     }
     const int t0 = part * P;
     if (t0 >= L) return;
-    const int t1 = min(t0 + P, L);
-    const int np = (L + P - 1) / P;
-    process_piece<Eng, D>(p, sm, s, kvh, lane, t0, t1, np, s * p.max_parts + part, s * p.max_parts);
+    Segment g;
+    g.s = s;
+    g.t0 = t0;
+    g.t1 = min(t0 + P, L);
+    g.lbl = (g.t1 - 1) >> p.log2_block;
+    g.npieces = (L + P - 1) / P;
+    g.slot = s * p.max_parts + part;
+    g.first_slot = s * p.max_parts;
+    g.valid = 1;
+    src.fixed = uniform(g);
+    run_stream<Eng, D>(p, sm, src, kvh, lane);
     return;
   }
 
-  // Balanced split: the chunks of all sequences (per KV head) are laid end
-  // to end; worker w takes chunks [w*T/W, (w+1)*T/W). Every worker scans the
-  // lengths itself (S <= kMaxBalancedSeqs), so no planning launch is needed.
+  // Balanced split: every worker scans the lengths itself (S <=
+  // kMaxBalancedSeqs), so no planning launch is needed.
   const int S = p.num_seqs;
   const int per = (S + 63) >> 6;
   const int s_lo = min(lane * per, S), s_hi = min(s_lo + per, S);
@@ -697,7 +846,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
   const long long excl = incl - mine;
 
   for (int s = w; s < S; s += W)
-    if (eff_len(p, s) <= 0) write_zero_rows<Eng, D>(p, s, kvh, lane);
+    if (eff_len_uniform(p, s) <= 0) write_zero_rows<Eng, D>(p, s, kvh, lane);
   if (T == 0) return;
   // with no more workers than chunks every range is non-empty, so the pieces
   // of a sequence are exactly the workers owner_of(first chunk)..owner_of(last)
@@ -722,23 +871,14 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
       c += n;
     }
   }
-  s_first = __shfl(s_first, owner);
-  c_first = __shfl(c_first, owner);
-
-  long long c = c_first;
-  for (int s = s_first; s < S && c < end; ++s) {
-    const int L = eff_len(p, s);
-    const int n = num_chunks(L);
-    if (n == 0) continue;
-    const long long c0 = start > c ? start : c;
-    const long long c1 = end < c + n ? end : c + n;
-    const int t0 = (int)(c0 - c) * kChunk;
-    const int t1 = min((int)(c1 - c) * kChunk, L);
-    const int first = (int)owner_of(c, Wn, T);
-    const int last = (int)owner_of(c + n - 1, Wn, T);
-    process_piece<Eng, D>(p, sm, s, kvh, lane, t0, t1, last - first + 1, w + s, first + s);
-    c += n;
-  }
+  src.s = __builtin_amdgcn_readfirstlane(__shfl(s_first, owner));
+  src.c = __shfl(c_first, owner);
+  src.start = start;
+  src.end = end;
+  src.W = Wn;
+  src.T = T;
+  src.fixed = invalid_segment();
+  run_stream<Eng, D>(p, sm, src, kvh, lane);
 }
 
 // Combine the partial results of every split (sequence, KV head): the
