@@ -1,8 +1,10 @@
 """Throughput of one decode step of the paged-KV hot path on one MI355X.
 
 A step = this step's copy-on-write block copies (none in this workload) +
-pa_write_kv of every sequence's new token + pa_decode over the paged cache,
-on seeded synthetic inputs already resident in HBM. Prints one JSON line.
+pa_write_decode (every sequence's new token stored into its slot, then decode
+attention over the paged cache, in one launch), on seeded synthetic inputs
+already resident in HBM. `--two-calls` times pa_write_kv + pa_decode instead.
+Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload llama3_8b]
 """
@@ -57,11 +59,14 @@ def decode_bytes(w) -> dict:
     return {"kv": kv, "q": q, "out": out, "ids": ids, "lens": lens, "total": kv + q + out + ids + lens}
 
 
-def write_bytes(w) -> int:
+def write_bytes(w, fused: bool) -> int:
+    """New K and V of every sequence read once and stored once (+ the slot
+    mapping when the write is its own call; the fused call finds the slot in
+    the block table entries already counted for the decode)."""
     c = w.cfg
     es = {"f32": 4, "f16": 2, "bf16": 2}[c.etype]
     T = len(w.slot_mapping)
-    return 2 * T * c.num_kv_heads * c.head_dim * es * 2 + 4 * T
+    return 2 * T * c.num_kv_heads * c.head_dim * es * 2 + (0 if fused else 4 * T)
 
 
 def cpu_baseline(w, budget_s: float) -> dict:
@@ -91,32 +96,89 @@ def cpu_baseline(w, budget_s: float) -> dict:
 
 
 def traffic_for(kernel: str, workload: str):
-    """HBM bytes per launch from the committed counter summary, if it was
-    taken on the current kernel sources."""
+    """HBM bytes per step of the timed launches from the committed counter
+    summary, if it was taken on the current kernel sources."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    entry = rec.get(workload, {}).get(kernel)
-    if not entry or entry.get("kernel_hash") != kernel_hash():
+    entry = rec.get(workload, {})
+    if entry.get("kernel_hash") != kernel_hash():
         return None
-    return entry.get("traffic_bytes")
+    return entry.get(kernel)
+
+
+FUSED_KERNELS = ("decode_kernel", "merge_kernel")
+TWO_CALL_KERNELS = ("write_kv_kernel", "decode_kernel", "merge_kernel")
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, workload: str, calibration_mib: int) -> dict:
+    """Per-launch HBM bytes of the step's kernels from two rocprofv3 --pmc
+    runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what the
+    counter read for the run's plain device copy of calibration_mib MiB, and
+    recorded in the traffic file with the hash of the kernel sources."""
+    import csv
+    from collections import defaultdict
+
+    def per_kernel(path):
+        vals, calib = defaultdict(list), 0.0
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                name, v = r["Kernel_Name"], float(r["Counter_Value"])
+                if name.startswith("__amd_rocclr_copyBuffer"):
+                    calib = max(calib, v)
+                    continue
+                for k in TWO_CALL_KERNELS:
+                    if f"::{k}<" in name:
+                        vals[k].append(v)
+        return {k: float(np.mean(v)) for k, v in vals.items()}, calib
+
+    fetch, fcal = per_kernel(fetch_csv)
+    write, wcal = per_kernel(write_csv)
+    want = calibration_mib * 1024.0
+    fs, ws = want / fcal, want / wcal
+    kernels = {k: {"fetch_kib_per_launch": round(fetch[k], 1), "write_kib_per_launch": round(write[k], 1),
+                   "traffic_bytes": int(round((fetch[k] * fs + write[k] * ws) * 1024))}
+               for k in fetch if k in write}
+    entry = {"kernel_hash": kernel_hash(), "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
+             "calibration": f"one {calibration_mib} MiB device-to-device torch copy (__amd_rocclr_copyBuffer) in "
+                            f"the same run: FETCH_SIZE {fcal:.1f} KiB, WRITE_SIZE {wcal:.1f} KiB",
+             "kernels": kernels}
+    for key, ks in (("+".join(FUSED_KERNELS), FUSED_KERNELS), ("+".join(TWO_CALL_KERNELS), TWO_CALL_KERNELS)):
+        if all(k in kernels for k in ks):
+            entry[key] = sum(kernels[k]["traffic_bytes"] for k in ks)
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    rec[workload] = entry
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    return entry
 
 
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama3_8b", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--algo", default="auto", choices=["auto", "vector", "mfma"])
     ap.add_argument("--partition", type=int, default=None, help="partition size (-1 balanced, 0 none)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--two-calls", action="store_true", help="time pa_write_kv + pa_decode instead of the fused call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run one plain device copy of this size first (traffic counter calibration)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the traffic file from two rocprofv3 counter_collection.csv files and exit")
     args = ap.parse_args()
+    if args.summarize_counters:
+        entry = summarize_counters(*args.summarize_counters, args.workload, args.calibration_copy_mib or 1024)
+        print(json.dumps(entry, indent=1))
+        return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the decode path here has no "
               "multi-GPU mode: per-GPU work is the single-GPU kernel on that GPU's share", file=sys.stderr)
@@ -152,36 +214,43 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    def step(ev=None):
-        pb.pa_copy_blocks(kc, vc, copies)
-        pb.pa_write_kv(k_new, v_new, kc, vc, slots)
-        if ev is not None:
-            ev[0].record()
-        pb.pa_decode(out, q, kc, vc, bt, cl, cfg.scale, max_len, partition_size=part, algo=args.algo)
-        if ev is not None:
-            ev[1].record()
+    fused = not args.two_calls
+    if fused and args.algo != "auto":
+        raise SystemExit("--algo needs --two-calls (the fused call picks the kernel family itself)")
+
+    def step():
+        pb.pa_copy_blocks(kc, vc, copies)   # no pairs: returns without a launch
+        if fused:
+            pb.pa_write_decode(out, q, k_new, v_new, kc, vc, bt, cl, cfg.scale, max_len, partition_size=part)
+        else:
+            pb.pa_write_kv(k_new, v_new, kc, vc, slots)
+            pb.pa_decode(out, q, kc, vc, bt, cl, cfg.scale, max_len, partition_size=part, algo=args.algo)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    # one event pair on the launch stream brackets the timed steps (events
+    # between the launches would add their own gaps to what they measure)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    decode_ms = [a.elapsed_time(b) for a, b in events]
+    call_ms = ev0.elapsed_time(ev1) / args.steps
 
     db = decode_bytes(w)
-    wb = write_bytes(w)
+    wb = write_bytes(w, fused)
     step_bytes = db["total"] + wb
     ms_per_step = elapsed * 1e3 / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    decode_avg_ms = float(np.mean(decode_ms))
-    achieved = db["total"] / (decode_avg_ms * 1e-3) / 1e9
-    kernel = "decode_kernel"
+    # per step on the GPU: the fused call's launches (decode_kernel, then
+    # merge_kernel: merges split sequences and stores the new tokens)
+    launch_bytes = step_bytes if fused else db["total"] + wb
+    achieved = launch_bytes / (call_ms * 1e-3) / 1e9
+    kernel = "decode_kernel+merge_kernel" if fused else "write_kv_kernel+decode_kernel+merge_kernel"
     traffic = traffic_for(kernel, args.workload)
     result = {
         "metric": "paged decode attention: achieved HBM GB/s (% of peak) + sequences/s at 1 GPU",
@@ -203,13 +272,16 @@ def main() -> int:
             "max_context_len": max_len,
             "partition_size": part,
             "algo": args.algo,
-            "step": "copy blocks (0 pairs) + write 1 token/seq + decode",
+            "step": ("copy blocks (0 pairs) + fused write 1 token/seq and decode" if fused
+                     else "copy blocks (0 pairs) + write 1 token/seq + decode"),
         },
         "sequences_per_s": round(cfg.num_seqs / (ms_per_step * 1e-3), 1),
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "step_bytes": step_bytes,
-        "decode": {"bytes": db, "avg_ms": round(decode_avg_ms, 5), "min_ms": round(float(np.min(decode_ms)), 5),
-                   "GBps": round(achieved, 1), "seq_per_s": round(cfg.num_seqs / (decode_avg_ms * 1e-3), 1)},
+        "decode": {"call": "pa_write_decode" if fused else "pa_write_kv + pa_decode", "bytes": db,
+                   "write_bytes": wb, "launch_bytes": launch_bytes, "avg_ms": round(call_ms, 5),
+                   "GBps": round(achieved, 1), "seq_per_s": round(cfg.num_seqs / (call_ms * 1e-3), 1),
+                   "timed": "HIP events on the launch stream around the timed steps, divided by the steps"},
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
         "input_generation_s": round(gen_s, 2),

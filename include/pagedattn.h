@@ -137,6 +137,32 @@ pa_status pa_decode_ex(void* out, const void* q, const void* k_cache, const void
                        void* workspace, size_t workspace_bytes, pa_dtype dtype,
                        pa_dtype out_dtype, pa_algo algo, void* stream);
 
+/*
+ * pa_write_decode -- the decode step's write and attention in one call:
+ * the same result as pa_write_kv of every sequence's new token (k_new[s],
+ * v_new[s], [num_seqs][num_kv_heads][head_dim] of dtype) into the slot of
+ * its position L-1 = context_lens[s]-1, found through block_tables[s],
+ * followed by pa_decode with the same arguments: output and cache contents
+ * are bit-identical to that pair of calls ([notes-zh] §5.3: the new token's
+ * KV goes into the last logical block, then attention reads the blocks).
+ * The attention kernel takes position L-1 from k_new/v_new; the launch
+ * after it (which also merges split sequences) stores them into the cache.
+ * The block of position L-1 must not be shared with another sequence of the
+ * call (copy-on-write has already made it private, [notes-zh] §6.1). No
+ * write is made for a sequence with L <= 0, with L beyond
+ * max_blocks_per_seq*block_size (or, with fixed partitions, beyond
+ * max_context_len), or whose table entry for position L-1 is not a block of
+ * the pool (its output is then unspecified, as with any invalid entry).
+ * k_new/v_new: device, 16-byte aligned, both given. Workspace as for
+ * pa_decode.
+ */
+pa_status pa_write_decode(void* out, const void* q, const void* k_new, const void* v_new, void* k_cache,
+                          void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                          int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                          int32_t max_context_len, float scale, int32_t partition_size, void* workspace,
+                          size_t workspace_bytes, pa_dtype dtype, pa_dtype out_dtype, void* stream);
+
 /* Workspace bytes pa_decode needs for these sizes (0 when it needs none).
  * Returns 0 as well for arguments pa_decode would reject. Pure host function. */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,

@@ -31,6 +31,8 @@ SIGNATURES = {
                          _p, _sz, _i32, _i32, _p]),
     "pa_decode_ex": (_i32, [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                             _p, _sz, _i32, _i32, _i32, _p]),
+    "pa_write_decode": (_i32, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                               _i32, _p, _sz, _i32, _i32, _p]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_copy_blocks": (_i32, [_p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p]),
     "pa_status_string": (ctypes.c_char_p, [_i32]),
@@ -184,3 +186,31 @@ def to_host(t: torch.Tensor, etype: str):
 def int32_to_device(arr, device) -> torch.Tensor:
     import numpy as np
     return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.int32)).to(device)
+
+
+def pa_write_decode(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+                    partition_size=PA_PARTITION_AUTO, workspace=None, stream=None) -> None:
+    """Store each sequence's new token (k_new/v_new [S][Hkv][d]) at position context_lens[s]-1 and decode,
+    in one launch."""
+    lib = load_library()
+    S, Hq, d = q.shape
+    NB, Hkv, B, _ = k_cache.shape
+    if out.shape != q.shape or v_cache.shape != (NB, Hkv, d, B) or k_cache.shape[3] != d:
+        raise ValueError("inconsistent shapes")
+    if k_new.shape != (S, Hkv, d) or v_new.shape != (S, Hkv, d):
+        raise ValueError("k_new/v_new must be [num_seqs][num_kv_heads][head_dim]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables must be [num_seqs][max_blocks], context_lens [num_seqs]")
+    dt = k_cache.dtype
+    need = int(lib.pa_decode_workspace_bytes(S, Hq, Hkv, d, int(max_context_len), int(partition_size)))
+    if workspace is None and need:
+        workspace = workspace_for(q.device, need)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    status = lib.pa_write_decode(
+        _dev(out, "out"), _dev(q, "q", dt), _dev(k_new, "k_new", dt), _dev(v_new, "v_new", dt),
+        _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
+        _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
+        S, Hq, Hkv, d, B, NB, block_tables.shape[1], int(max_context_len), float(scale), int(partition_size),
+        ws_ptr, ws_bytes, DTYPE_CODE[dt], DTYPE_CODE[out.dtype], _stream(stream))
+    _check("pa_write_decode", status)

@@ -14,7 +14,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 constexpr size_t kAlign = 256;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -176,12 +176,14 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapp
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
-pa_status pa_decode_ex(void* out, const void* q, const void* k_cache, const void* v_cache,
-                       const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
-                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                       int32_t max_blocks_per_seq, int32_t max_context_len, float scale, int32_t partition_size,
-                       void* workspace, size_t workspace_bytes, pa_dtype dtype, pa_dtype out_dtype, pa_algo algo,
-                       void* stream) {
+}  // extern "C"
+
+static pa_status decode_impl(void* out, const void* q, const void* k_new, const void* v_new, const void* k_cache,
+                             const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                             int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                             float scale, int32_t partition_size, void* workspace, size_t workspace_bytes, pa_dtype dtype,
+                             pa_dtype out_dtype, pa_algo algo, void* stream) {
   if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return PA_ERR_INVALID_ARG;
   if (algo != PA_ALGO_AUTO && algo != PA_ALGO_VECTOR && algo != PA_ALGO_MFMA) return PA_ERR_INVALID_ARG;
   if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads) return PA_ERR_INVALID_ARG;
@@ -198,6 +200,8 @@ pa_status pa_decode_ex(void* out, const void* q, const void* k_cache, const void
   if (group > pa::kMaxGroup) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
+  if ((k_new == nullptr) != (v_new == nullptr)) return PA_ERR_INVALID_ARG;
+  if (k_new && (!aligned(k_new, 16) || !aligned(v_new, 16))) return PA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 4) ||
       !aligned(block_tables, 4) || !aligned(context_lens, 4))
     return PA_ERR_INVALID_ARG;
@@ -223,6 +227,8 @@ pa_status pa_decode_ex(void* out, const void* q, const void* k_cache, const void
   pa::DecodeParams p{};
   p.out = out;
   p.q = q;
+  p.k_new = k_new;
+  p.v_new = v_new;
   p.k_cache = k_cache;
   p.v_cache = v_cache;
   p.block_tables = block_tables;
@@ -259,6 +265,31 @@ pa_status pa_decode_ex(void* out, const void* q, const void* k_cache, const void
   const hipError_t e = pa::launch_decode(p, elem, head_dim, kernel_algo, G, (unsigned)workers, pl.slots > 0,
                                          static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+extern "C" {
+
+pa_status pa_decode_ex(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                       int32_t max_blocks_per_seq, int32_t max_context_len, float scale, int32_t partition_size,
+                       void* workspace, size_t workspace_bytes, pa_dtype dtype, pa_dtype out_dtype, pa_algo algo,
+                       void* stream) {
+  return decode_impl(out, q, nullptr, nullptr, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len, scale,
+                     partition_size, workspace, workspace_bytes, dtype, out_dtype, algo, stream);
+}
+
+pa_status pa_write_decode(void* out, const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                          const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                          int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                          int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                          int32_t partition_size, void* workspace, size_t workspace_bytes, pa_dtype dtype,
+                          pa_dtype out_dtype, void* stream) {
+  if (num_seqs > 0 && (!k_new || !v_new)) return PA_ERR_INVALID_ARG;
+  return decode_impl(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len, scale,
+                     partition_size, workspace, workspace_bytes, dtype, out_dtype, PA_ALGO_AUTO, stream);
 }
 
 pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,

@@ -30,6 +30,8 @@ struct DecodeParams {
   const void* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
+  const void* k_new;  // [num_seqs][num_kv_heads][head_dim] new token per sequence (fused write), or null
+  const void* v_new;
   int32_t* ws_meta;   // [num_seqs][2] balanced split: (first slot, pieces) of each sequence
   float* ws_ml;       // [slots][num_heads][2]  (running max in log2 units, sum)
   float* ws_acc;      // [slots][num_heads][head_dim] (unnormalised output)
@@ -46,12 +48,14 @@ struct DecodeParams {
   int32_t part_chunks;  // fixed mode: chunks per partition
   int32_t max_parts;    // fixed mode: partitions per sequence (grid.x = num_seqs*max_parts)
   int32_t out_dtype;    // Elem of `out`
+  int32_t merge;        // set by launch_decode: some sequence is split and needs merging
 };
 
 // Launch the decode kernel for (elem, head_dim, algo, group bucket G),
 // grid = (workers per KV head, num_kv_heads), 64 threads per workgroup, then,
-// when `merge` is set, the kernel that combines the partial results of split
-// sequences (grid = (num_seqs, num_kv_heads)).
+// when `merge` is set or the call brings new tokens (k_new), the closing
+// kernel (grid = (num_seqs, num_kv_heads)) that combines the partial results
+// of split sequences and stores the new tokens into the cache.
 hipError_t launch_decode(const DecodeParams& p, int elem, int head_dim, int algo, int G,
                          unsigned workers, bool merge, hipStream_t stream);
 // Resident waves per CU of that kernel (0 if unknown).

@@ -154,13 +154,18 @@ __device__ __forceinline__ ChunkIds load_chunk_ids(const int32_t* tbl, int cs, i
   return c;
 }
 
-__device__ __forceinline__ int pick_block(ChunkIds c, int tok, int log2_block, int lbl, int num_blocks) {
+// The table entry of token tok's block, as stored.
+__device__ __forceinline__ int pick_entry(ChunkIds c, int tok, int log2_block, int lbl) {
   const int k = min(tok >> log2_block, lbl) - c.lb0;
   int id = c.id0;
   id = k >= 1 ? c.id1 : id;
   id = k >= 2 ? c.id2 : id;
   id = k >= 3 ? c.id3 : id;
-  return min(max(id, 0), num_blocks - 1);
+  return id;
+}
+
+__device__ __forceinline__ int pick_block(ChunkIds c, int tok, int log2_block, int lbl, int num_blocks) {
+  return min(max(pick_entry(c, tok, log2_block, lbl), 0), num_blocks - 1);
 }
 
 __device__ __forceinline__ int eff_len(const DecodeParams& p, int s) {
@@ -170,10 +175,70 @@ __device__ __forceinline__ int eff_len(const DecodeParams& p, int s) {
 
 // The same for a wave-uniform s, read with a scalar load so that it never
 // waits behind the K/V vector loads in flight.
-__device__ __forceinline__ int eff_len_uniform(const DecodeParams& p, int s) {
-  const int cap = p.max_blocks_per_seq << p.log2_block;
+__device__ __forceinline__ int len_uniform(const DecodeParams& p, int s) {
   const const_i32* lens = (const const_i32*)p.context_lens;
-  return min(lens[__builtin_amdgcn_readfirstlane(s)], cap);
+  return lens[__builtin_amdgcn_readfirstlane(s)];
+}
+
+__device__ __forceinline__ int eff_len_uniform(const DecodeParams& p, int s) {
+  return min(len_uniform(p, s), p.max_blocks_per_seq << p.log2_block);
+}
+
+// Position of the token the fused write stores for a piece ending at t1 of
+// a sequence of stored length L_raw, cut to L: its last, when the piece holds
+// it and the length was not cut; else -1.
+__device__ __forceinline__ int new_token_pos(const DecodeParams& p, int t1, int L, int L_raw) {
+  return (p.k_new != nullptr && L == L_raw && t1 == L && L > 0) ? L - 1 : -1;
+}
+
+__device__ __forceinline__ u32x4 put_elem16(u32x4 w, int e, uint32_t v) {
+  const int wi = e >> 1, sh = (e & 1) * 16;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = i == wi ? ((w[i] & ~(0xffffu << sh)) | ((v & 0xffffu) << sh)) : w[i];
+  return w;
+}
+
+__device__ __forceinline__ u32x4 put_elem32(u32x4 w, int e, uint32_t v) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = i == e ? v : w[i];
+  return w;
+}
+
+// element e (< 16 / sizeof(U)) of a 16-byte register group set to v; e < 0: unchanged
+template <typename U>
+__device__ __forceinline__ u32x4 put_elem(u32x4 w, int e, uint32_t v) {
+  return sizeof(U) == 4 ? put_elem32(w, e, v) : put_elem16(w, e, v);
+}
+
+// One sequence's share of a worker's work: tokens [t0, t1) of sequence s,
+// whose last logical block is lbl; tnew is the position of the token the
+// fused write stores (the sequence's last, when this piece holds it and the
+// call brings one), else -1.
+struct Segment {
+  int s, t0, t1, lbl, npieces, slot, first_slot;
+  int tnew;
+  int valid;
+};
+
+__device__ __forceinline__ Segment invalid_segment() {
+  Segment g;
+  g.s = g.t0 = g.t1 = g.lbl = g.npieces = g.slot = g.first_slot = 0;
+  g.tnew = -1;
+  g.valid = 0;
+  return g;
+}
+
+__device__ __forceinline__ Segment uniform(Segment g) {
+  g.s = __builtin_amdgcn_readfirstlane(g.s);
+  g.t0 = __builtin_amdgcn_readfirstlane(g.t0);
+  g.t1 = __builtin_amdgcn_readfirstlane(g.t1);
+  g.lbl = __builtin_amdgcn_readfirstlane(g.lbl);
+  g.npieces = __builtin_amdgcn_readfirstlane(g.npieces);
+  g.slot = __builtin_amdgcn_readfirstlane(g.slot);
+  g.first_slot = __builtin_amdgcn_readfirstlane(g.first_slot);
+  g.tnew = __builtin_amdgcn_readfirstlane(g.tnew);
+  g.valid = __builtin_amdgcn_readfirstlane(g.valid);
+  return g;
 }
 
 __device__ __forceinline__ int num_chunks(int L) { return L > 0 ? (L + kChunk - 1) / kChunk : 0; }
@@ -215,10 +280,13 @@ struct MfmaEngine {
   f32x4 o[NT];
   float m_run;
   float l_run;
+  uint32_t vn[NT];  // the segment's new token's V at this lane's output columns 16j + col
 
-  // q of one sequence as the QK B operand (columns = head slots)
+  // q of one sequence as the QK B operand (columns = head slots), and the
+  // new token's V values this lane's B operands carry (fused write)
   struct Q {
     u32x4 w[MQ];
+    uint32_t vn[NT];
   };
 
   __device__ void load_q(Q& q, const DecodeParams& p, int s, int kvh, int lane) const {
@@ -231,13 +299,21 @@ struct MfmaEngine {
       if (hs >= 0) w = load16(qb + (size_t)hs * D + 32 * m + 8 * grp);
       q.w[m] = w;
     }
+    // read unconditionally (from q when the call brings no new token: an
+    // in-bounds row, never used) so every segment issues the same loads
+    const raw* vb = static_cast<const raw*>(p.v_new ? p.v_new : p.q) + ((size_t)s * p.num_kv_heads + kvh) * D + col;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) q.vn[j] = vb[16 * j];
   }
 
   __device__ void reset(const Q& q) {
 #pragma unroll
     for (int m = 0; m < MQ; ++m) qop[m] = __builtin_bit_cast(op8, q.w[m]);
 #pragma unroll
-    for (int j = 0; j < NT; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NT; ++j) {
+      o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      vn[j] = q.vn[j];
+    }
     m_run = kNegInf;
     l_run = 0.f;
   }
@@ -249,26 +325,31 @@ struct MfmaEngine {
     u32x4 vr[SUB][NT];
   };
 
+  // The row of the segment's new token (g.tnew) comes from the caller's
+  // k_new, not from the cache slot the same launch writes.
   __device__ void load_k(Frag& f, const DecodeParams& p, int kvh, int lane, int cs, const ChunkIds* ids,
-                         int lbl) const {
+                         const Segment& g) const {
     const int col = lane & 15, grp = lane >> 4;
     const int B = p.block_size, lg = p.log2_block, Hkv = p.num_kv_heads;
     const raw* __restrict__ kc = static_cast<const raw*>(p.k_cache);
+    const raw* kn = static_cast<const raw*>(p.k_new) + ((size_t)g.s * Hkv + kvh) * D + 8 * grp;
     // K rows: A-operand row `col` of row group c holds token 8*(col/4)+4c+col%4
 #pragma unroll
     for (int u = 0; u < SUB; ++u)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const int tok = cs + kChunk * u + 8 * (col >> 2) + 4 * c + (col & 3);
-        const int phys = pick_block(ids[u], tok, lg, lbl, p.num_blocks);
+        const int phys = pick_block(ids[u], tok, lg, g.lbl, p.num_blocks);
         const raw* row = kc + (((size_t)phys * Hkv + kvh) * B + (tok & (B - 1))) * D + 8 * grp;
+        row = tok == g.tnew ? kn : row;
 #pragma unroll
         for (int m = 0; m < MQ; ++m) f.ka[u][c][m] = load16_stream(row + 32 * m);
       }
   }
 
   __device__ void load_v(Frag& f, const DecodeParams& p, int kvh, int lane, int cs, const ChunkIds* ids,
-                         int lbl) const {
+                         const Segment& g) const {
+    const int lbl = g.lbl;
     const int col = lane & 15, grp = lane >> 4;
     const int B = p.block_size, lg = p.log2_block, Hkv = p.num_kv_heads;
     const raw* __restrict__ vc = static_cast<const raw*>(p.v_cache);
@@ -286,9 +367,11 @@ struct MfmaEngine {
   // Compute the step at `cs` from `f`; as soon as a register set is
   // consumed it is refilled with the next step (K after QK, V after PV), so
   // one step's loads are always in flight behind the math.
-  __device__ void step(Frag& f, const DecodeParams& p, Smem&, int kvh, int lane, int cs, int t1, int cs_next,
-                       const ChunkIds* ids_next, int lbl_next) {
+  __device__ void step(Frag& f, const DecodeParams& p, Smem&, int kvh, int lane, int cs, const Segment& cur,
+                       int cs_next, const ChunkIds* ids_next, const Segment& nxt) {
     const int col = lane & 15, grp = lane >> 4, g = p.group;
+    const int t1 = cur.t1;
+    const bool has_new = cur.tnew >= cs && cur.tnew < cs + SUB * kChunk;
     // scores: in sub-chunk u the lane holds tokens cs+32u+8*grp+0..7 of head slot `col`
     f32x4 sc[SUB][2];
 #pragma unroll
@@ -304,7 +387,7 @@ struct MfmaEngine {
     // unconditional refill (at the end of the stream the last step re-reads
     // itself from L2) keeps the count of loads in flight the same on every
     // path, so the PV wait below never has to drain the next step's K loads
-    load_k(f, p, kvh, lane, cs_next, ids_next, lbl_next);
+    load_k(f, p, kvh, lane, cs_next, ids_next, nxt);
     float sv[SUB][8];
 #pragma unroll
     for (int u = 0; u < SUB; ++u)
@@ -368,10 +451,17 @@ struct MfmaEngine {
 #pragma unroll
         for (int j = 0; j < NT; ++j) f.vr[u][j] = Tr::keep_first(f.vr[u][j], nvalid);
       }
+      if (has_new) {
+        // the new token's V replaces what its slot held before this launch
+        const int e = cur.tnew - (cs + kChunk * u + 8 * grp);
+        const int en = e >= 0 && e < 8 ? e : -1;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) f.vr[u][j] = put_elem<raw>(f.vr[u][j], en, vn[j]);
+      }
 #pragma unroll
       for (int j = 0; j < NT; ++j) o[j] = mfma_16x16x32(pa, __builtin_bit_cast(op8, f.vr[u][j]), o[j]);
     }
-    load_v(f, p, kvh, lane, cs_next, ids_next, lbl_next);
+    load_v(f, p, kvh, lane, cs_next, ids_next, nxt);
   }
 
   __device__ void finish(Smem& sm, int lane) {
@@ -425,9 +515,11 @@ struct VecEngine {
   float acc[G][VSTEPS];
   float m_run[G];
   float l_run[G];
+  uint32_t vn[VSTEPS];  // the segment's new token's V at this lane's rows st*DPS + lane/LPD
 
   struct Q {
     u32x4 w[G];
+    uint32_t vn[VSTEPS];
   };
 
   __device__ void load_q(Q& q, const DecodeParams& p, int s, int kvh, int lane) const {
@@ -439,6 +531,12 @@ struct VecEngine {
       if (h < g) w = load16(qb + (size_t)h * D + piece * VEC);
       q.w[h] = w;
     }
+    // read unconditionally (from q when the call brings no new token: an
+    // in-bounds row, never used) so every segment issues the same loads
+    const raw* vb = static_cast<const raw*>(p.v_new ? p.v_new : p.q) + ((size_t)s * p.num_kv_heads + kvh) * D +
+                    lane / LPD;
+#pragma unroll
+    for (int st = 0; st < VSTEPS; ++st) q.vn[st] = vb[st * DPS];
   }
 
   __device__ void reset(const Q& q) {
@@ -450,6 +548,8 @@ struct VecEngine {
       m_run[h] = kNegInf;
       l_run[h] = 0.f;
     }
+#pragma unroll
+    for (int st = 0; st < VSTEPS; ++st) vn[st] = q.vn[st];
   }
 
   struct Frag {
@@ -457,22 +557,27 @@ struct VecEngine {
     u32x4 vr[VSTEPS];
   };
 
+  // The row of the segment's new token (g.tnew) comes from the caller's
+  // k_new, not from the cache slot the same launch writes.
   __device__ void load_k(Frag& f, const DecodeParams& p, int kvh, int lane, int cs, const ChunkIds* idp,
-                         int lbl) const {
+                         const Segment& g) const {
     const ChunkIds ids = idp[0];
     const int B = p.block_size, lg = p.log2_block, Hkv = p.num_kv_heads;
     const raw* __restrict__ kc = static_cast<const raw*>(p.k_cache);
     const int piece = lane % LPR;
+    const raw* kn = static_cast<const raw*>(p.k_new) + ((size_t)g.s * Hkv + kvh) * D + piece * VEC;
 #pragma unroll
     for (int st = 0; st < KSTEPS; ++st) {
       const int tok = cs + st * RPS + lane / LPR;
-      const int phys = pick_block(ids, tok, lg, lbl, p.num_blocks);
-      f.kr[st] = load16_stream(kc + (((size_t)phys * Hkv + kvh) * B + (tok & (B - 1))) * D + piece * VEC);
+      const int phys = pick_block(ids, tok, lg, g.lbl, p.num_blocks);
+      const raw* row = kc + (((size_t)phys * Hkv + kvh) * B + (tok & (B - 1))) * D + piece * VEC;
+      f.kr[st] = load16_stream(tok == g.tnew ? kn : row);
     }
   }
 
   __device__ void load_v(Frag& f, const DecodeParams& p, int kvh, int lane, int cs, const ChunkIds* idp,
-                         int lbl) const {
+                         const Segment& g) const {
+    const int lbl = g.lbl;
     const ChunkIds ids = idp[0];
     const int B = p.block_size, lg = p.log2_block, Hkv = p.num_kv_heads;
     const raw* __restrict__ vc = static_cast<const raw*>(p.v_cache);
@@ -484,8 +589,10 @@ struct VecEngine {
     for (int st = 0; st < VSTEPS; ++st) f.vr[st] = load16_stream(vb + (size_t)st * DPS * B);
   }
 
-  __device__ void step(Frag& f, const DecodeParams& p, Smem& sm, int kvh, int lane, int cs, int t1, int cs_next,
-                       const ChunkIds* ids_next, int lbl_next) {
+  __device__ void step(Frag& f, const DecodeParams& p, Smem& sm, int kvh, int lane, int cs, const Segment& cur,
+                       int cs_next, const ChunkIds* ids_next, const Segment& nxt) {
+    const int t1 = cur.t1;
+    const bool has_new = cur.tnew >= cs && cur.tnew < cs + kChunk;
     const int piece = lane % LPR;
     const int tg = lane % LPD;
     const int tv = cs + tg * VEC;
@@ -505,7 +612,7 @@ struct VecEngine {
         if (piece == 0) sm.sc[h][st * RPS + lane / LPR] = d;
       }
     }
-    load_k(f, p, kvh, lane, cs_next, ids_next, lbl_next);
+    load_k(f, p, kvh, lane, cs_next, ids_next, nxt);
     __syncthreads();
 
     // softmax over the chunk's 32 tokens
@@ -528,6 +635,7 @@ struct VecEngine {
     __syncthreads();
 
     // PV
+    const int enew = has_new && cur.tnew >= tv && cur.tnew < tv + VEC ? cur.tnew - tv : -1;
     float pw[G][VEC];
 #pragma unroll
     for (int h = 0; h < G; ++h)
@@ -537,6 +645,7 @@ struct VecEngine {
     for (int st = 0; st < VSTEPS; ++st) {
       u32x4 w = f.vr[st];
       if (partial) w = Tr::keep_first(w, t1 - tv);
+      if (has_new) w = put_elem<raw>(w, enew, vn[st]);  // the new token's V, not its slot's old value
       float vf[VEC];
       Tr::widen(w, vf);
 #pragma unroll
@@ -547,7 +656,7 @@ struct VecEngine {
         acc[h][st] = a;
       }
     }
-    load_v(f, p, kvh, lane, cs_next, ids_next, lbl_next);
+    load_v(f, p, kvh, lane, cs_next, ids_next, nxt);
     __syncthreads();  // sc/pl are rewritten by the next chunk
   }
 
@@ -608,31 +717,6 @@ __device__ void merge_pieces(const DecodeParams& p, int s, int kvh, int lane, in
   }
 }
 
-// One worker's share of one sequence (all values wave-uniform).
-struct Segment {
-  int s, t0, t1, lbl, npieces, slot, first_slot;
-  int valid;
-};
-
-__device__ __forceinline__ Segment invalid_segment() {
-  Segment g;
-  g.s = g.t0 = g.t1 = g.lbl = g.npieces = g.slot = g.first_slot = 0;
-  g.valid = 0;
-  return g;
-}
-
-__device__ __forceinline__ Segment uniform(Segment g) {
-  g.s = __builtin_amdgcn_readfirstlane(g.s);
-  g.t0 = __builtin_amdgcn_readfirstlane(g.t0);
-  g.t1 = __builtin_amdgcn_readfirstlane(g.t1);
-  g.lbl = __builtin_amdgcn_readfirstlane(g.lbl);
-  g.npieces = __builtin_amdgcn_readfirstlane(g.npieces);
-  g.slot = __builtin_amdgcn_readfirstlane(g.slot);
-  g.first_slot = __builtin_amdgcn_readfirstlane(g.first_slot);
-  g.valid = __builtin_amdgcn_readfirstlane(g.valid);
-  return g;
-}
-
 __device__ __forceinline__ long long owner_of(long long c, long long W, long long T) {
   return ((c + 1) * W - 1) / T;
 }
@@ -655,7 +739,8 @@ struct SegmentSource {
       return g;
     }
     while (s < p.num_seqs && c < end) {
-      const int L = eff_len_uniform(p, s);
+      const int L_raw = len_uniform(p, s);
+      const int L = min(L_raw, p.max_blocks_per_seq << p.log2_block);
       const int n = num_chunks(L);
       if (n == 0) {
         ++s;
@@ -668,6 +753,7 @@ struct SegmentSource {
       g.t0 = (int)(c0 - c) * kChunk;
       g.t1 = min((int)(c1 - c) * kChunk, L);
       g.lbl = (g.t1 - 1) >> p.log2_block;
+      g.tnew = new_token_pos(p, g.t1, L, L_raw);
       const int first = (int)owner_of(c, W, T);
       const int last = (int)owner_of(c + n - 1, W, T);
       g.npieces = last - first + 1;
@@ -764,15 +850,15 @@ __device__ void run_stream(const DecodeParams& p, typename Eng::Smem& sm, Segmen
   const ChunkIds ids0 = ids_at(p, p0, A, B, C);
   ChunkIds ids1 = ids_at(p, p1, A, B, C);
   typename Eng::Frag f;
-  eng.load_k(f, p, kvh, lane, p0.cs, &ids0, A.lbl);
-  eng.load_v(f, p, kvh, lane, p0.cs, &ids0, A.lbl);
+  eng.load_k(f, p, kvh, lane, p0.cs, &ids0, A);
+  eng.load_v(f, p, kvh, lane, p0.cs, &ids0, A);
   for (;;) {
     const ChunkIds ids2 = ids_at(p, p2, A, B, C);
     const bool leaving = p1.rel != 0;                       // p0 is the current segment's last chunk
     const bool at_end = !leaving && p1.cs == p0.cs;         // and there is no next segment
     const Segment n1 = seg_at(p1.rel, A, B, C);
     if (leaving) eng.load_q(qn, p, n1.s, kvh, lane);
-    eng.step(f, p, sm, kvh, lane, p0.cs, A.t1, p1.cs, &ids1, n1.lbl);
+    eng.step(f, p, sm, kvh, lane, p0.cs, A, p1.cs, &ids1, n1);
     if (leaving || at_end) {
       eng.finish(sm, lane);
       segment_epilogue<Eng, D>(p, sm, A, kvh, lane);
@@ -808,7 +894,8 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
     // a context longer than max_parts partitions (longer than the host's
     // bound) is cut there rather than left without a merging piece
     const long long cap = (long long)p.max_parts * P;
-    const int L = (int)min((long long)eff_len_uniform(p, s), cap);
+    const int L_raw = len_uniform(p, s);
+    const int L = (int)min((long long)min(L_raw, p.max_blocks_per_seq << p.log2_block), cap);
     if (L <= 0) {
       if (part == 0) write_zero_rows<Eng, D>(p, s, kvh, lane);
       return;
@@ -823,6 +910,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
     g.npieces = (L + P - 1) / P;
     g.slot = s * p.max_parts + part;
     g.first_slot = s * p.max_parts;
+    g.tnew = new_token_pos(p, g.t1, L, L_raw);
     g.valid = 1;
     src.fixed = uniform(g);
     run_stream<Eng, D>(p, sm, src, kvh, lane);
@@ -889,10 +977,10 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
 // loaded independently; longer piece lists take a plain per-output loop.
 constexpr int kMergeTile = 256;
 
+// Combines one (sequence, KV head)'s pieces when it was split.
 template <int D>
-__global__ __launch_bounds__(64) void merge_kernel(DecodeParams p) {
-  __shared__ float wgt[kMaxGroup][kMergeTile];
-  const int s = blockIdx.x, kvh = blockIdx.y, lane = threadIdx.x;
+__device__ void merge_sequence(const DecodeParams& p, int s, int kvh, int lane, float (*wgt)[kMergeTile],
+                               float (*ls)[kMergeTile]) {
   int L = eff_len(p, s);
   int first_slot, npieces;
   if (p.mode == kModeFixed) {
@@ -914,7 +1002,6 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeParams p) {
   const int g = p.group, Hq = p.num_heads;
   const size_t head0 = (size_t)kvh * g;
   // (m, l) of every (head, piece): m into wgt, l kept in the same slot's pair
-  __shared__ float ls[kMaxGroup][kMergeTile];
   for (int i = lane; i < g * npieces; i += 64) {
     const int h = i / npieces, k = i % npieces;
     const size_t r = ((size_t)(first_slot + k) * Hq + head0 + h) * 2;
@@ -951,6 +1038,56 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeParams p) {
     const size_t o = ((size_t)s * Hq + head0 + h) * D + lane;
 #pragma unroll
     for (int i = 0; i < PER; ++i) store_out(p.out, o + 64 * i, acc[i], p.out_dtype);
+  }
+}
+
+// Position-L-1 slot of sequence s for the fused write, or -1 when no write is
+// made: the conditions under which the attention kernel took that position
+// from k_new/v_new (new_token_pos), and a table entry inside the pool.
+__device__ __forceinline__ int new_token_slot(const DecodeParams& p, int s) {
+  const int L = p.context_lens[s];
+  if (L <= 0 || L > (p.max_blocks_per_seq << p.log2_block)) return -1;
+  if (p.mode == kModeFixed && (long long)L > (long long)p.max_parts * p.part_chunks * kChunk) return -1;
+  const int t = L - 1;
+  const int phys = p.block_tables[(size_t)s * p.max_blocks_per_seq + (t >> p.log2_block)];
+  if (phys < 0 || phys >= p.num_blocks) return -1;  // no such slot: nothing stored, as in the plain write
+  return phys * p.block_size + (t & (p.block_size - 1));
+}
+
+// The launch after the attention kernel, one workgroup per (sequence, KV
+// head): merges the sequence's pieces when it was split and, for
+// pa_write_decode, stores its new token into the cache. That store follows
+// every read of the cache by the attention kernel, which took the new token
+// from k_new/v_new; its values are read first and stored last, so its round
+// trips overlap the merge's.
+template <int D, typename U>
+__global__ __launch_bounds__(64) void merge_kernel(DecodeParams p) {
+  __shared__ float wgt[kMaxGroup][kMergeTile];
+  __shared__ float ls[kMaxGroup][kMergeTile];
+  constexpr int PER = D / 64;
+  const int s = blockIdx.x, kvh = blockIdx.y, lane = threadIdx.x;
+  const int Hkv = p.num_kv_heads;
+  U kn[PER], vn[PER];
+  int slot = -1;
+  if (p.k_new) {
+    const size_t src = ((size_t)s * Hkv + kvh) * D + lane;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      kn[i] = static_cast<const U*>(p.k_new)[src + 64 * i];
+      vn[i] = static_cast<const U*>(p.v_new)[src + 64 * i];
+    }
+    slot = new_token_slot(p, s);
+  }
+  if (p.merge) merge_sequence<D>(p, s, kvh, lane, wgt, ls);
+  if (slot >= 0) {
+    const int B = p.block_size, phys = slot / B, off = slot % B;
+    U* kd = const_cast<U*>(static_cast<const U*>(p.k_cache)) + (((size_t)phys * Hkv + kvh) * B + off) * D + lane;
+    U* vd = const_cast<U*>(static_cast<const U*>(p.v_cache)) + (((size_t)phys * Hkv + kvh) * D + lane) * B + off;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      kd[64 * i] = kn[i];
+      vd[(size_t)64 * i * B] = vn[i];
+    }
   }
 }
 
@@ -1040,11 +1177,18 @@ hipError_t launch_decode(const DecodeParams& p, int elem, int head_dim, int algo
   const void* fn = decode_fn(elem, head_dim, algo, G);
   if (!fn) return hipErrorInvalidDeviceFunction;
   DecodeParams args = p;
+  args.merge = merge ? 1 : 0;
   void* kargs[] = {&args};
   hipError_t e = hipLaunchKernel(fn, dim3(workers, (unsigned)p.num_kv_heads, 1), dim3(64, 1, 1), kargs, 0, stream);
-  if (e != hipSuccess || !merge) return e;
-  const void* mf = head_dim == 64 ? reinterpret_cast<const void*>(&merge_kernel<64>)
-                                  : reinterpret_cast<const void*>(&merge_kernel<128>);
+  // the closing launch merges split sequences and stores the fused write
+  if (e != hipSuccess || (!merge && !p.k_new)) return e;
+  const void* mf;
+  if (elem == kF32)
+    mf = head_dim == 64 ? reinterpret_cast<const void*>(&merge_kernel<64, uint32_t>)
+                        : reinterpret_cast<const void*>(&merge_kernel<128, uint32_t>);
+  else
+    mf = head_dim == 64 ? reinterpret_cast<const void*>(&merge_kernel<64, uint16_t>)
+                        : reinterpret_cast<const void*>(&merge_kernel<128, uint16_t>);
   return hipLaunchKernel(mf, dim3((unsigned)p.num_seqs, (unsigned)p.num_kv_heads, 1), dim3(64, 1, 1), kargs, 0,
                          stream);
 }

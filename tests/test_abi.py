@@ -43,7 +43,7 @@ def test_exports_match_header(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.pa_abi_version() == 2
+    assert lib.pa_abi_version() == 3
     assert lib.pa_status_string(OK) == b"ok"
     assert lib.pa_status_string(WORKSPACE) == b"workspace missing or too small"
     assert lib.pa_status_string(123) == b"unknown status"
@@ -93,6 +93,21 @@ def test_decode_workspace_sizes(lib):
     assert auto >= (1024 + 256) * 32 * 130 * 4             # balanced: workers + sequences slots
     assert f(4, 30, 8, 128, 1024, -1) == 0                 # rejected shape
     assert f(4, 32, 8, 128, 1024, 40) == 0
+
+
+def test_write_decode_argument_checks(lib):
+    args = decode_args()
+    # out, q, k_new, v_new, k, v, then the decode tail without `algo`
+    full = args[:2] + [FAKE, FAKE] + args[2:20] + [args[21]]
+    bad = list(full)
+    bad[2] = None
+    assert lib.pa_write_decode(*bad) == INVALID
+    bad = list(full)
+    bad[3] = FAKE + 8
+    assert lib.pa_write_decode(*bad) == INVALID
+    bad = list(full)
+    bad[11] = 96                                             # head_dim
+    assert lib.pa_write_decode(*bad) == UNSUPPORTED
 
 
 def test_write_and_copy_argument_checks(lib):
