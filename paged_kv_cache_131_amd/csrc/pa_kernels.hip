@@ -977,11 +977,16 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
 // loaded independently; longer piece lists take a plain per-output loop.
 constexpr int kMergeTile = 256;
 
-// Combines one (sequence, KV head)'s pieces when it was split.
+// Pieces whose partial outputs the merge requests together with the (m, l)
+// pairs, before the weights are known (most split sequences have 2-3).
+constexpr int kMergePre = 4;
+
+// Combines one (sequence, KV head)'s pieces when it was split. L_raw and the
+// split record (meta_first, meta_n; balanced mode) were loaded by the caller.
 template <int D>
 __device__ void merge_sequence(const DecodeParams& p, int s, int kvh, int lane, float (*wgt)[kMergeTile],
-                               float (*ls)[kMergeTile]) {
-  int L = eff_len(p, s);
+                               float (*ls)[kMergeTile], int L_raw, int meta_first, int meta_n) {
+  int L = min(L_raw, p.max_blocks_per_seq << p.log2_block);
   int first_slot, npieces;
   if (p.mode == kModeFixed) {
     const int P = p.part_chunks * kChunk;
@@ -991,8 +996,8 @@ __device__ void merge_sequence(const DecodeParams& p, int s, int kvh, int lane, 
     first_slot = s * p.max_parts;
   } else {
     if (L <= 0) return;
-    first_slot = p.ws_meta[2 * s];
-    npieces = p.ws_meta[2 * s + 1];
+    first_slot = meta_first;
+    npieces = meta_n;
   }
   if (npieces <= 1) return;
   if (npieces > kMergeTile) {
@@ -1001,6 +1006,17 @@ __device__ void merge_sequence(const DecodeParams& p, int s, int kvh, int lane, 
   }
   const int g = p.group, Hq = p.num_heads;
   const size_t head0 = (size_t)kvh * g;
+  constexpr int PER = D / 64;
+  const size_t step = (size_t)Hq * D;
+  const float* acc0 = p.ws_acc + ((size_t)first_slot * Hq + head0) * D + lane;
+  float pre[kMaxGroup][kMergePre][PER];
+#pragma unroll
+  for (int h = 0; h < kMaxGroup; ++h)
+#pragma unroll
+    for (int k = 0; k < kMergePre; ++k)
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        pre[h][k][i] = (h < g && k < npieces) ? acc0[(size_t)h * D + k * step + 64 * i] : 0.f;
   // (m, l) of every (head, piece): m into wgt, l kept in the same slot's pair
   for (int i = lane; i < g * npieces; i += 64) {
     const int h = i / npieces, k = i % npieces;
@@ -1022,15 +1038,23 @@ __device__ void merge_sequence(const DecodeParams& p, int s, int kvh, int lane, 
     for (int k = 0; k < npieces; ++k) wgt[lane][k] *= inv;
   }
   __syncthreads();
-  constexpr int PER = D / 64;
-  for (int h = 0; h < g; ++h) {
+  // pieces in ascending order: the first kMergePre from registers, the rest loaded here
+#pragma unroll
+  for (int h = 0; h < kMaxGroup; ++h) {
+    if (h >= g) break;
     float acc[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-    const float* base = p.ws_acc + ((size_t)first_slot * Hq + head0 + h) * D + lane;
-    const size_t step = (size_t)Hq * D;
-#pragma unroll 4
-    for (int k = 0; k < npieces; ++k) {
+#pragma unroll
+    for (int k = 0; k < kMergePre; ++k) {
+      if (k < npieces) {
+        const float w = wgt[h][k];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, pre[h][k][i], acc[i]);
+      }
+    }
+    const float* base = acc0 + (size_t)h * D;
+    for (int k = kMergePre; k < npieces; ++k) {
       const float w = wgt[h][k];
 #pragma unroll
       for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, base[k * step + 64 * i], acc[i]);
@@ -1044,8 +1068,7 @@ __device__ void merge_sequence(const DecodeParams& p, int s, int kvh, int lane, 
 // Position-L-1 slot of sequence s for the fused write, or -1 when no write is
 // made: the conditions under which the attention kernel took that position
 // from k_new/v_new (new_token_pos), and a table entry inside the pool.
-__device__ __forceinline__ int new_token_slot(const DecodeParams& p, int s) {
-  const int L = p.context_lens[s];
+__device__ __forceinline__ int new_token_slot(const DecodeParams& p, int s, int L) {
   if (L <= 0 || L > (p.max_blocks_per_seq << p.log2_block)) return -1;
   if (p.mode == kModeFixed && (long long)L > (long long)p.max_parts * p.part_chunks * kChunk) return -1;
   const int t = L - 1;
@@ -1067,26 +1090,36 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeParams p) {
   constexpr int PER = D / 64;
   const int s = blockIdx.x, kvh = blockIdx.y, lane = threadIdx.x;
   const int Hkv = p.num_kv_heads;
-  U kn[PER], vn[PER];
-  int slot = -1;
-  if (p.k_new) {
+  // every load that depends on nothing else is issued first
+  const int L = p.context_lens[s];
+  int meta_first = 0, meta_n = 0;
+  if (p.merge && p.mode != kModeFixed) {
+    meta_first = p.ws_meta[2 * s];
+    meta_n = p.ws_meta[2 * s + 1];
+  }
+  // the new token, read unconditionally (from q without one: an in-bounds
+  // row, never stored) and widened, so nothing waits for it before the merge
+  uint32_t kn[PER], vn[PER];
+  {
     const size_t src = ((size_t)s * Hkv + kvh) * D + lane;
+    const U* ks = static_cast<const U*>(p.k_new ? p.k_new : p.q) + src;
+    const U* vs = static_cast<const U*>(p.v_new ? p.v_new : p.q) + src;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      kn[i] = static_cast<const U*>(p.k_new)[src + 64 * i];
-      vn[i] = static_cast<const U*>(p.v_new)[src + 64 * i];
+      kn[i] = ks[64 * i];
+      vn[i] = vs[64 * i];
     }
-    slot = new_token_slot(p, s);
   }
-  if (p.merge) merge_sequence<D>(p, s, kvh, lane, wgt, ls);
+  if (p.merge) merge_sequence<D>(p, s, kvh, lane, wgt, ls, L, meta_first, meta_n);
+  const int slot = p.k_new ? new_token_slot(p, s, L) : -1;
   if (slot >= 0) {
     const int B = p.block_size, phys = slot / B, off = slot % B;
     U* kd = const_cast<U*>(static_cast<const U*>(p.k_cache)) + (((size_t)phys * Hkv + kvh) * B + off) * D + lane;
     U* vd = const_cast<U*>(static_cast<const U*>(p.v_cache)) + (((size_t)phys * Hkv + kvh) * D + lane) * B + off;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      kd[64 * i] = kn[i];
-      vd[(size_t)64 * i * B] = vn[i];
+      kd[64 * i] = static_cast<U>(kn[i]);
+      vd[(size_t)64 * i * B] = static_cast<U>(vn[i]);
     }
   }
 }
