@@ -29,7 +29,7 @@ int log2_exact(int v) {
 
 // How a decode call splits its work.
 struct Plan {
-  int mode;         // pa::kModeBalanced / pa::kModeFixed
+  int mode;         // pa::Mode
   int part_chunks;  // fixed: chunks per partition
   int max_parts;    // fixed: partitions per sequence
   int max_workers;  // balanced: upper bound of workers per KV head
@@ -51,11 +51,15 @@ Plan make_plan(int num_seqs, int num_kv_heads, int max_context_len, int partitio
   if (partition_size > 0) {
     pl.part_chunks = partition_size / pa::kChunk;
     pl.max_parts = (int)((max_chunks + pl.part_chunks - 1) / pl.part_chunks);
-  } else {  // NONE, or AUTO with too many sequences: one wave per (sequence, KV head)
+  } else {  // NONE, or AUTO with too many sequences: every sequence in one piece
     pl.part_chunks = (int)(max_chunks < INT_MAX ? max_chunks : INT_MAX);
     pl.max_parts = 1;
   }
   if (pl.max_parts < 1) pl.max_parts = 1;
+  // persistent workers take real partitions in ranges when the per-worker
+  // length scan is affordable; else (and without partitions, where whole
+  // sequences would be dealt out unevenly) one workgroup per partition
+  if (num_seqs <= pa::kMaxBalancedSeqs && pl.max_parts > 1) pl.mode = pa::kModeFixedStream;
   pl.slots = pl.max_parts > 1 ? (size_t)num_seqs * pl.max_parts : 0;
   return pl;
 }
@@ -253,10 +257,11 @@ static pa_status decode_impl(void* out, const void* q, const void* k_new, const 
 
   const int elem = dtype == PA_F32 ? pa::kF32 : (dtype == PA_F16 ? pa::kF16 : pa::kBF16);
   long long workers;
-  if (pl.mode == pa::kModeBalanced) {
+  if (pl.mode == pa::kModeBalanced || pl.mode == pa::kModeFixedStream) {
     const int target = workers_target(elem, head_dim, kernel_algo, G);
     workers = (target + num_kv_heads - 1) / num_kv_heads;
-    if (workers > pl.max_workers) workers = pl.max_workers;
+    const long long cap = pl.mode == pa::kModeBalanced ? pl.max_workers : (long long)num_seqs * pl.max_parts;
+    if (workers > cap) workers = cap;
     if (workers < 1) workers = 1;
   } else {
     workers = (long long)num_seqs * pl.max_parts;

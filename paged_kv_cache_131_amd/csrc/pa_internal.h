@@ -20,7 +20,10 @@ constexpr int kMaxGroup = 8;
 constexpr int kMaxBalancedSeqs = 4096;
 
 enum Elem : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
-enum Mode : int { kModeBalanced = 0, kModeFixed = 1 };
+// Balanced: chunk ranges per persistent worker. Fixed: one workgroup per
+// partition. FixedStream: fixed partitions taken in ranges by persistent
+// workers.
+enum Mode : int { kModeBalanced = 0, kModeFixed = 1, kModeFixedStream = 2 };
 enum Algo : int { kAlgoVector = 1, kAlgoMfma = 2 };
 
 struct DecodeParams {
@@ -44,7 +47,7 @@ struct DecodeParams {
   int32_t num_blocks;
   int32_t max_blocks_per_seq;
   float scale_log2;     // scale * log2(e): scores live in base-2 exponent units
-  int32_t mode;         // kModeBalanced or kModeFixed
+  int32_t mode;         // Mode
   int32_t part_chunks;  // fixed mode: chunks per partition
   int32_t max_parts;    // fixed mode: partitions per sequence (grid.x = num_seqs*max_parts)
   int32_t out_dtype;    // Elem of `out`

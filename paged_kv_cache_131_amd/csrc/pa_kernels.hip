@@ -168,21 +168,29 @@ __device__ __forceinline__ int pick_block(ChunkIds c, int tok, int log2_block, i
   return min(max(pick_entry(c, tok, log2_block, lbl), 0), num_blocks - 1);
 }
 
-__device__ __forceinline__ int eff_len(const DecodeParams& p, int s) {
-  const int cap = p.max_blocks_per_seq << p.log2_block;
-  return min(p.context_lens[s], cap);
+// The length a decode works on: the stored one, cut to what the block
+// table can address and, with fixed partitions, to max_parts partitions (a
+// context longer than the host's bound is cut there rather than left
+// without a merging piece).
+__device__ __forceinline__ int capped_len(const DecodeParams& p, int L_raw) {
+  int L = min(L_raw, p.max_blocks_per_seq << p.log2_block);
+  if (p.mode != kModeBalanced) L = (int)min((long long)L, (long long)p.max_parts * p.part_chunks * kChunk);
+  return L;
 }
 
-// The same for a wave-uniform s, read with a scalar load so that it never
-// waits behind the K/V vector loads in flight.
+// Stored length of sequence s (wave-uniform), read with a scalar load so
+// that it never waits behind the K/V vector loads in flight.
 __device__ __forceinline__ int len_uniform(const DecodeParams& p, int s) {
   const const_i32* lens = (const const_i32*)p.context_lens;
   return lens[__builtin_amdgcn_readfirstlane(s)];
 }
 
-__device__ __forceinline__ int eff_len_uniform(const DecodeParams& p, int s) {
-  return min(len_uniform(p, s), p.max_blocks_per_seq << p.log2_block);
-}
+// The workers of the balanced split and of the partition stream copy every
+// stored length into LDS at their start (num_seqs entries of dynamic shared
+// memory) and walk their sequences from there.
+extern __shared__ int32_t g_lens[];
+
+__device__ __forceinline__ int lds_len(int s) { return __builtin_amdgcn_readfirstlane(g_lens[s]); }
 
 // Position of the token the fused write stores for a piece ending at t1 of
 // a sequence of stored length L_raw, cut to L: its last, when the piece holds
@@ -697,26 +705,6 @@ __device__ void write_zero_rows(const DecodeParams& p, int s, int kvh, int lane)
   for (int idx = lane; idx < g * D; idx += 64) store_out(p.out, base + idx, 0.f, p.out_dtype);
 }
 
-template <int D>
-__device__ void merge_pieces(const DecodeParams& p, int s, int kvh, int lane, int first_slot, int npieces) {
-  const int g = p.group, Hq = p.num_heads;
-  for (int idx = lane; idx < g * D; idx += 64) {
-    const int h = idx / D, dd = idx % D;
-    const int head = kvh * g + h;
-    float M = kNegInf;
-    for (int k = 0; k < npieces; ++k)
-      M = fmaxf(M, p.ws_ml[((size_t)(first_slot + k) * Hq + head) * 2]);
-    float num = 0.f, den = 0.f;
-    for (int k = 0; k < npieces; ++k) {
-      const size_t r = (size_t)(first_slot + k) * Hq + head;
-      const float wgt = fast_exp2(p.ws_ml[r * 2] - M);
-      den = fmaf(wgt, p.ws_ml[r * 2 + 1], den);
-      num = fmaf(wgt, p.ws_acc[r * D + dd], num);
-    }
-    store_out(p.out, ((size_t)s * Hq + head) * D + dd, num / den, p.out_dtype);
-  }
-}
-
 __device__ __forceinline__ long long owner_of(long long c, long long W, long long T) {
   return ((c + 1) * W - 1) / T;
 }
@@ -726,11 +714,12 @@ __device__ __forceinline__ long long owner_of(long long c, long long W, long lon
 // [start, end); fixed mode: a single partition.
 struct SegmentSource {
   int mode;
-  int s;          // next sequence to look at (balanced) / the sequence (fixed)
+  int s;          // next sequence to look at
   long long c;    // first chunk of sequence s in the laid-out order
+  int k;          // fixed-partition stream: next partition of sequence s
   long long start, end, W, T;
   int w;
-  Segment fixed;  // fixed mode's only segment
+  Segment fixed;  // one-partition-per-workgroup mode's only segment
 
   __device__ Segment next(const DecodeParams& p) {
     if (mode == kModeFixed) {
@@ -738,9 +727,10 @@ struct SegmentSource {
       fixed.valid = 0;
       return g;
     }
+    if (mode == kModeFixedStream) return next_partition(p);
     while (s < p.num_seqs && c < end) {
-      const int L_raw = len_uniform(p, s);
-      const int L = min(L_raw, p.max_blocks_per_seq << p.log2_block);
+      const int L_raw = lds_len(s);
+      const int L = capped_len(p, L_raw);
       const int n = num_chunks(L);
       if (n == 0) {
         ++s;
@@ -763,6 +753,38 @@ struct SegmentSource {
       c += n;
       ++s;
       return uniform(g);
+    }
+    return invalid_segment();
+  }
+
+  // Fixed partitions of part_chunks chunks, laid end to end like the chunks:
+  // the worker takes every partition whose first chunk lies in [start, end).
+  __device__ Segment next_partition(const DecodeParams& p) {
+    const int pc = p.part_chunks;
+    while (s < p.num_seqs && c < end) {
+      const int L_raw = lds_len(s);
+      const int L = capped_len(p, L_raw);
+      const int n = num_chunks(L);
+      const int np = (n + pc - 1) / pc;
+      if (c + (long long)k * pc < start) k = (int)((start - c + pc - 1) / pc);
+      if (k < np) {
+        if (c + (long long)k * pc >= end) break;
+        Segment g;
+        g.s = s;
+        g.t0 = k * pc * kChunk;
+        g.t1 = (int)min((long long)g.t0 + (long long)pc * kChunk, (long long)L);
+        g.lbl = (g.t1 - 1) >> p.log2_block;
+        g.tnew = new_token_pos(p, g.t1, L, L_raw);
+        g.npieces = np;
+        g.slot = s * p.max_parts + k;
+        g.first_slot = s * p.max_parts;
+        g.valid = 1;
+        ++k;
+        return uniform(g);
+      }
+      c += n;
+      ++s;
+      k = 0;
     }
     return invalid_segment();
   }
@@ -843,7 +865,6 @@ __device__ void run_stream(const DecodeParams& p, typename Eng::Smem& sm, Segmen
   Eng eng;
   typename Eng::Q q, qn;
   eng.load_q(q, p, A.s, kvh, lane);
-  eng.reset(q);
   Pos p0{0, A.t0};
   Pos p1 = advance(p0, A, B, C);
   Pos p2 = advance(p1, A, B, C);
@@ -852,6 +873,7 @@ __device__ void run_stream(const DecodeParams& p, typename Eng::Smem& sm, Segmen
   typename Eng::Frag f;
   eng.load_k(f, p, kvh, lane, p0.cs, &ids0, A);
   eng.load_v(f, p, kvh, lane, p0.cs, &ids0, A);
+  eng.reset(q);  // after the first K/V loads are issued: only the first QK needs q
   for (;;) {
     const ChunkIds ids2 = ids_at(p, p2, A, B, C);
     const bool leaving = p1.rel != 0;                       // p0 is the current segment's last chunk
@@ -891,11 +913,8 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
   if (p.mode == kModeFixed) {
     const int s = w / p.max_parts, part = w % p.max_parts;
     const int P = p.part_chunks * kChunk;
-    // a context longer than max_parts partitions (longer than the host's
-    // bound) is cut there rather than left without a merging piece
-    const long long cap = (long long)p.max_parts * P;
     const int L_raw = len_uniform(p, s);
-    const int L = (int)min((long long)min(L_raw, p.max_blocks_per_seq << p.log2_block), cap);
+    const int L = capped_len(p, L_raw);
     if (L <= 0) {
       if (part == 0) write_zero_rows<Eng, D>(p, s, kvh, lane);
       return;
@@ -917,13 +936,18 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
     return;
   }
 
-  // Balanced split: every worker scans the lengths itself (S <=
-  // kMaxBalancedSeqs), so no planning launch is needed.
+  // Balanced split or fixed-partition stream: every worker scans the lengths
+  // itself (S <= kMaxBalancedSeqs), so no planning launch is needed.
   const int S = p.num_seqs;
   const int per = (S + 63) >> 6;
   const int s_lo = min(lane * per, S), s_hi = min(s_lo + per, S);
   long long mine = 0;
-  for (int s = s_lo; s < s_hi; ++s) mine += num_chunks(eff_len(p, s));
+  for (int s = s_lo; s < s_hi; ++s) {
+    const int L_raw = p.context_lens[s];
+    g_lens[s] = L_raw;
+    mine += num_chunks(capped_len(p, L_raw));
+  }
+  __syncthreads();
   long long incl = mine;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -934,7 +958,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
   const long long excl = incl - mine;
 
   for (int s = w; s < S; s += W)
-    if (eff_len_uniform(p, s) <= 0) write_zero_rows<Eng, D>(p, s, kvh, lane);
+    if (capped_len(p, lds_len(s)) <= 0) write_zero_rows<Eng, D>(p, s, kvh, lane);
   if (T == 0) return;
   // with no more workers than chunks every range is non-empty, so the pieces
   // of a sequence are exactly the workers owner_of(first chunk)..owner_of(last)
@@ -950,7 +974,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
   if (lane == owner) {
     long long c = excl;
     for (int s = s_lo; s < s_hi; ++s) {
-      const int n = num_chunks(eff_len(p, s));
+      const int n = num_chunks(capped_len(p, g_lens[s]));
       if (start < c + n) {
         s_first = s;
         c_first = c;
@@ -961,6 +985,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
   }
   src.s = __builtin_amdgcn_readfirstlane(__shfl(s_first, owner));
   src.c = __shfl(c_first, owner);
+  src.k = 0;
   src.start = start;
   src.end = end;
   src.W = Wn;
@@ -972,96 +997,157 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
 // Combine the partial results of every split (sequence, KV head): the
 // pieces' maxima and exponential sums give piece k of head h the weight
 // w_k = 2^(m_k - M) / sum_j 2^(m_j - M) l_j with M = max_j m_j (base-2 units),
-// and out = sum_k w_k acc_k. Up to kMergeTile pieces the (m, l) pairs are
-// staged in LDS with one parallel load pass and every partial output is
-// loaded independently; longer piece lists take a plain per-output loop.
+// and out = sum_k w_k acc_k. W waves share a (sequence, heads) unit: wave v
+// sums pieces v, v+W, v+2W, ... in ascending order for all its heads at once
+// (many independent loads in flight) and the W partial sums are added in
+// wave order. Each wave's first kPre pieces are requested together with the
+// (m, l) pairs, which are staged in LDS up to kMergeTile pieces; longer piece
+// lists take a plain per-output loop. The balanced split leaves few pieces
+// per sequence: one wave per (sequence, KV head). Fixed partitions leave
+// many: four waves per (sequence, query head).
 constexpr int kMergeTile = 256;
 
-// Pieces whose partial outputs the merge requests together with the (m, l)
-// pairs, before the weights are known (most split sequences have 2-3).
-constexpr int kMergePre = 4;
+template <int W>
+struct MergeSmem {
+  float wgt[kMaxGroup][kMergeTile];
+  float ls[kMaxGroup][kMergeTile];
+  float part[W][kMaxGroup][128];
+};
 
-// Combines one (sequence, KV head)'s pieces when it was split. L_raw and the
-// split record (meta_first, meta_n; balanced mode) were loaded by the caller.
-template <int D>
-__device__ void merge_sequence(const DecodeParams& p, int s, int kvh, int lane, float (*wgt)[kMergeTile],
-                               float (*ls)[kMergeTile], int L_raw, int meta_first, int meta_n) {
-  int L = min(L_raw, p.max_blocks_per_seq << p.log2_block);
+template <int D, int W>
+__device__ void merge_long(const DecodeParams& p, int s, int head0, int nh, int tid, int first_slot, int npieces) {
+  const int Hq = p.num_heads;
+  for (int idx = tid; idx < nh * D; idx += 64 * W) {
+    const int head = head0 + idx / D, dd = idx % D;
+    float M = kNegInf;
+    for (int k = 0; k < npieces; ++k) M = fmaxf(M, p.ws_ml[((size_t)(first_slot + k) * Hq + head) * 2]);
+    float num = 0.f, den = 0.f;
+    for (int k = 0; k < npieces; ++k) {
+      const size_t r = (size_t)(first_slot + k) * Hq + head;
+      const float wgt = fast_exp2(p.ws_ml[r * 2] - M);
+      den = fmaf(wgt, p.ws_ml[r * 2 + 1], den);
+      num = fmaf(wgt, p.ws_acc[r * D + dd], num);
+    }
+    store_out(p.out, ((size_t)s * Hq + head) * D + dd, num / den, p.out_dtype);
+  }
+}
+
+// Combines the pieces of query heads head0 .. head0+nh-1 of sequence s when
+// it was split; called by the whole workgroup. L_raw and the split record
+// (meta_first, meta_n; balanced mode) were loaded by the caller.
+template <int D, int W>
+__device__ void merge_sequence(const DecodeParams& p, MergeSmem<W>& sm, int s, int head0, int nh, int tid, int L_raw,
+                               int meta_first, int meta_n) {
+  static_assert(D <= 128, "partial-sum tile");
+  constexpr int kPre = W == 1 ? 4 : 2;
+  const int L = capped_len(p, L_raw);
+  if (L <= 0) return;
   int first_slot, npieces;
-  if (p.mode == kModeFixed) {
+  if (p.mode != kModeBalanced) {
     const int P = p.part_chunks * kChunk;
-    L = (int)min((long long)L, (long long)p.max_parts * P);
-    if (L <= 0) return;
     npieces = (L + P - 1) / P;
     first_slot = s * p.max_parts;
   } else {
-    if (L <= 0) return;
     first_slot = meta_first;
     npieces = meta_n;
   }
   if (npieces <= 1) return;
   if (npieces > kMergeTile) {
-    merge_pieces<D>(p, s, kvh, lane, first_slot, npieces);
+    merge_long<D, W>(p, s, head0, nh, tid, first_slot, npieces);
     return;
   }
-  const int g = p.group, Hq = p.num_heads;
-  const size_t head0 = (size_t)kvh * g;
+  const int Hq = p.num_heads;
+  const int wave = tid >> 6, lane = tid & 63;
   constexpr int PER = D / 64;
   const size_t step = (size_t)Hq * D;
   const float* acc0 = p.ws_acc + ((size_t)first_slot * Hq + head0) * D + lane;
-  float pre[kMaxGroup][kMergePre][PER];
+  float pre[kPre][kMaxGroup][PER];
+#pragma unroll
+  for (int j = 0; j < kPre; ++j)
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h)
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int k = wave + W * j;
+        pre[j][h][i] = (h < nh && k < npieces) ? acc0[(size_t)h * D + k * step + 64 * i] : 0.f;
+      }
+  // (m, l) of every (head, piece): m into wgt, l kept in the same slot's pair
+  for (int i = tid; i < nh * npieces; i += 64 * W) {
+    const int h = i / npieces, k = i % npieces;
+    const size_t r = ((size_t)(first_slot + k) * Hq + head0 + h) * 2;
+    sm.wgt[h][k] = p.ws_ml[r];
+    sm.ls[h][k] = p.ws_ml[r + 1];
+  }
+  __syncthreads();
+  // weights: wave v handles heads v, v+W, ...; lanes over pieces
+  for (int h = wave; h < nh; h += W) {
+    float M = kNegInf;
+    for (int k = lane; k < npieces; k += 64) M = fmaxf(M, sm.wgt[h][k]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    float den = 0.f;
+    for (int k = lane; k < npieces; k += 64) {
+      const float e = fast_exp2(sm.wgt[h][k] - M);
+      sm.wgt[h][k] = e;
+      den = fmaf(e, sm.ls[h][k], den);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
+    const float inv = 1.f / den;
+    for (int k = lane; k < npieces; k += 64) sm.wgt[h][k] *= inv;
+  }
+  __syncthreads();
+  float acc[kMaxGroup][PER];
 #pragma unroll
   for (int h = 0; h < kMaxGroup; ++h)
 #pragma unroll
-    for (int k = 0; k < kMergePre; ++k)
+    for (int i = 0; i < PER; ++i) acc[h][i] = 0.f;
 #pragma unroll
-      for (int i = 0; i < PER; ++i)
-        pre[h][k][i] = (h < g && k < npieces) ? acc0[(size_t)h * D + k * step + 64 * i] : 0.f;
-  // (m, l) of every (head, piece): m into wgt, l kept in the same slot's pair
-  for (int i = lane; i < g * npieces; i += 64) {
-    const int h = i / npieces, k = i % npieces;
-    const size_t r = ((size_t)(first_slot + k) * Hq + head0 + h) * 2;
-    wgt[h][k] = p.ws_ml[r];
-    ls[h][k] = p.ws_ml[r + 1];
-  }
-  __syncthreads();
-  if (lane < g) {
-    float M = kNegInf;
-    for (int k = 0; k < npieces; ++k) M = fmaxf(M, wgt[lane][k]);
-    float den = 0.f;
-    for (int k = 0; k < npieces; ++k) {
-      const float e = fast_exp2(wgt[lane][k] - M);
-      wgt[lane][k] = e;
-      den = fmaf(e, ls[lane][k], den);
-    }
-    const float inv = 1.f / den;
-    for (int k = 0; k < npieces; ++k) wgt[lane][k] *= inv;
-  }
-  __syncthreads();
-  // pieces in ascending order: the first kMergePre from registers, the rest loaded here
+  for (int j = 0; j < kPre; ++j) {
+    const int k = wave + W * j;
+    if (k < npieces) {
 #pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h) {
-    if (h >= g) break;
-    float acc[PER];
+      for (int h = 0; h < kMaxGroup; ++h) {
+        if (h < nh) {
+          const float w = sm.wgt[h][k];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-#pragma unroll
-    for (int k = 0; k < kMergePre; ++k) {
-      if (k < npieces) {
-        const float w = wgt[h][k];
-#pragma unroll
-        for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, pre[h][k][i], acc[i]);
+          for (int i = 0; i < PER; ++i) acc[h][i] = fmaf(w, pre[j][h][i], acc[h][i]);
+        }
       }
     }
-    const float* base = acc0 + (size_t)h * D;
-    for (int k = kMergePre; k < npieces; ++k) {
-      const float w = wgt[h][k];
+  }
+#pragma unroll 2
+  for (int k = wave + W * kPre; k < npieces; k += W) {
 #pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, base[k * step + 64 * i], acc[i]);
+    for (int h = 0; h < kMaxGroup; ++h) {
+      if (h < nh) {
+        const float w = sm.wgt[h][k];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) acc[h][i] = fmaf(w, acc0[(size_t)h * D + k * step + 64 * i], acc[h][i]);
+      }
     }
-    const size_t o = ((size_t)s * Hq + head0 + h) * D + lane;
+  }
+  if constexpr (W == 1) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) store_out(p.out, o + 64 * i, acc[i], p.out_dtype);
+    for (int h = 0; h < kMaxGroup; ++h)
+      if (h < nh)
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+          store_out(p.out, ((size_t)s * Hq + head0 + h) * D + lane + 64 * i, acc[h][i], p.out_dtype);
+  } else {
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h)
+      if (h < nh)
+#pragma unroll
+        for (int i = 0; i < PER; ++i) sm.part[wave][h][lane + 64 * i] = acc[h][i];
+    __syncthreads();
+    const int nw = npieces < W ? npieces : W;
+    for (int idx = tid; idx < nh * D; idx += 64 * W) {
+      const int h = idx / D, dd = idx % D;
+      float o = sm.part[0][h][dd];
+      for (int v = 1; v < nw; ++v) o += sm.part[v][h][dd];
+      store_out(p.out, ((size_t)s * Hq + head0 + h) * D + dd, o, p.out_dtype);
+    }
   }
 }
 
@@ -1069,57 +1155,62 @@ __device__ void merge_sequence(const DecodeParams& p, int s, int kvh, int lane, 
 // made: the conditions under which the attention kernel took that position
 // from k_new/v_new (new_token_pos), and a table entry inside the pool.
 __device__ __forceinline__ int new_token_slot(const DecodeParams& p, int s, int L) {
-  if (L <= 0 || L > (p.max_blocks_per_seq << p.log2_block)) return -1;
-  if (p.mode == kModeFixed && (long long)L > (long long)p.max_parts * p.part_chunks * kChunk) return -1;
+  if (L <= 0 || capped_len(p, L) != L) return -1;
   const int t = L - 1;
   const int phys = p.block_tables[(size_t)s * p.max_blocks_per_seq + (t >> p.log2_block)];
   if (phys < 0 || phys >= p.num_blocks) return -1;  // no such slot: nothing stored, as in the plain write
   return phys * p.block_size + (t & (p.block_size - 1));
 }
 
-// The launch after the attention kernel, one workgroup per (sequence, KV
-// head): merges the sequence's pieces when it was split and, for
-// pa_write_decode, stores its new token into the cache. That store follows
+// The launch after the attention kernel: workgroups of W waves, grid
+// (sequences, KV heads, head split Z) with g / Z query heads each. It merges
+// the sequence's pieces when it was split and, for pa_write_decode, the
+// z = 0 workgroup stores the new token into the cache. That store follows
 // every read of the cache by the attention kernel, which took the new token
 // from k_new/v_new; its values are read first and stored last, so its round
 // trips overlap the merge's.
-template <int D, typename U>
-__global__ __launch_bounds__(64) void merge_kernel(DecodeParams p) {
-  __shared__ float wgt[kMaxGroup][kMergeTile];
-  __shared__ float ls[kMaxGroup][kMergeTile];
-  constexpr int PER = D / 64;
-  const int s = blockIdx.x, kvh = blockIdx.y, lane = threadIdx.x;
+template <int D, typename U, int W>
+__global__ __launch_bounds__(64 * W) void merge_kernel(DecodeParams p) {
+  __shared__ MergeSmem<W> sm;
+  const int s = blockIdx.x, kvh = blockIdx.y, tid = threadIdx.x;
   const int Hkv = p.num_kv_heads;
+  const int nh = p.group / gridDim.z, head0 = kvh * p.group + (int)blockIdx.z * nh;
   // every load that depends on nothing else is issued first
   const int L = p.context_lens[s];
   int meta_first = 0, meta_n = 0;
-  if (p.merge && p.mode != kModeFixed) {
+  if (p.merge && p.mode == kModeBalanced) {
     meta_first = p.ws_meta[2 * s];
     meta_n = p.ws_meta[2 * s + 1];
   }
-  // the new token, read unconditionally (from q without one: an in-bounds
-  // row, never stored) and widened, so nothing waits for it before the merge
-  uint32_t kn[PER], vn[PER];
+  // the new token's elements e = tid, tid + 64W, ..., read unconditionally
+  // (from q without one: an in-bounds row, never stored) and widened, so
+  // nothing waits for them before the merge
+  constexpr int NE = (D + 64 * W - 1) / (64 * W);
+  uint32_t kn[NE], vn[NE];
   {
-    const size_t src = ((size_t)s * Hkv + kvh) * D + lane;
+    const size_t src = ((size_t)s * Hkv + kvh) * D;
     const U* ks = static_cast<const U*>(p.k_new ? p.k_new : p.q) + src;
     const U* vs = static_cast<const U*>(p.v_new ? p.v_new : p.q) + src;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      kn[i] = ks[64 * i];
-      vn[i] = vs[64 * i];
+    for (int j = 0; j < NE; ++j) {
+      const int e = min(tid + 64 * W * j, D - 1);
+      kn[j] = ks[e];
+      vn[j] = vs[e];
     }
   }
-  if (p.merge) merge_sequence<D>(p, s, kvh, lane, wgt, ls, L, meta_first, meta_n);
-  const int slot = p.k_new ? new_token_slot(p, s, L) : -1;
+  if (p.merge) merge_sequence<D, W>(p, sm, s, head0, nh, tid, L, meta_first, meta_n);
+  const int slot = (p.k_new && blockIdx.z == 0) ? new_token_slot(p, s, L) : -1;
   if (slot >= 0) {
     const int B = p.block_size, phys = slot / B, off = slot % B;
-    U* kd = const_cast<U*>(static_cast<const U*>(p.k_cache)) + (((size_t)phys * Hkv + kvh) * B + off) * D + lane;
-    U* vd = const_cast<U*>(static_cast<const U*>(p.v_cache)) + (((size_t)phys * Hkv + kvh) * D + lane) * B + off;
+    U* kd = const_cast<U*>(static_cast<const U*>(p.k_cache)) + (((size_t)phys * Hkv + kvh) * B + off) * D;
+    U* vd = const_cast<U*>(static_cast<const U*>(p.v_cache)) + ((size_t)phys * Hkv + kvh) * D * B + off;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      kd[64 * i] = static_cast<U>(kn[i]);
-      vd[(size_t)64 * i * B] = static_cast<U>(vn[i]);
+    for (int j = 0; j < NE; ++j) {
+      const int e = tid + 64 * W * j;
+      if (e < D) {
+        kd[e] = static_cast<U>(kn[j]);
+        vd[(size_t)e * B] = static_cast<U>(vn[j]);
+      }
     }
   }
 }
@@ -1212,18 +1303,34 @@ hipError_t launch_decode(const DecodeParams& p, int elem, int head_dim, int algo
   DecodeParams args = p;
   args.merge = merge ? 1 : 0;
   void* kargs[] = {&args};
-  hipError_t e = hipLaunchKernel(fn, dim3(workers, (unsigned)p.num_kv_heads, 1), dim3(64, 1, 1), kargs, 0, stream);
+  // the balanced split and the partition stream keep every length in LDS
+  const size_t lens_lds = p.mode == kModeFixed ? 0 : (size_t)p.num_seqs * sizeof(int32_t);
+  hipError_t e =
+      hipLaunchKernel(fn, dim3(workers, (unsigned)p.num_kv_heads, 1), dim3(64, 1, 1), kargs, lens_lds, stream);
   // the closing launch merges split sequences and stores the fused write
   if (e != hipSuccess || (!merge && !p.k_new)) return e;
+  // few pieces per sequence (balanced split): one wave per (sequence, KV
+  // head); fixed partitions: four waves per (sequence, query head)
+  const bool wide = p.mode != kModeBalanced && merge && p.max_parts > 4;
   const void* mf;
-  if (elem == kF32)
-    mf = head_dim == 64 ? reinterpret_cast<const void*>(&merge_kernel<64, uint32_t>)
-                        : reinterpret_cast<const void*>(&merge_kernel<128, uint32_t>);
-  else
-    mf = head_dim == 64 ? reinterpret_cast<const void*>(&merge_kernel<64, uint16_t>)
-                        : reinterpret_cast<const void*>(&merge_kernel<128, uint16_t>);
-  return hipLaunchKernel(mf, dim3((unsigned)p.num_seqs, (unsigned)p.num_kv_heads, 1), dim3(64, 1, 1), kargs, 0,
-                         stream);
+  if (wide) {
+    if (elem == kF32)
+      mf = head_dim == 64 ? reinterpret_cast<const void*>(&merge_kernel<64, uint32_t, 4>)
+                          : reinterpret_cast<const void*>(&merge_kernel<128, uint32_t, 4>);
+    else
+      mf = head_dim == 64 ? reinterpret_cast<const void*>(&merge_kernel<64, uint16_t, 4>)
+                          : reinterpret_cast<const void*>(&merge_kernel<128, uint16_t, 4>);
+  } else {
+    if (elem == kF32)
+      mf = head_dim == 64 ? reinterpret_cast<const void*>(&merge_kernel<64, uint32_t, 1>)
+                          : reinterpret_cast<const void*>(&merge_kernel<128, uint32_t, 1>);
+    else
+      mf = head_dim == 64 ? reinterpret_cast<const void*>(&merge_kernel<64, uint16_t, 1>)
+                          : reinterpret_cast<const void*>(&merge_kernel<128, uint16_t, 1>);
+  }
+  const unsigned z = wide ? (unsigned)p.group : 1u;
+  return hipLaunchKernel(mf, dim3((unsigned)p.num_seqs, (unsigned)p.num_kv_heads, z), dim3(wide ? 256 : 64, 1, 1),
+                         kargs, 0, stream);
 }
 
 int decode_waves_per_cu(int elem, int head_dim, int algo, int G) {

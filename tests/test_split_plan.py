@@ -76,3 +76,54 @@ def test_fixed_partitions_cover_each_token_once():
             if t0 < L:
                 covered.extend(range(t0, t1))
         assert covered == list(range(L))
+
+
+def partition_stream_plan(lengths, W, pc):
+    """Fixed partitions of pc chunks taken in ranges: worker w runs every
+    partition whose first chunk lies in its chunk range [w*T/Wn, (w+1)*T/Wn),
+    walking the sequences from the one holding its first chunk, as the
+    kernel's partition stream does."""
+    n = [(L + CHUNK - 1) // CHUNK if L > 0 else 0 for L in lengths]
+    pref = np.concatenate([[0], np.cumsum(n)]).astype(np.int64)
+    T = int(pref[-1])
+    runs = []
+    if T == 0:
+        return runs
+    Wn = min(W, T)
+    for w in range(Wn):
+        start, end = w * T // Wn, (w + 1) * T // Wn
+        s = int(np.searchsorted(pref, start, side="right") - 1)
+        c, k = int(pref[s]), 0
+        while s < len(lengths) and c < end:
+            npart = (n[s] + pc - 1) // pc
+            if c + k * pc < start:
+                k = (start - c + pc - 1) // pc
+            if k < npart:
+                if c + k * pc >= end:
+                    break
+                runs.append((w, s, k))
+                k += 1
+                continue
+            c += n[s]
+            s += 1
+            k = 0
+    return runs
+
+
+@pytest.mark.parametrize("W", [1, 2, 3, 7, 16, 128, 5000])
+@pytest.mark.parametrize("pc", [1, 2, 16, 1000])
+def test_partition_stream_runs_each_partition_once(W, pc):
+    rng = np.random.default_rng(W * 7 + pc)
+    for trial in range(40):
+        S = int(rng.integers(1, 10))
+        lengths = rng.integers(0, 2000, size=S).tolist()
+        if trial % 5 == 0:
+            lengths[-1] = 0
+        runs = partition_stream_plan(lengths, W, pc)
+        want = sorted((s, k) for s, L in enumerate(lengths)
+                      for k in range(((L + CHUNK - 1) // CHUNK + pc - 1) // pc))
+        assert sorted((s, k) for (_, s, k) in runs) == want
+        # each worker's partitions come in stream order
+        for w in {r[0] for r in runs}:
+            mine = [(s, k) for (ww, s, k) in runs if ww == w]
+            assert mine == sorted(mine)
