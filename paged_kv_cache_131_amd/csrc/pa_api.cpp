@@ -258,8 +258,10 @@ static pa_status decode_impl(void* out, const void* q, const void* k_new, const 
   const int elem = dtype == PA_F32 ? pa::kF32 : (dtype == PA_F16 ? pa::kF16 : pa::kBF16);
   long long workers;
   if (pl.mode == pa::kModeBalanced || pl.mode == pa::kModeFixedStream) {
+    // rounded down: every worker of the grid must be resident at once, or
+    // the ones left over start only when others finish
     const int target = workers_target(elem, head_dim, kernel_algo, G);
-    workers = (target + num_kv_heads - 1) / num_kv_heads;
+    workers = target / num_kv_heads;
     const long long cap = pl.mode == pa::kModeBalanced ? pl.max_workers : (long long)num_seqs * pl.max_parts;
     if (workers > cap) workers = cap;
     if (workers < 1) workers = 1;
