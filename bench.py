@@ -34,6 +34,9 @@ WORKLOAD_TEXT = {
     "opt13b": "OPT-13B-shaped decode: 64 seqs, 40 heads (MHA), head_dim 128, block 16, fp16, lengths U[128, 2048]",
     "long_context": "long-context split decode: 16 seqs, 64 q / 8 kv heads, head_dim 128, block 32, bf16, "
                     "lengths U[32768, 131072], 512-token partitions",
+    "parallel_sampling": "parallel sampling, last of 256 decode steps: 32 prompts of 1016 tokens x 8 samples "
+                         "sharing the prompt blocks (copy-on-write at divergence), 32 q / 8 kv heads, head_dim 128, "
+                         "block 16, bf16",
 }
 
 
@@ -45,12 +48,11 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def decode_bytes(w) -> dict:
+def decode_bytes(c, context_lens) -> dict:
     """Algorithmic bytes of one pa_decode call: K and V of every context token,
     q, the fp32 output, the block ids read and the lengths."""
-    c = w.cfg
     es = {"f32": 4, "f16": 2, "bf16": 2}[c.etype]
-    L = w.context_lens.astype(np.int64)
+    L = context_lens.astype(np.int64)
     kv = int(L.sum()) * c.num_kv_heads * c.head_dim * 2 * es
     q = c.num_seqs * c.num_heads * c.head_dim * es
     out = c.num_seqs * c.num_heads * c.head_dim * 4
@@ -59,13 +61,11 @@ def decode_bytes(w) -> dict:
     return {"kv": kv, "q": q, "out": out, "ids": ids, "lens": lens, "total": kv + q + out + ids + lens}
 
 
-def write_bytes(w, fused: bool) -> int:
+def write_bytes(c, T: int, fused: bool) -> int:
     """New K and V of every sequence read once and stored once (+ the slot
     mapping when the write is its own call; the fused call finds the slot in
     the block table entries already counted for the decode)."""
-    c = w.cfg
     es = {"f32": 4, "f16": 2, "bf16": 2}[c.etype]
-    T = len(w.slot_mapping)
     return 2 * T * c.num_kv_heads * c.head_dim * es * 2 + (0 if fused else 4 * T)
 
 
@@ -159,6 +159,79 @@ def summarize_counters(fetch_csv: str, write_csv: str, workload: str, calibratio
     return entry
 
 
+class Case:
+    """Device inputs of the timed step and what the report needs about them."""
+
+
+def decode_case(cfg, wl, pb, dev) -> Case:
+    c = Case()
+    t0 = time.perf_counter()
+    w = wl.make_decode_workload(cfg)
+    c.gen_s = time.perf_counter() - t0
+    et = cfg.etype
+    c.w, c.cfg = w, cfg
+    c.kc, c.vc = pb.to_device(w.k_cache, et, dev), pb.to_device(w.v_cache, et, dev)
+    c.q = pb.to_device(w.q, et, dev)
+    c.k_new, c.v_new = pb.to_device(w.k_new, et, dev), pb.to_device(w.v_new, et, dev)
+    c.slots = pb.int32_to_device(w.slot_mapping, dev)
+    c.bt, c.cl = pb.int32_to_device(w.block_tables, dev), pb.int32_to_device(w.context_lens, dev)
+    c.copy_pairs = np.zeros((0, 2), np.int32)  # no shared blocks in this workload
+    c.context_lens, c.max_len = w.context_lens, w.max_context_len
+    c.unique_kv = None
+    c.extra = {}
+    return c
+
+
+def sampling_case(wl, pb, dev, torch, reps: int) -> Case:
+    """Runs steps 1..255 of the parallel-sampling workload on the device
+    (copies + writes, as a serving loop would) and returns step 256; the
+    copy-on-write call of the divergence step is timed on the way."""
+    c = Case()
+    t0 = time.perf_counter()
+    ps = wl.ParallelSamplingWorkload(prompt_len=1016)
+    cfg, et = ps.cfg, ps.cfg.etype
+    c.cfg, c.w = cfg, None
+    c.kc, c.vc = pb.to_device(ps.k_cache, et, dev), pb.to_device(ps.v_cache, et, dev)
+    c.extra = {}
+    for step in range(1, ps.new_tokens + 1):
+        st = ps.step()
+        pairs = pb.int32_to_device(st.block_mapping, dev) if st.block_mapping.shape[0] else None
+        if step == 1 and pairs is not None:
+            # repeated copies of one step are idempotent until the step writes
+            for _ in range(3):
+                pb.pa_copy_blocks(c.kc, c.vc, pairs)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                pb.pa_copy_blocks(c.kc, c.vc, pairs)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            P = st.block_mapping.shape[0]
+            nbytes = 2 * P * cfg.num_kv_heads * cfg.block_size * cfg.head_dim * 2 * 2 + 8 * P
+            c.extra["copy_blocks"] = {"pairs": P, "avg_ms": round(ms, 5), "bytes": nbytes,
+                                      "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+        if step == ps.new_tokens:
+            break
+        if pairs is not None:
+            pb.pa_copy_blocks(c.kc, c.vc, pairs)
+        pb.pa_write_kv(pb.to_device(st.k_new, et, dev), pb.to_device(st.v_new, et, dev), c.kc, c.vc,
+                       pb.int32_to_device(st.slot_mapping, dev))
+    torch.cuda.synchronize()
+    c.q = pb.to_device(st.q, et, dev)
+    c.k_new, c.v_new = pb.to_device(st.k_new, et, dev), pb.to_device(st.v_new, et, dev)
+    c.slots = pb.int32_to_device(st.slot_mapping, dev)
+    c.bt, c.cl = pb.int32_to_device(st.block_tables, dev), pb.int32_to_device(st.context_lens, dev)
+    c.copy_pairs = st.block_mapping
+    c.context_lens, c.max_len = st.context_lens, int(st.context_lens.max())
+    # each prompt's tokens once, plus every sample's own tokens
+    own = c.context_lens.astype(np.int64) - ps.prompt_len
+    unique_tokens = ps.num_prompts * ps.prompt_len + int(own.sum())
+    c.unique_kv = unique_tokens * cfg.num_kv_heads * cfg.head_dim * 2 * 2
+    c.gen_s = time.perf_counter() - t0
+    return c
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -191,20 +264,17 @@ def main() -> int:
 
     pb.load_library()
     dev = torch.device("cuda:0")
-    cfg = wl.CONFIGS[args.workload]
+    if args.workload == "parallel_sampling":
+        c = sampling_case(wl, pb, dev, torch, max(args.steps, 10))
+    else:
+        c = decode_case(wl.CONFIGS[args.workload], wl, pb, dev)
+    cfg, et = c.cfg, c.cfg.etype
     part = cfg.partition_size if args.partition is None else args.partition
-    t_gen = time.perf_counter()
-    w = wl.make_decode_workload(cfg)
-    gen_s = time.perf_counter() - t_gen
-    et = cfg.etype
-    kc, vc = pb.to_device(w.k_cache, et, dev), pb.to_device(w.v_cache, et, dev)
-    q = pb.to_device(w.q, et, dev)
-    k_new, v_new = pb.to_device(w.k_new, et, dev), pb.to_device(w.v_new, et, dev)
-    slots = pb.int32_to_device(w.slot_mapping, dev)
-    bt, cl = pb.int32_to_device(w.block_tables, dev), pb.int32_to_device(w.context_lens, dev)
-    copies = torch.empty((0, 2), dtype=torch.int32, device=dev)   # no shared blocks in this workload
+    kc, vc, q, k_new, v_new, slots, bt, cl = c.kc, c.vc, c.q, c.k_new, c.v_new, c.slots, c.bt, c.cl
+    copies = pb.int32_to_device(c.copy_pairs, dev) if c.copy_pairs.shape[0] else torch.empty(
+        (0, 2), dtype=torch.int32, device=dev)
     out = torch.empty(q.shape, dtype=torch.float32, device=dev)
-    max_len = w.max_context_len
+    max_len = c.max_len
 
     if args.calibration_copy_mib:
         n = args.calibration_copy_mib << 20
@@ -219,7 +289,7 @@ def main() -> int:
         raise SystemExit("--algo needs --two-calls (the fused call picks the kernel family itself)")
 
     def step():
-        pb.pa_copy_blocks(kc, vc, copies)   # no pairs: returns without a launch
+        pb.pa_copy_blocks(kc, vc, copies)   # this step's copy-on-write pairs (none here: no launch)
         if fused:
             pb.pa_write_decode(out, q, k_new, v_new, kc, vc, bt, cl, cfg.scale, max_len, partition_size=part)
         else:
@@ -241,8 +311,13 @@ def main() -> int:
     elapsed = time.perf_counter() - t0
     call_ms = ev0.elapsed_time(ev1) / args.steps
 
-    db = decode_bytes(w)
-    wb = write_bytes(w, fused)
+    db = decode_bytes(cfg, c.context_lens)
+    wb = write_bytes(cfg, len(c.context_lens), fused)
+    if c.unique_kv is not None:
+        # shared prompt blocks count once: the bytes HBM must deliver at least
+        db["kv_logical"] = db["kv"]
+        db["total"] += c.unique_kv - db["kv"]
+        db["kv"] = c.unique_kv
     step_bytes = db["total"] + wb
     ms_per_step = elapsed * 1e3 / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -267,27 +342,28 @@ def main() -> int:
         "data": "synthetic",
         "config": {
             "workload": WORKLOAD_TEXT[args.workload],
-            "num_seqs": cfg.num_seqs,
-            "context_tokens": int(w.context_lens.astype(np.int64).sum()),
+            "num_seqs": len(c.context_lens),
+            "context_tokens": int(c.context_lens.astype(np.int64).sum()),
             "max_context_len": max_len,
             "partition_size": part,
             "algo": args.algo,
             "step": ("copy blocks (0 pairs) + fused write 1 token/seq and decode" if fused
                      else "copy blocks (0 pairs) + write 1 token/seq + decode"),
         },
-        "sequences_per_s": round(cfg.num_seqs / (ms_per_step * 1e-3), 1),
+        "sequences_per_s": round(len(c.context_lens) / (ms_per_step * 1e-3), 1),
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "step_bytes": step_bytes,
         "decode": {"call": "pa_write_decode" if fused else "pa_write_kv + pa_decode", "bytes": db,
                    "write_bytes": wb, "launch_bytes": launch_bytes, "avg_ms": round(call_ms, 5),
-                   "GBps": round(achieved, 1), "seq_per_s": round(cfg.num_seqs / (call_ms * 1e-3), 1),
+                   "GBps": round(achieved, 1), "seq_per_s": round(len(c.context_lens) / (call_ms * 1e-3), 1),
                    "timed": "HIP events on the launch stream around the timed steps, divided by the steps"},
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
-        "input_generation_s": round(gen_s, 2),
+        "input_generation_s": round(c.gen_s, 2),
+        **c.extra,
     }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    if not args.no_cpu_baseline and c.w is not None:
+        result["cpu_baseline"] = cpu_baseline(c.w, args.cpu_budget)
     print(json.dumps(result), flush=True)
     return 0
 

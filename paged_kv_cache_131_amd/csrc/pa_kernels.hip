@@ -899,13 +899,24 @@ __device__ void run_stream(const DecodeParams& p, typename Eng::Smem& sm, Segmen
   }
 }
 
+// Workgroups are handed to the 8 XCDs (each with its own L2) in turn by
+// linear id; with W a multiple of 8 that is blockIdx.x % 8 for every KV
+// head. Numbering the persistent workers XCD-major puts neighbouring chunk
+// ranges -- the same or adjacent sequences, e.g. samples sharing a prompt's
+// blocks -- on one XCD, so blocks several of them read are fetched once into
+// that L2. The one-workgroup-per-partition mode keeps its own numbering.
+__device__ __forceinline__ int worker_index(int bx, int W, int mode) {
+  if (mode == kModeFixed || (W & 7)) return bx;
+  return (bx & 7) * (W >> 3) + (bx >> 3);
+}
+
 template <class Eng, int D>
 __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
   __shared__ typename Eng::Smem sm;
   const int lane = threadIdx.x;
   const int kvh = blockIdx.y;
-  const int w = blockIdx.x;
   const int W = gridDim.x;
+  const int w = worker_index(blockIdx.x, W, p.mode);
   SegmentSource src;
   src.mode = p.mode;
   src.w = w;
@@ -1079,7 +1090,22 @@ __device__ void merge_sequence(const DecodeParams& p, MergeSmem<W>& sm, int s, i
     sm.ls[h][k] = p.ws_ml[r + 1];
   }
   __syncthreads();
-  // weights: wave v handles heads v, v+W, ...; lanes over pieces
+  // weights: with one wave (few pieces) lane h walks head h's pieces; with
+  // W waves, wave v handles heads v, v+W, ... with its lanes over the pieces
+  if constexpr (W == 1) {
+    if (tid < nh) {
+      float M = kNegInf;
+      for (int k = 0; k < npieces; ++k) M = fmaxf(M, sm.wgt[tid][k]);
+      float den = 0.f;
+      for (int k = 0; k < npieces; ++k) {
+        const float e = fast_exp2(sm.wgt[tid][k] - M);
+        sm.wgt[tid][k] = e;
+        den = fmaf(e, sm.ls[tid][k], den);
+      }
+      const float inv = 1.f / den;
+      for (int k = 0; k < npieces; ++k) sm.wgt[tid][k] *= inv;
+    }
+  } else {
   for (int h = wave; h < nh; h += W) {
     float M = kNegInf;
     for (int k = lane; k < npieces; k += 64) M = fmaxf(M, sm.wgt[h][k]);
@@ -1095,6 +1121,7 @@ __device__ void merge_sequence(const DecodeParams& p, MergeSmem<W>& sm, int s, i
     for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
     const float inv = 1.f / den;
     for (int k = lane; k < npieces; k += 64) sm.wgt[h][k] *= inv;
+  }
   }
   __syncthreads();
   float acc[kMaxGroup][PER];
