@@ -268,6 +268,36 @@ def test_permutation_invariance_is_bit_exact(algo, part):
     assert torch.equal(again.decode(partition_size=part, algo=algo), outs[0])
 
 
+@pytest.mark.parametrize("part", [-1, 0, 32])
+def test_more_sequences_than_the_length_scan_takes(part):
+    # above 4096 sequences the automatic mode runs one workgroup per
+    # (sequence, KV head) and fixed partitions one workgroup per partition
+    cfg = wl.DecodeConfig("many-seqs", 31, 4200, 8, 2, 64, 16, "bf16", 1.0, ("uniform", 1, 80), 80)
+    say(f"4200 sequences part={part}")
+    w = wl.make_decode_workload(cfg)
+    dv = Dev(w)
+    dv.write()
+    kr, vr = host_after_write(w)
+    seqs = list(range(0, 4200, 13)) + [4199]
+    ref = oracle.decode(w.q, kr, vr, w.block_tables, w.context_lens, cfg.scale, 16, "bf16", seqs=seqs)
+    out = dv.decode(partition_size=part).cpu().numpy()
+    check(out[seqs], ref[seqs], 2e-3, f"4200 sequences part={part}")
+
+
+@pytest.mark.parametrize("part", [32, 64, -1])
+def test_long_piece_lists(part):
+    # 282 and 257 partitions of 32 tokens: more pieces than the merge stages
+    # in LDS (plain per-output loop); 141 partitions of 64: four-wave merge
+    cfg = wl.DecodeConfig("long-pieces", 32, 2, 8, 1, 128, 16, "bf16", 1.0, ("fixed", (9000, 8193)), 9000)
+    say(f"long piece lists part={part}")
+    w = wl.make_decode_workload(cfg)
+    dv = Dev(w)
+    dv.write()
+    kr, vr = host_after_write(w)
+    ref = oracle.decode(w.q, kr, vr, w.block_tables, w.context_lens, cfg.scale, 16, "bf16")
+    check(dv.decode(partition_size=part), ref, 2e-3, f"long pieces part={part}")
+
+
 # ---------------------------------------------------------------------------
 # Full-size workloads (sampled outputs + properties at full size)
 # ---------------------------------------------------------------------------
