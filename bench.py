@@ -163,10 +163,10 @@ class Case:
     """Device inputs of the timed step and what the report needs about them."""
 
 
-def decode_case(cfg, wl, pb, dev) -> Case:
+def decode_case(cfg, wl, pb, dev, contiguous=False) -> Case:
     c = Case()
     t0 = time.perf_counter()
-    w = wl.make_decode_workload(cfg)
+    w = wl.make_decode_workload(cfg, contiguous=contiguous)
     c.gen_s = time.perf_counter() - t0
     et = cfg.etype
     c.w, c.cfg = w, cfg
@@ -241,6 +241,9 @@ def main() -> int:
     ap.add_argument("--algo", default="auto", choices=["auto", "vector", "mfma"])
     ap.add_argument("--partition", type=int, default=None, help="partition size (-1 balanced, 0 none)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--block-size", type=int, default=None, help="tokens per block (default: the workload's)")
+    ap.add_argument("--contiguous", action="store_true",
+                    help="hand out the pool's blocks in order instead of the seeded shuffled order")
     ap.add_argument("--two-calls", action="store_true", help="time pa_write_kv + pa_decode instead of the fused call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -265,9 +268,15 @@ def main() -> int:
     pb.load_library()
     dev = torch.device("cuda:0")
     if args.workload == "parallel_sampling":
+        if args.block_size or args.contiguous:
+            raise SystemExit("--block-size/--contiguous apply to the single-step workloads")
         c = sampling_case(wl, pb, dev, torch, max(args.steps, 10))
     else:
-        c = decode_case(wl.CONFIGS[args.workload], wl, pb, dev)
+        import dataclasses
+        cfg0 = wl.CONFIGS[args.workload]
+        if args.block_size:
+            cfg0 = dataclasses.replace(cfg0, block_size=args.block_size)
+        c = decode_case(cfg0, wl, pb, dev, contiguous=args.contiguous)
     cfg, et = c.cfg, c.cfg.etype
     part = cfg.partition_size if args.partition is None else args.partition
     kc, vc, q, k_new, v_new, slots, bt, cl = c.kc, c.vc, c.q, c.k_new, c.v_new, c.slots, c.bt, c.cl
@@ -346,6 +355,8 @@ def main() -> int:
             "context_tokens": int(c.context_lens.astype(np.int64).sum()),
             "max_context_len": max_len,
             "partition_size": part,
+            "block_size": cfg.block_size,
+            "pool": "contiguous" if args.contiguous else "shuffled",
             "algo": args.algo,
             "step": ("copy blocks (0 pairs) + fused write 1 token/seq and decode" if fused
                      else "copy blocks (0 pairs) + write 1 token/seq + decode"),

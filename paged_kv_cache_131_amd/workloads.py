@@ -185,9 +185,11 @@ class DecodeWorkload:
 
 
 def make_decode_workload(cfg: DecodeConfig, lengths=None, poison: bool = True,
-                         values: bool = True) -> DecodeWorkload:
+                         values: bool = True, contiguous: bool = False) -> DecodeWorkload:
     """Draw one decode step's inputs. With values=False only the integer
-    inputs (lengths, block tables, slot mapping) are produced."""
+    inputs (lengths, block tables, slot mapping) are produced. contiguous=True
+    hands the pool's blocks out in order (sequence s's blocks adjacent, after
+    those of s-1) instead of in the seeded shuffled order."""
     seqs = np.random.SeedSequence(1000 + cfg.index).spawn(6)
     rng_len, rng_pool = np.random.default_rng(seqs[0]), np.random.default_rng(seqs[1])
     ss_q, ss_k, ss_v, ss_new = seqs[2:]
@@ -201,6 +203,8 @@ def make_decode_workload(cfg: DecodeConfig, lengths=None, poison: bool = True,
     if num_blocks <= need:
         raise ValueError("pool too small to leave a spare block for poisoned padding")
     perm = rng_pool.permutation(num_blocks).astype(np.int32)
+    if contiguous:
+        perm = np.arange(num_blocks, dtype=np.int32)
     max_blocks = max(-(-cfg.max_len // B), int(nblk.max()))
     poison_block = int(perm[need])             # first block never handed out
     tables = np.full((cfg.num_seqs, max_blocks), poison_block, dtype=np.int32)
