@@ -52,9 +52,9 @@ typedef enum pa_status {
   PA_ERR_LAUNCH = -4        /* the HIP runtime reported an error at launch */
 } pa_status;
 
-/* Decode kernel family. AUTO picks MFMA for 16-bit elements when
- * num_heads / num_kv_heads >= 3 (grouped query heads make QK and PV a dense
- * contraction), the vector kernel otherwise. */
+/* Decode kernel family. AUTO picks MFMA for 16-bit elements (at every group
+ * size, MHA included: it measured fastest on MI355X) and the vector kernel
+ * for fp32 elements. */
 typedef enum pa_algo { PA_ALGO_AUTO = 0, PA_ALGO_VECTOR = 1, PA_ALGO_MFMA = 2 } pa_algo;
 
 /* partition_size values for pa_decode besides a positive multiple of 32:

@@ -217,7 +217,8 @@ static pa_status decode_impl(void* out, const void* q, const void* k_new, const 
   } else if (algo == PA_ALGO_VECTOR) {
     kernel_algo = pa::kAlgoVector;
   } else {
-    kernel_algo = (dtype != PA_F32 && group >= 3) ? pa::kAlgoMfma : pa::kAlgoVector;
+    // measured on MI355X: the MFMA engine leads at every group size, MHA included
+    kernel_algo = dtype != PA_F32 ? pa::kAlgoMfma : pa::kAlgoVector;
   }
   const int G = kernel_algo == pa::kAlgoMfma ? 0 : (group <= 1 ? 1 : group <= 2 ? 2 : group <= 4 ? 4 : 8);
 
