@@ -37,6 +37,11 @@ WORKLOAD_TEXT = {
     "parallel_sampling": "parallel sampling, last of 256 decode steps: 32 prompts of 1016 tokens x 8 samples "
                          "sharing the prompt blocks (copy-on-write at divergence), 32 q / 8 kv heads, head_dim 128, "
                          "block 16, bf16",
+    "beam_search": "beam search, last of 64 decode steps: 32 prompts of 1000 tokens x 4 beams, beams re-selected "
+                   "every step (fork / release, copy-on-write of shared last blocks), 32 q / 8 kv heads, head_dim "
+                   "128, block 16, bf16",
+    "shared_prefix": "shared prefix: 256 requests mapping one 1024-token prompt prefix plus own suffixes of U[16, 512] "
+                     "tokens, 32 q / 8 kv heads, head_dim 128, block 16, bf16",
 }
 
 
@@ -163,10 +168,24 @@ class Case:
     """Device inputs of the timed step and what the report needs about them."""
 
 
-def decode_case(cfg, wl, pb, dev, contiguous=False) -> Case:
+def unique_kv_bytes(c, tables, lens) -> int:
+    """K and V bytes of the distinct blocks the step reads (a block several
+    sequences map counts once, with the most tokens any of them reads)."""
+    es = {"f32": 4, "f16": 2, "bf16": 2}[c.etype]
+    B = c.block_size
+    reads = {}
+    for s, L in enumerate(lens.tolist()):
+        for b in range(-(-L // B)):
+            blk = int(tables[s, b])
+            reads[blk] = max(reads.get(blk, 0), min(B, L - b * B))
+    return sum(reads.values()) * c.num_kv_heads * c.head_dim * 2 * es
+
+
+def decode_case(cfg, wl, pb, dev, contiguous=False, shared_prefix=False) -> Case:
     c = Case()
     t0 = time.perf_counter()
-    w = wl.make_decode_workload(cfg, contiguous=contiguous)
+    w = wl.make_shared_prefix_workload() if shared_prefix else wl.make_decode_workload(cfg, contiguous=contiguous)
+    cfg = w.cfg
     c.gen_s = time.perf_counter() - t0
     et = cfg.etype
     c.w, c.cfg = w, cfg
@@ -177,23 +196,23 @@ def decode_case(cfg, wl, pb, dev, contiguous=False) -> Case:
     c.bt, c.cl = pb.int32_to_device(w.block_tables, dev), pb.int32_to_device(w.context_lens, dev)
     c.copy_pairs = np.zeros((0, 2), np.int32)  # no shared blocks in this workload
     c.context_lens, c.max_len = w.context_lens, w.max_context_len
-    c.unique_kv = None
+    c.unique_kv = unique_kv_bytes(cfg, w.block_tables, w.context_lens)
     c.extra = {}
     return c
 
 
-def sampling_case(wl, pb, dev, torch, reps: int) -> Case:
-    """Runs steps 1..255 of the parallel-sampling workload on the device
-    (copies + writes, as a serving loop would) and returns step 256; the
-    copy-on-write call of the divergence step is timed on the way."""
+def loop_case(ps, nsteps: int, pb, dev, torch, reps: int) -> Case:
+    """Runs steps 1..nsteps-1 of a multi-step workload (parallel sampling,
+    beam search) on the device -- copies, then writes, as a serving loop
+    would -- and returns step nsteps; the copy-on-write call of step 1 is
+    timed on the way."""
     c = Case()
     t0 = time.perf_counter()
-    ps = wl.ParallelSamplingWorkload(prompt_len=1016)
     cfg, et = ps.cfg, ps.cfg.etype
     c.cfg, c.w = cfg, None
     c.kc, c.vc = pb.to_device(ps.k_cache, et, dev), pb.to_device(ps.v_cache, et, dev)
     c.extra = {}
-    for step in range(1, ps.new_tokens + 1):
+    for step in range(1, nsteps + 1):
         st = ps.step()
         pairs = pb.int32_to_device(st.block_mapping, dev) if st.block_mapping.shape[0] else None
         if step == 1 and pairs is not None:
@@ -211,7 +230,7 @@ def sampling_case(wl, pb, dev, torch, reps: int) -> Case:
             nbytes = 2 * P * cfg.num_kv_heads * cfg.block_size * cfg.head_dim * 2 * 2 + 8 * P
             c.extra["copy_blocks"] = {"pairs": P, "avg_ms": round(ms, 5), "bytes": nbytes,
                                       "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
-        if step == ps.new_tokens:
+        if step == nsteps:
             break
         if pairs is not None:
             pb.pa_copy_blocks(c.kc, c.vc, pairs)
@@ -224,10 +243,8 @@ def sampling_case(wl, pb, dev, torch, reps: int) -> Case:
     c.bt, c.cl = pb.int32_to_device(st.block_tables, dev), pb.int32_to_device(st.context_lens, dev)
     c.copy_pairs = st.block_mapping
     c.context_lens, c.max_len = st.context_lens, int(st.context_lens.max())
-    # each prompt's tokens once, plus every sample's own tokens
-    own = c.context_lens.astype(np.int64) - ps.prompt_len
-    unique_tokens = ps.num_prompts * ps.prompt_len + int(own.sum())
-    c.unique_kv = unique_tokens * cfg.num_kv_heads * cfg.head_dim * 2 * 2
+    c.unique_kv = unique_kv_bytes(cfg, st.block_tables, st.context_lens)
+    c.extra["copy_pairs_timed_step"] = int(st.block_mapping.shape[0])
     c.gen_s = time.perf_counter() - t0
     return c
 
@@ -267,10 +284,14 @@ def main() -> int:
 
     pb.load_library()
     dev = torch.device("cuda:0")
+    if args.workload in ("parallel_sampling", "beam_search", "shared_prefix") and (args.block_size or args.contiguous):
+        raise SystemExit("--block-size/--contiguous apply to the drawn-length workloads")
     if args.workload == "parallel_sampling":
-        if args.block_size or args.contiguous:
-            raise SystemExit("--block-size/--contiguous apply to the single-step workloads")
-        c = sampling_case(wl, pb, dev, torch, max(args.steps, 10))
+        c = loop_case(wl.ParallelSamplingWorkload(prompt_len=1016), 256, pb, dev, torch, max(args.steps, 10))
+    elif args.workload == "beam_search":
+        c = loop_case(wl.BeamSearchWorkload(), 64, pb, dev, torch, max(args.steps, 10))
+    elif args.workload == "shared_prefix":
+        c = decode_case(None, wl, pb, dev, shared_prefix=True)
     else:
         import dataclasses
         cfg0 = wl.CONFIGS[args.workload]
@@ -322,8 +343,8 @@ def main() -> int:
 
     db = decode_bytes(cfg, c.context_lens)
     wb = write_bytes(cfg, len(c.context_lens), fused)
-    if c.unique_kv is not None:
-        # shared prompt blocks count once: the bytes HBM must deliver at least
+    if c.unique_kv != db["kv"]:
+        # shared blocks count once: the bytes HBM must deliver at least
         db["kv_logical"] = db["kv"]
         db["total"] += c.unique_kv - db["kv"]
         db["kv"] = c.unique_kv

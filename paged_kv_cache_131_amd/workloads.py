@@ -357,3 +357,169 @@ class ParallelSamplingWorkload:
 
     def unique_blocks(self) -> int:
         return self.num_blocks - self.bm.num_free
+
+
+BEAM_SEARCH = DecodeConfig("beam_search", 5, 128, 32, 8, 128, 16, "bf16", 1.0, ("fixed", ()), 1000 + 64)
+
+
+class BeamSearchWorkload:
+    """Beam search over a paged cache: every request's prompt is prefilled
+    once and forked into `beams` beams that share its blocks. Each step first
+    re-selects the beams (from the second step on): new beam j continues a
+    seeded choice of current beam, so some beams end (their blocks are
+    released) and others split (forks share every block). Then one token is
+    appended per beam, with copy-on-write of a shared, partly filled last
+    block. Stream 0 of the seed draws the beam choices (no lengths here)."""
+
+    def __init__(self, prompt_len: int = 1000, num_requests: int = 32, beams: int = 4, steps: int = 64,
+                 cfg: DecodeConfig = BEAM_SEARCH, poison: bool = True, values: bool = True):
+        self.cfg = cfg
+        self.prompt_len, self.num_requests, self.beams, self.steps = prompt_len, num_requests, beams, steps
+        self.values = values
+        seqs = np.random.SeedSequence(1000 + cfg.index).spawn(6)
+        self.rng_beam = np.random.default_rng(seqs[0])
+        rng_pool = np.random.default_rng(seqs[1])
+        self.ss_q, self.ss_new = seqs[2], seqs[5]
+        B = cfg.block_size
+        # every beam distinct at the end bounds what is ever held at once
+        per_beam = -(-(prompt_len + steps) // B)
+        self.num_blocks = math.ceil(1.1 * num_requests * beams * per_beam)
+        perm = rng_pool.permutation(self.num_blocks)
+        self.bm = BlockManager(self.num_blocks, B, free_order=perm)
+        self.max_blocks = per_beam
+        Hkv, d = cfg.num_kv_heads, cfg.head_dim
+        self.k_cache = self.v_cache = None
+        if values:
+            self.k_cache = random_stored(seqs[3], (self.num_blocks, Hkv, B, d), cfg.etype, cfg.value_scale)
+            self.v_cache = random_stored(seqs[4], (self.num_blocks, Hkv, d, B), cfg.etype, cfg.value_scale)
+        self.groups = []
+        prompt_blocks = []
+        for _ in range(num_requests):
+            parent = self.bm.new_sequence()
+            for _ in range(prompt_len):
+                self.bm.append_token(parent)
+            prompt_blocks.extend(parent.block_table)
+            self.groups.append([parent] + [self.bm.fork(parent) for _ in range(beams - 1)])
+        self.poison_block = int(self.bm.free[-1])
+        if poison and values:
+            pv = poison_value(cfg.etype)
+            held = np.zeros(self.num_blocks, dtype=bool)
+            held[prompt_blocks] = True
+            self.k_cache[~held] = pv
+            self.v_cache[~held] = pv
+            tail = prompt_len % B
+            if tail:
+                for g in self.groups:
+                    last = g[0].block_table[-1]
+                    self.k_cache[last, :, tail:, :] = pv
+                    self.v_cache[last, :, :, tail:] = pv
+        self.step_index = 0
+
+    @property
+    def num_seqs(self):
+        return self.num_requests * self.beams
+
+    def reselect(self) -> None:
+        K = self.beams
+        for r, cur in enumerate(self.groups):
+            parents = np.sort(self.rng_beam.integers(0, K, size=K))
+            new = [self.bm.fork(cur[int(pj)]) for pj in parents]
+            for b in cur:
+                self.bm.free_sequence(b)
+            self.groups[r] = new
+
+    def step(self) -> SamplingStep:
+        if self.step_index >= self.steps:
+            raise StopIteration
+        if self.step_index > 0:
+            self.reselect()
+        self.step_index += 1
+        cfg = self.cfg
+        slots, pairs = [], []
+        seqs = [b for g in self.groups for b in g]
+        for seq in seqs:
+            slot, copy = self.bm.append_token(seq)
+            slots.append(slot)
+            if copy is not None:
+                pairs.append(copy)
+        S, Hkv, d = self.num_seqs, cfg.num_kv_heads, cfg.head_dim
+        q = k_new = v_new = None
+        if self.values:
+            q_ss = self.ss_q.spawn(1)[0]
+            kn_ss, vn_ss = self.ss_new.spawn(1)[0].spawn(2)
+            q = random_stored(q_ss, (S, cfg.num_heads, d), cfg.etype, cfg.value_scale)
+            k_new = random_stored(kn_ss, (S, Hkv, d), cfg.etype, cfg.value_scale)
+            v_new = random_stored(vn_ss, (S, Hkv, d), cfg.etype, cfg.value_scale)
+        tables = np.full((S, self.max_blocks), self.poison_block, dtype=np.int32)
+        for i, seq in enumerate(seqs):
+            tables[i, :len(seq.block_table)] = seq.block_table
+        lens = np.array([seq.num_tokens for seq in seqs], dtype=np.int32)
+        mapping = np.array(pairs, dtype=np.int32).reshape(-1, 2)
+        return SamplingStep(self.step_index, mapping, np.array(slots, dtype=np.int32),
+                            k_new, v_new, q, tables, lens)
+
+    def blocks_in_use(self) -> int:
+        return self.num_blocks - self.bm.num_free
+
+
+SHARED_PREFIX = DecodeConfig("shared_prefix", 6, 256, 32, 8, 128, 16, "bf16", 1.0, ("uniform", 16, 512),
+                             1024 + 512)
+
+
+def make_shared_prefix_workload(prefix_len: int = 1024, cfg: DecodeConfig = SHARED_PREFIX, poison: bool = True,
+                                values: bool = True) -> DecodeWorkload:
+    """One decode step of requests that all map the same prompt prefix (a
+    shared system prompt): the prefix is prefilled once and its blocks are
+    mapped into every request (forks, reference counts raised); each request
+    then holds its own suffix of a drawn length, whose last token is the new
+    one. A block-aligned prefix needs no copy."""
+    seqs = np.random.SeedSequence(1000 + cfg.index).spawn(6)
+    rng_len, rng_pool = np.random.default_rng(seqs[0]), np.random.default_rng(seqs[1])
+    suffix = draw_lengths(cfg, rng_len)
+    B = cfg.block_size
+    lens = (prefix_len + suffix).astype(np.int32)
+    prefix_blocks = -(-prefix_len // B)
+    own = -(-(lens.astype(np.int64) - (prefix_len // B) * B) // B)
+    need = prefix_blocks + int(own.sum())
+    num_blocks = math.ceil(1.1 * need)
+    perm = rng_pool.permutation(num_blocks)
+    bm = BlockManager(num_blocks, B, free_order=perm)
+    root = bm.new_sequence()
+    for _ in range(prefix_len):
+        bm.append_token(root)
+    max_blocks = -(-int(lens.max()) // B)
+    poison_block = int(bm.free[-1])
+    tables = np.full((cfg.num_seqs, max_blocks), poison_block, dtype=np.int32)
+    slots = np.empty(cfg.num_seqs, dtype=np.int32)
+    copies = 0
+    for s in range(cfg.num_seqs):
+        seq = bm.fork(root)
+        for _ in range(int(suffix[s])):
+            slot, copy = bm.append_token(seq)
+            copies += copy is not None
+        tables[s, :len(seq.block_table)] = seq.block_table
+        slots[s] = slot
+    if copies and prefix_len % B == 0:
+        raise AssertionError("a block-aligned prefix must not be copied")
+    used = np.array(sorted(set(tables[tables != poison_block].tolist())), dtype=np.int64)
+    if not values:
+        return DecodeWorkload(cfg, None, None, None, tables, lens, None, None, slots, num_blocks, poison_block, used)
+    Hkv, d = cfg.num_kv_heads, cfg.head_dim
+    q = random_stored(seqs[2], (cfg.num_seqs, cfg.num_heads, d), cfg.etype, cfg.value_scale)
+    k_cache = random_stored(seqs[3], (num_blocks, Hkv, B, d), cfg.etype, cfg.value_scale)
+    v_cache = random_stored(seqs[4], (num_blocks, Hkv, d, B), cfg.etype, cfg.value_scale)
+    kn_ss, vn_ss = seqs[5].spawn(2)
+    k_new = random_stored(kn_ss, (cfg.num_seqs, Hkv, d), cfg.etype, cfg.value_scale)
+    v_new = random_stored(vn_ss, (cfg.num_seqs, Hkv, d), cfg.etype, cfg.value_scale)
+    if poison:
+        pv = poison_value(cfg.etype)
+        held = np.zeros(num_blocks, dtype=bool)
+        held[used] = True
+        k_cache[~held] = pv
+        v_cache[~held] = pv
+        for s in range(cfg.num_seqs):
+            last = tables[s, (int(lens[s]) - 1) // B]
+            off = (int(lens[s]) - 1) % B          # the new token's slot and the rest
+            k_cache[last, :, off:, :] = pv
+            v_cache[last, :, :, off:] = pv
+    return DecodeWorkload(cfg, q, k_cache, v_cache, tables, lens, k_new, v_new, slots, num_blocks, poison_block, used)

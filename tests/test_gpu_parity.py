@@ -409,3 +409,56 @@ def test_parallel_sampling_steps(prompt):
     still_shared = [b for b in prompt_blocks if ps.bm.refcount[b] == ps.samples]
     idx = [prompt_blocks.index(b) for b in still_shared]
     np.testing.assert_array_equal(pb.to_host(kc, "bf16")[still_shared], initial_prompt_k[idx])
+
+
+def test_beam_search_steps():
+    # beams re-selected every step (ended beams release their blocks, split
+    # beams share them), then copy-on-write pairs and the fused write+decode
+    say("beam search")
+    bs = wl.BeamSearchWorkload(steps=40)
+    cfg = bs.cfg
+    kc = pb.to_device(bs.k_cache, "bf16", DEV)
+    vc = pb.to_device(bs.v_cache, "bf16", DEV)
+    hk, hv = bs.k_cache.copy(), bs.v_cache.copy()
+    copies = 0
+    for step in range(1, 41):
+        st = bs.step()
+        if st.block_mapping.shape[0]:
+            copies += st.block_mapping.shape[0]
+            pb.pa_copy_blocks(kc, vc, pb.int32_to_device(st.block_mapping, DEV))
+            oracle.copy_blocks(hk, hv, st.block_mapping, inplace=True)
+        oracle.write_kv(hk, hv, st.k_new, st.v_new, st.slot_mapping, 16, inplace=True)
+        out = torch.empty(st.q.shape, dtype=torch.float32, device=DEV)
+        pb.pa_write_decode(out, pb.to_device(st.q, "bf16", DEV), pb.to_device(st.k_new, "bf16", DEV),
+                           pb.to_device(st.v_new, "bf16", DEV), kc, vc, pb.int32_to_device(st.block_tables, DEV),
+                           pb.int32_to_device(st.context_lens, DEV), cfg.scale, int(st.context_lens.max()))
+        if step in (1, 2, 9, 40):
+            torch.cuda.synchronize()
+            seqs = list(range(0, bs.num_seqs, 7)) + [bs.num_seqs - 1]
+            ref = oracle.decode(st.q, hk, hv, st.block_tables, st.context_lens, cfg.scale, 16, "bf16", seqs=seqs)
+            check(out, ref, 2e-3, f"beam search step={step}")
+    torch.cuda.synchronize()
+    say(f"  {copies} block copies over 40 steps")
+    # the whole pool, released blocks included, holds exactly the oracle's bytes
+    np.testing.assert_array_equal(pb.to_host(kc, "bf16"), hk)
+    np.testing.assert_array_equal(pb.to_host(vc, "bf16"), hv)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_shared_prefix(fused):
+    w = wl.make_shared_prefix_workload()
+    say(f"shared prefix fused={fused}")
+    dv = Dev(w)
+    kr, vr = host_after_write(w)
+    seqs = list(range(0, w.cfg.num_seqs, 11)) + [w.cfg.num_seqs - 1]
+    ref = oracle.decode(w.q, kr, vr, w.block_tables, w.context_lens, w.cfg.scale, 16, "bf16", seqs=seqs)
+    if fused:
+        out = torch.empty(dv.q.shape, dtype=torch.float32, device=DEV)
+        pb.pa_write_decode(out, dv.q, dv.k_new, dv.v_new, dv.kc, dv.vc, dv.bt, dv.cl, w.cfg.scale, w.max_context_len)
+    else:
+        dv.write()
+        out = dv.decode()
+    check(out.cpu().numpy()[seqs], ref[seqs], 2e-3, f"shared prefix fused={fused}")
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(pb.to_host(dv.kc, "bf16"), kr)
+    np.testing.assert_array_equal(pb.to_host(dv.vc, "bf16"), vr)

@@ -132,3 +132,47 @@ def test_bf16_rounding_matches_torch():
     np.testing.assert_array_equal(ours, theirs)
     f16 = wl.round_to(x[:1000], "f16")
     np.testing.assert_array_equal(f16, torch.from_numpy(x[:1000]).to(torch.float16).numpy())
+
+
+def test_beam_search_workload_invariants():
+    # every step: copies go to fresh, distinct blocks that are not sources;
+    # reference counts equal the number of beams mapping each block; no block
+    # leaks; after the step every beam's last block is its own (the fused
+    # write's precondition); each new token's slot is position L-1
+    bs = wl.BeamSearchWorkload(values=False)
+    total = 0
+    for i in range(bs.steps):
+        st = bs.step()
+        m = st.block_mapping
+        total += m.shape[0]
+        if m.shape[0]:
+            assert len(set(m[:, 1].tolist())) == m.shape[0]
+            assert not set(m[:, 1].tolist()) & set(m[:, 0].tolist())
+        rc = np.zeros(bs.num_blocks, dtype=np.int64)
+        for g in bs.groups:
+            for b in g:
+                for blk in b.block_table:
+                    rc[blk] += 1
+        assert rc.tolist() == bs.bm.refcount
+        assert bs.bm.num_free == int((rc == 0).sum())
+        B = bs.cfg.block_size
+        for s, L in enumerate(st.context_lens):
+            last = st.block_tables[s, (L - 1) // B]
+            assert bs.bm.refcount[last] == 1
+            assert st.slot_mapping[s] == last * B + (L - 1) % B
+    assert total > 0 and bs.step_index == bs.steps
+
+
+def test_shared_prefix_workload_maps_one_prefix():
+    w = wl.make_shared_prefix_workload(values=False)
+    B = w.cfg.block_size
+    prefix_blocks = 1024 // B
+    first = w.block_tables[0, :prefix_blocks]
+    assert (w.block_tables[:, :prefix_blocks] == first).all()
+    own = w.block_tables[:, prefix_blocks:]
+    mapped = [own[s, :-(-(int(L) - 1024) // B)] for s, L in enumerate(w.context_lens)]
+    flat = np.concatenate(mapped)
+    assert len(set(flat.tolist())) == flat.size and not set(flat.tolist()) & set(first.tolist())
+    last = w.block_tables[np.arange(len(w.context_lens)), (w.context_lens - 1) // B]
+    assert (w.slot_mapping == last * B + (w.context_lens - 1) % B).all()
+    assert ((w.context_lens >= 1024 + 16) & (w.context_lens <= 1024 + 512)).all()
