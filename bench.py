@@ -249,6 +249,51 @@ def loop_case(ps, nsteps: int, pb, dev, torch, reps: int) -> Case:
     return c
 
 
+def swap_sweep(torch, pb, total_mib: int, reps: int) -> dict:
+    """pa_swap_out / pa_swap_in of a shuffled set of blocks totalling
+    total_mib MiB (K + V) per block size, Llama-3-8B head shape (8 KV heads,
+    head_dim 128, bf16), against one contiguous device <-> pinned-host copy of
+    the same size (the link's rate)."""
+    dev = torch.device("cuda:0")
+    res = {}
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    nbytes = total_mib << 20
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    host = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    d2h = timed(lambda: host.copy_(src, non_blocking=True))
+    h2d = timed(lambda: src.copy_(host, non_blocking=True))
+    res["contiguous_copy"] = {"bytes": nbytes, "d2h_GBps": round(nbytes / d2h / 1e6, 1),
+                              "h2d_GBps": round(nbytes / h2d / 1e6, 1)}
+    del src, host
+    rng = np.random.default_rng(0)
+    for B in (8, 16, 32, 64, 128):
+        block_bytes = 2 * 8 * B * 128 * 2
+        n = nbytes // block_bytes
+        kc = torch.empty((n, 8, B, 128), dtype=torch.bfloat16, device=dev)
+        vc = torch.empty((n, 8, 128, B), dtype=torch.bfloat16, device=dev)
+        space = pb.swap_space(n, kc)
+        pairs = np.stack([rng.permutation(n), np.arange(n)], axis=1).astype(np.int32)
+        m = pb.int32_to_device(pairs, dev)
+        t_out = timed(lambda: pb.pa_swap_out(space, kc, vc, m))
+        t_in = timed(lambda: pb.pa_swap_in(kc, vc, space, m))
+        res[f"B{B}"] = {"blocks": int(n), "block_bytes": block_bytes,
+                        "out_ms": round(t_out, 4), "out_GBps": round(n * block_bytes / t_out / 1e6, 1),
+                        "in_ms": round(t_in, 4), "in_GBps": round(n * block_bytes / t_in / 1e6, 1)}
+        del kc, vc, space
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -265,6 +310,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run one plain device copy of this size first (traffic counter calibration)")
+    ap.add_argument("--swap-sweep", type=int, default=0, metavar="MIB",
+                    help="measure pa_swap_out/pa_swap_in of MIB MiB of blocks per block size and exit")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic file from two rocprofv3 counter_collection.csv files and exit")
     args = ap.parse_args()
@@ -284,6 +331,9 @@ def main() -> int:
 
     pb.load_library()
     dev = torch.device("cuda:0")
+    if args.swap_sweep:
+        print(json.dumps({"swap_sweep": swap_sweep(torch, pb, args.swap_sweep, 5)}), flush=True)
+        return 0
     if args.workload in ("parallel_sampling", "beam_search", "shared_prefix") and (args.block_size or args.contiguous):
         raise SystemExit("--block-size/--contiguous apply to the drawn-length workloads")
     if args.workload == "parallel_sampling":

@@ -184,6 +184,35 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapp
                          int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
                          int32_t block_size, int32_t num_blocks, pa_dtype dtype, void* stream);
 
+/*
+ * pa_swap_out / pa_swap_in -- move whole blocks between the device pool and a
+ * swap space in host memory, for preemption by swapping ([notes-zh] §7.4: the
+ * blocks of an evicted group go to CPU RAM, a CPU block allocator tracks
+ * them, and they are brought back into GPU blocks when the group resumes;
+ * [notes-zh] §7.5: small blocks mean many small transfers). One launch moves
+ * every pair; the kernel reads and writes host memory directly.
+ *   host: pinned host memory from hipHostMalloc (torch pin_memory), mapped for
+ *     the device, holding host_slots slots; slot j is the block's K image
+ *     (num_kv_heads*block_size*head_dim elements of dtype, the pool's own
+ *     per-block layout) followed by its V image. The call checks that host is
+ *     such memory and that the allocation holds host_slots slots from host on;
+ *     otherwise PA_ERR_INVALID_ARG.
+ *   block_mapping: device [num_pairs][2] int32 (device block, host slot).
+ *     swap_out: host slot <- device block; swap_in: device block <- host slot.
+ *     Bit-exact. Pairs with a block outside [0, num_blocks) or a slot outside
+ *     [0, host_slots) are skipped. Preconditions: the written side (slots for
+ *     swap_out, blocks for swap_in) is distinct within one call. The host data
+ *     is complete when the stream reaches the end of the call.
+ */
+pa_status pa_swap_out(void* host, int32_t host_slots, const void* k_cache, const void* v_cache,
+                      const int32_t* block_mapping, int32_t num_pairs, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int32_t num_blocks, pa_dtype dtype,
+                      void* stream);
+pa_status pa_swap_in(void* k_cache, void* v_cache, const void* host, int32_t host_slots,
+                     const int32_t* block_mapping, int32_t num_pairs, int32_t num_kv_heads,
+                     int32_t head_dim, int32_t block_size, int32_t num_blocks, pa_dtype dtype,
+                     void* stream);
+
 /* Static, human-readable name of a status. */
 const char* pa_status_string(pa_status status);
 

@@ -15,6 +15,8 @@ from .paged_attention import (  # noqa: F401
     decode_partitioned,
     decode_probabilities,
     gather_sequence,
+    swap_in,
+    swap_out,
     to_float64,
     write_kv,
 )

@@ -1,5 +1,6 @@
 """Plain, slow, float64 reference for paged decode attention, the slot-mapped KV
-write and the copy-on-write block copy.
+write, the copy-on-write block copy and the swap of whole blocks to and from
+host memory.
 
 TEST INFRASTRUCTURE ONLY: imported by tests/, __graft_entry__.smoke() and the
 cpu_baseline leg of bench.py. The library never calls it.
@@ -97,6 +98,35 @@ def copy_blocks(k_cache, v_cache, block_mapping, inplace=False):
     for src, dst in np.asarray(block_mapping).reshape(-1, 2).tolist():
         k_out[dst] = k_out[src]
         v_out[dst] = v_out[src]
+    return k_out, v_out
+
+
+def swap_out(k_cache, v_cache, host, block_mapping, inplace=False):
+    """Swapping out ([notes-zh] §7.4: the blocks of an evicted sequence group
+    are copied to CPU RAM, into slots a CPU block allocator hands out). For
+    each (device block, host slot) pair, in list order, host slot j receives
+    the block's whole K tile, every KV head, then its whole V tile, each
+    flattened in the pool's own element order: host is
+    [slots][2][num_kv_heads * block_size * head_dim]. Returns the new swap
+    space (the given one when inplace=True)."""
+    out = host if inplace else np.array(host, copy=True)
+    for blk, slot in np.asarray(block_mapping).reshape(-1, 2).tolist():
+        out[slot, 0] = k_cache[blk].reshape(-1)
+        out[slot, 1] = v_cache[blk].reshape(-1)
+    return out
+
+
+def swap_in(k_cache, v_cache, host, block_mapping, inplace=False):
+    """Swapping in ([notes-zh] §7.4: a resumed group's blocks are loaded back
+    into GPU blocks, not necessarily the ones they left). For each (device
+    block, host slot) pair, in list order, the block's K and V tiles are
+    restored from the slot's two images. Returns new pools (the given ones
+    when inplace=True)."""
+    k_out = k_cache if inplace else np.array(k_cache, copy=True)
+    v_out = v_cache if inplace else np.array(v_cache, copy=True)
+    for blk, slot in np.asarray(block_mapping).reshape(-1, 2).tolist():
+        k_out[blk] = host[slot, 0].reshape(k_out.shape[1:])
+        v_out[blk] = host[slot, 1].reshape(v_out.shape[1:])
     return k_out, v_out
 
 

@@ -35,6 +35,8 @@ SIGNATURES = {
                                _i32, _p, _sz, _i32, _i32, _p]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_copy_blocks": (_i32, [_p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p]),
+    "pa_swap_out": (_i32, [_p, _i32, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p]),
+    "pa_swap_in": (_i32, [_p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p]),
     "pa_status_string": (ctypes.c_char_p, [_i32]),
     "pa_abi_version": (_i32, []),
 }
@@ -214,3 +216,45 @@ def pa_write_decode(out, q, k_new, v_new, k_cache, v_cache, block_tables, contex
         S, Hq, Hkv, d, B, NB, block_tables.shape[1], int(max_context_len), float(scale), int(partition_size),
         ws_ptr, ws_bytes, DTYPE_CODE[dt], DTYPE_CODE[out.dtype], _stream(stream))
     _check("pa_write_decode", status)
+
+
+def swap_space(num_slots: int, k_cache) -> torch.Tensor:
+    """Pinned host swap space for whole blocks of this pool: [slots][2][block
+    elements] (K image, V image) of the pool's element type."""
+    NB, Hkv, B, d = k_cache.shape
+    return torch.empty((num_slots, 2, Hkv * B * d), dtype=k_cache.dtype, pin_memory=True)
+
+
+def _swap_args(host, k_cache, v_cache, block_mapping):
+    NB, Hkv, B, d = k_cache.shape
+    if v_cache.shape != (NB, Hkv, d, B):
+        raise ValueError("inconsistent shapes")
+    if not isinstance(host, torch.Tensor) or host.is_cuda or not host.is_pinned() or not host.is_contiguous():
+        raise TypeError("host must be a contiguous pinned CPU tensor")
+    if host.dim() != 3 or host.shape[1:] != (2, Hkv * B * d) or host.dtype != k_cache.dtype:
+        raise ValueError("host must be [slots][2][num_kv_heads*block_size*head_dim] of the pool's dtype")
+    P = block_mapping.shape[0] if block_mapping.numel() else 0
+    if block_mapping.numel() and tuple(block_mapping.shape) != (P, 2):
+        raise ValueError("block_mapping must be [num_pairs][2]")
+    ptr = _dev(block_mapping, "block_mapping", torch.int32) if P else None
+    return host.shape[0], ptr, P, Hkv, d, B, NB
+
+
+def pa_swap_out(host, k_cache, v_cache, block_mapping, stream=None) -> None:
+    """block_mapping [P][2] int32 (device block, host slot): host slot <- block."""
+    lib = load_library()
+    slots, ptr, P, Hkv, d, B, NB = _swap_args(host, k_cache, v_cache, block_mapping)
+    dt = k_cache.dtype
+    _check("pa_swap_out", lib.pa_swap_out(host.data_ptr(), slots, _dev(k_cache, "k_cache", dt),
+                                          _dev(v_cache, "v_cache", dt), ptr, P, Hkv, d, B, NB, DTYPE_CODE[dt],
+                                          _stream(stream)))
+
+
+def pa_swap_in(k_cache, v_cache, host, block_mapping, stream=None) -> None:
+    """block_mapping [P][2] int32 (device block, host slot): block <- host slot."""
+    lib = load_library()
+    slots, ptr, P, Hkv, d, B, NB = _swap_args(host, k_cache, v_cache, block_mapping)
+    dt = k_cache.dtype
+    _check("pa_swap_in", lib.pa_swap_in(_dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
+                                        host.data_ptr(), slots, ptr, P, Hkv, d, B, NB, DTYPE_CODE[dt],
+                                        _stream(stream)))

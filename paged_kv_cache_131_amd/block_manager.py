@@ -13,7 +13,10 @@ mappings and copy lists); it never touches K/V values.
     the old count and writes the copy, while the last sharer writes in place
     ("PagedAttention 论文精读笔记", §6.1);
   * blocks return to the free pool when their count reaches zero (same page,
-    §5.1 and §6.2).
+    §5.1 and §6.2);
+  * swapping: an evicted group's blocks move to slots of a host swap space
+    handed out by a CPU block allocator and come back into fresh GPU blocks
+    when the group resumes, all or nothing per group (same page, §7.3-§7.4).
 """
 
 from __future__ import annotations
@@ -28,8 +31,26 @@ class PoolExhausted(RuntimeError):
 
 @dataclass
 class Sequence:
-    block_table: list = field(default_factory=list)
+    block_table: list = field(default_factory=list)   # GPU blocks, or host slots while swapped out
     num_tokens: int = 0
+    swapped: bool = False
+
+
+class SwapSpace:
+    """CPU block allocator: slots of a host swap space, each holding one
+    block, with the number of sequence references the block had on the GPU
+    (restored on swap-in)."""
+
+    def __init__(self, num_slots: int):
+        if num_slots < 1:
+            raise ValueError("num_slots must be positive")
+        self.num_slots = num_slots
+        self.free = deque(range(num_slots))
+        self.refs = [0] * num_slots
+
+    @property
+    def num_free(self) -> int:
+        return len(self.free)
 
 
 class BlockManager:
@@ -103,3 +124,63 @@ class BlockManager:
     def slot_of(self, seq: Sequence, token_index: int) -> int:
         blk = seq.block_table[token_index // self.block_size]
         return blk * self.block_size + token_index % self.block_size
+
+    # -- swapping -----------------------------------------------------------
+    def swap_out(self, seqs, space: SwapSpace):
+        """Evict a group of sequences: each distinct block the group maps goes
+        to one host slot (in order of first appearance). The group must hold
+        every reference to its blocks. Returns the (gpu block, host slot)
+        pairs to copy out before the blocks are reused."""
+        slot_of, pairs = {}, []
+        refs = {}
+        for seq in seqs:
+            if seq.swapped:
+                raise ValueError("sequence already swapped out")
+            for blk in seq.block_table:
+                refs[blk] = refs.get(blk, 0) + 1
+        for blk, n in refs.items():
+            if self.refcount[blk] != n:
+                raise ValueError(f"block {blk} is also mapped outside the group")
+        if len(refs) > space.num_free:
+            raise PoolExhausted("swap space exhausted")
+        for seq in seqs:
+            for blk in seq.block_table:
+                if blk not in slot_of:
+                    slot = space.free.popleft()
+                    space.refs[slot] = refs[blk]
+                    slot_of[blk] = slot
+                    pairs.append((blk, slot))
+        for seq in seqs:
+            for blk in seq.block_table:
+                self.release(blk)
+            seq.block_table = [slot_of[b] for b in seq.block_table]
+            seq.swapped = True
+        return pairs
+
+    def swap_in(self, seqs, space: SwapSpace):
+        """Resume a swapped-out group: every host slot it maps gets a fresh GPU
+        block with the slot's reference count. Returns the (gpu block, host
+        slot) pairs to copy in before the group runs again."""
+        block_of, pairs = {}, []
+        slots = []
+        for seq in seqs:
+            if not seq.swapped:
+                raise ValueError("sequence is not swapped out")
+            for slot in seq.block_table:
+                if slot not in block_of:
+                    block_of[slot] = None
+                    slots.append(slot)
+        if len(slots) > self.num_free:
+            raise PoolExhausted("KV block pool exhausted")
+        for slot in slots:
+            blk = self.allocate()
+            self.refcount[blk] = space.refs[slot]
+            block_of[slot] = blk
+            pairs.append((blk, slot))
+        for slot in slots:
+            space.refs[slot] = 0
+            space.free.append(slot)
+        for seq in seqs:
+            seq.block_table = [block_of[s] for s in seq.block_table]
+            seq.swapped = False
+        return pairs

@@ -14,7 +14,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 constexpr size_t kAlign = 256;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -120,6 +120,47 @@ int workers_target(int elem, int head_dim, int algo, int G) {
   return g_cus[dev] * waves;
 }
 
+// Device address of a host swap space that is pinned, mapped for the device
+// and holds `bytes` from `host` on; null otherwise (any error the queries
+// leave is cleared).
+void* mapped_host(const void* host, size_t bytes) {
+  hipPointerAttribute_t attr{};
+  if (hipPointerGetAttributes(&attr, host) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (attr.type != hipMemoryTypeHost || attr.devicePointer == nullptr) return nullptr;
+  void* start = nullptr;
+  size_t size = 0;
+  if (hipPointerGetAttribute(&start, HIP_POINTER_ATTRIBUTE_RANGE_START_ADDR, const_cast<void*>(host)) != hipSuccess ||
+      hipPointerGetAttribute(&size, HIP_POINTER_ATTRIBUTE_RANGE_SIZE, const_cast<void*>(host)) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  const uintptr_t h = reinterpret_cast<uintptr_t>(host), s0 = reinterpret_cast<uintptr_t>(start);
+  if (h < s0 || h - s0 > size || bytes > size - (h - s0)) return nullptr;
+  return attr.devicePointer;
+}
+
+pa_status swap_impl(void* k_cache, void* v_cache, const void* host, int32_t host_slots, const int32_t* mapping,
+                    int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                    pa_dtype dtype, bool out, void* stream) {
+  if (!valid_dtype(dtype)) return PA_ERR_INVALID_ARG;
+  if (num_pairs < 0 || host_slots < 0 || num_kv_heads < 1 || head_dim < 1 || block_size < 1 || num_blocks < 1)
+    return PA_ERR_INVALID_ARG;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !host || !mapping || host_slots == 0) return PA_ERR_INVALID_ARG;
+  const size_t block_bytes = (size_t)num_kv_heads * block_size * head_dim * elem_bytes(dtype);
+  const uintptr_t a = block_bytes % 16 == 0 ? 16 : 1;
+  if (!aligned(k_cache, a) || !aligned(v_cache, a) || !aligned(host, a) || !aligned(mapping, 4))
+    return PA_ERR_INVALID_ARG;
+  void* dev_host = mapped_host(host, (size_t)host_slots * 2 * block_bytes);
+  if (!dev_host) return PA_ERR_INVALID_ARG;
+  const hipError_t e = pa::launch_swap(k_cache, v_cache, dev_host, mapping, num_pairs, num_blocks, host_slots,
+                                       block_bytes, out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -162,6 +203,20 @@ pa_status pa_write_kv(const void* k_new, const void* v_new, void* k_cache, void*
                                            head_dim, block_size, num_blocks, elem_bytes(dtype),
                                            static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+pa_status pa_swap_out(void* host, int32_t host_slots, const void* k_cache, const void* v_cache,
+                      const int32_t* block_mapping, int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int32_t num_blocks, pa_dtype dtype, void* stream) {
+  return swap_impl(const_cast<void*>(k_cache), const_cast<void*>(v_cache), host, host_slots, block_mapping,
+                   num_pairs, num_kv_heads, head_dim, block_size, num_blocks, dtype, true, stream);
+}
+
+pa_status pa_swap_in(void* k_cache, void* v_cache, const void* host, int32_t host_slots,
+                     const int32_t* block_mapping, int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t block_size, int32_t num_blocks, pa_dtype dtype, void* stream) {
+  return swap_impl(k_cache, v_cache, host, host_slots, block_mapping, num_pairs, num_kv_heads, head_dim, block_size,
+                   num_blocks, dtype, false, stream);
 }
 
 pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping, int32_t num_pairs,

@@ -71,5 +71,11 @@ hipError_t launch_write_kv(const void* k_new, const void* v_new, void* k_cache, 
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* mapping, int num_pairs,
                               int num_blocks, size_t block_bytes, hipStream_t stream);
 
+// Whole-block moves between the pool and a device-mapped host swap space of
+// host_slots slots ([K image][V image] of block_bytes each); `out` selects
+// pool -> host.
+hipError_t launch_swap(void* k_cache, void* v_cache, void* host, const int32_t* mapping, int num_pairs,
+                       int num_blocks, int host_slots, size_t block_bytes, bool out, hipStream_t stream);
+
 
 }  // namespace pa

@@ -1243,7 +1243,7 @@ __global__ __launch_bounds__(64 * W) void merge_kernel(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// KV write, block copy
+// KV write, block copy, swap
 // ---------------------------------------------------------------------------
 template <typename U>
 __global__ __launch_bounds__(64) void write_kv_kernel(const U* __restrict__ k_new, const U* __restrict__ v_new,
@@ -1382,6 +1382,48 @@ hipError_t launch_write_kv(const void* k_new, const void* v_new, void* k_cache, 
                        static_cast<const uint16_t*>(v_new), static_cast<uint16_t*>(k_cache),
                        static_cast<uint16_t*>(v_cache), slots, num_kv_heads, head_dim, block_size, total);
   }
+  return hipGetLastError();
+}
+
+// One workgroup slice per (pair, K/V): 16-byte (or byte) moves between a
+// pool block and its host slot image.
+template <typename U, bool OUT>
+__global__ __launch_bounds__(256) void swap_kernel(uint8_t* k_cache, uint8_t* v_cache, uint8_t* host,
+                                                   const int32_t* __restrict__ mapping, int num_blocks,
+                                                   int host_slots, size_t block_bytes) {
+  const int pair = blockIdx.x;
+  const int blk = mapping[2 * pair], slot = mapping[2 * pair + 1];
+  if (blk < 0 || blk >= num_blocks || slot < 0 || slot >= host_slots) return;
+  uint8_t* pool = (blockIdx.y ? v_cache : k_cache) + (size_t)blk * block_bytes;
+  uint8_t* img = host + ((size_t)slot * 2 + blockIdx.y) * block_bytes;
+  const U* s = reinterpret_cast<const U*>(OUT ? pool : img);
+  U* d = reinterpret_cast<U*>(OUT ? img : pool);
+  const size_t n = block_bytes / sizeof(U);
+  for (size_t i = (size_t)blockIdx.z * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.z * blockDim.x)
+    d[i] = s[i];
+}
+
+hipError_t launch_swap(void* k_cache, void* v_cache, void* host, const int32_t* mapping, int num_pairs,
+                       int num_blocks, int host_slots, size_t block_bytes, bool out, hipStream_t stream) {
+  uint8_t* k = static_cast<uint8_t*>(k_cache);
+  uint8_t* v = static_cast<uint8_t*>(v_cache);
+  uint8_t* h = static_cast<uint8_t*>(host);
+  const bool wide = block_bytes % 16 == 0;
+  const size_t n = wide ? block_bytes / 16 : block_bytes;
+  const unsigned slices = (unsigned)((n + 255) / 256 < 64 ? (n + 255) / 256 : 64);
+  const dim3 grid((unsigned)num_pairs, 2, slices), block(256);
+  if (wide && out)
+    hipLaunchKernelGGL((swap_kernel<u32x4, true>), grid, block, 0, stream, k, v, h, mapping, num_blocks, host_slots,
+                       block_bytes);
+  else if (wide)
+    hipLaunchKernelGGL((swap_kernel<u32x4, false>), grid, block, 0, stream, k, v, h, mapping, num_blocks,
+                       host_slots, block_bytes);
+  else if (out)
+    hipLaunchKernelGGL((swap_kernel<uint8_t, true>), grid, block, 0, stream, k, v, h, mapping, num_blocks,
+                       host_slots, block_bytes);
+  else
+    hipLaunchKernelGGL((swap_kernel<uint8_t, false>), grid, block, 0, stream, k, v, h, mapping, num_blocks,
+                       host_slots, block_bytes);
   return hipGetLastError();
 }
 

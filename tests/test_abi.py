@@ -43,7 +43,7 @@ def test_exports_match_header(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.pa_abi_version() == 3
+    assert lib.pa_abi_version() == 4
     assert lib.pa_status_string(OK) == b"ok"
     assert lib.pa_status_string(WORKSPACE) == b"workspace missing or too small"
     assert lib.pa_status_string(123) == b"unknown status"
@@ -131,3 +131,16 @@ def test_binding_refuses_host_tensors(lib):
     with pytest.raises(TypeError):
         pb.pa_decode(q.clone(), q, torch.zeros(3, 4, 16, 64), torch.zeros(3, 4, 64, 16),
                      torch.zeros(2, 2, dtype=torch.int32), torch.ones(2, dtype=torch.int32), 0.125, 16)
+
+
+def test_swap_argument_checks(lib):
+    # pa_swap_out(host, slots, k, v, mapping, pairs, Hkv, d, B, NB, dtype, stream)
+    good = [FAKE, 4, FAKE, FAKE, FAKE, 2, 8, 128, 16, 100, 2, None]
+    assert lib.pa_swap_out(*(good[:5] + [0] + good[6:])) == OK          # no pairs: no-op
+    for i, v in ((0, None), (2, None), (4, None), (1, 0), (1, -1), (5, -1), (10, 7)):
+        bad = list(good)
+        bad[i] = v
+        assert lib.pa_swap_out(*bad) == INVALID, (i, v)
+    # a host pointer that is not mapped, pinned host memory is rejected before any launch
+    assert lib.pa_swap_out(*good) == INVALID
+    assert lib.pa_swap_in(FAKE, FAKE, FAKE, 4, FAKE, 2, 8, 128, 16, 100, 2, None) == INVALID

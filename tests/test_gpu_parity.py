@@ -126,6 +126,82 @@ def test_copy_blocks_bit_exact(etype, Hkv, B, d):
     np.testing.assert_array_equal(raw_bits(pb.to_host(vd, etype)), raw_bits(vr))
 
 
+@pytest.mark.parametrize("etype,Hkv,B,d", [("bf16", 8, 16, 128), ("f32", 2, 16, 64), ("f16", 1, 3, 5)])
+def test_swap_blocks_bit_exact(etype, Hkv, B, d):
+    # out to pinned host slots and back into other blocks, pairs outside the
+    # pool or the swap space skipped
+    say(f"swap {etype} {Hkv} {B} {d}")
+    NB, slots = 64, 30
+    seqk, seqv = np.random.SeedSequence(79).spawn(2)
+    k = wl.random_stored(seqk, (NB, Hkv, B, d), etype, 1.0)
+    v = wl.random_stored(seqv, (NB, Hkv, d, B), etype, 1.0)
+    k[5] = wl.poison_value(etype)
+    perm = np.random.default_rng(2).permutation(NB)
+    out_pairs = np.stack([perm[:20], np.arange(3, 23)], axis=1).astype(np.int32)
+    out_pairs[0, 0] = 5
+    bad = np.array([[-1, 24], [perm[30], slots], [NB, 25]], np.int32)
+    kd, vd = pb.to_device(k, etype, DEV), pb.to_device(v, etype, DEV)
+    host = pb.swap_space(slots, kd)
+    host.view(torch.uint8).fill_(0xA5)
+    pb.pa_swap_out(host, kd, vd, pb.int32_to_device(np.concatenate([out_pairs, bad]), DEV))
+    torch.cuda.synchronize()
+    h0 = host.view(torch.uint8).numpy().copy().view(raw_bits(k).dtype).reshape(slots, 2, -1)
+    want = np.full_like(h0, 0xA5A5A5A5 if h0.dtype == np.uint32 else 0xA5A5)
+    want = oracle.swap_out(k.view(want.dtype), v.view(want.dtype), want, out_pairs)
+    np.testing.assert_array_equal(h0, want)
+    in_pairs = np.stack([perm[30:50], np.arange(3, 23)], axis=1).astype(np.int32)
+    pb.pa_swap_in(kd, vd, host, pb.int32_to_device(np.concatenate([in_pairs, bad]), DEV))
+    torch.cuda.synchronize()
+    kr, vr = oracle.swap_in(k, v, h0.view(k.dtype), in_pairs)
+    np.testing.assert_array_equal(raw_bits(pb.to_host(kd, etype)), raw_bits(kr))
+    np.testing.assert_array_equal(raw_bits(pb.to_host(vd, etype)), raw_bits(vr))
+
+
+def test_swap_rejects_pageable_host_memory():
+    kd = torch.zeros((4, 1, 16, 64), dtype=torch.bfloat16, device=DEV)
+    vd = torch.zeros((4, 1, 64, 16), dtype=torch.bfloat16, device=DEV)
+    pageable = torch.zeros((4, 2, 16 * 64), dtype=torch.bfloat16)
+    lib = pb.load_library()
+    m = pb.int32_to_device(np.array([[0, 0]], np.int32), DEV)
+    st = lib.pa_swap_out(pageable.data_ptr(), 4, kd.data_ptr(), vd.data_ptr(), m.data_ptr(), 1, 1, 64, 16, 4, 2,
+                         torch.cuda.current_stream().cuda_stream)
+    assert st == -1
+    small = pb.swap_space(2, kd)            # pinned, but 2 slots where 4 are claimed
+    st = lib.pa_swap_out(small.data_ptr(), 4096, kd.data_ptr(), vd.data_ptr(), m.data_ptr(), 1, 1, 64, 16, 4, 2,
+                         torch.cuda.current_stream().cuda_stream)
+    assert st == -1
+
+
+def test_decode_after_swap_and_resume_is_bit_identical():
+    # a group of sequences is preempted (blocks out to host), its blocks are
+    # overwritten, and it resumes in other blocks: same output to the bit
+    cfg = small_cfg("llama3_8b", num_seqs=48)
+    say("swap and resume")
+    w = wl.make_decode_workload(cfg)
+    dv = Dev(w)
+    dv.write()
+    before = dv.decode()
+    B = cfg.block_size
+    group = range(5, 13)
+    blocks = [int(w.block_tables[s, b]) for s in group for b in range(-(-int(w.context_lens[s]) // B))]
+    host = pb.swap_space(len(blocks), dv.kc)
+    pb.pa_swap_out(host, dv.kc, dv.vc, pb.int32_to_device(np.array([[b, j] for j, b in enumerate(blocks)], np.int32), DEV))
+    idx = torch.tensor(blocks, device=DEV)
+    dv.kc[idx] = float("nan")
+    dv.vc[idx] = float("nan")
+    moved = np.roll(np.array(blocks), 5)
+    pb.pa_swap_in(dv.kc, dv.vc, host, pb.int32_to_device(np.stack([moved, np.arange(len(blocks))], 1).astype(np.int32), DEV))
+    remap = dict(zip(blocks, moved.tolist()))
+    tables = w.block_tables.copy()
+    for s in group:
+        for b in range(-(-int(w.context_lens[s]) // B)):
+            tables[s, b] = remap[int(tables[s, b])]
+    dv.bt = pb.int32_to_device(tables, DEV)
+    after = dv.decode()
+    torch.cuda.synchronize()
+    assert torch.equal(before, after)
+
+
 # ---------------------------------------------------------------------------
 # Decode: tiny fp32 workload, both readings of its lengths, every split mode
 # ---------------------------------------------------------------------------
