@@ -15,6 +15,7 @@ from .paged_attention import (  # noqa: F401
     decode_partitioned,
     decode_probabilities,
     gather_sequence,
+    prefill,
     swap_in,
     swap_out,
     to_float64,

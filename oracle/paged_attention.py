@@ -1,6 +1,6 @@
 """Plain, slow, float64 reference for paged decode attention, the slot-mapped KV
-write, the copy-on-write block copy and the swap of whole blocks to and from
-host memory.
+write, the copy-on-write block copy, the swap of whole blocks to and from
+host memory, and the prompt-phase (prefill) attention over the paged cache.
 
 TEST INFRASTRUCTURE ONLY: imported by tests/, __graft_entry__.smoke() and the
 cpu_baseline leg of bench.py. The library never calls it.
@@ -194,6 +194,44 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
             keys, values = cache[kvh]
             a = decode_probabilities(to_float64(q[s, h], etype), keys, scale)
             out[s, h] = a @ values
+    return out
+
+
+def prefill(q, q_start, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+            etype, seqs=None):
+    """Prompt-phase attention over a paged KV cache ([notes-zh] §2.2: every
+    prompt token is processed at once and its K/V cached; §2.1: token i
+    attends to tokens 1..i). Sequence s owns query rows q_start[s] ..
+    q_start[s+1]-1 of q ([total_q][num_heads][head_dim]); with L =
+    context_lens[s] and n of them, query j sits at position p = L - n + j (the
+    last n tokens of the context; n = L for a whole prompt, fewer when the
+    first tokens were cached before) and reads the cached tokens t <= p:
+        a_t = softmax_{t <= p}(scale * q_j,h . k_t),  o_j,h = sum_{t <= p} a_t v_t,
+    k_t, v_t found through the block table, grouped heads as in decode.
+
+    Returns float64 [total_q][num_heads][head_dim]; rows of sequences not in
+    `seqs` stay NaN.
+    """
+    group = _check_shapes(q, k_cache, v_cache)
+    total_q, num_heads, head_dim = q.shape
+    q_start = np.asarray(q_start)
+    out = np.full((total_q, num_heads, head_dim), np.nan, dtype=np.float64)
+    seq_list = range(len(q_start) - 1) if seqs is None else seqs
+    for s in seq_list:
+        L = int(context_lens[s])
+        q0, q1 = int(q_start[s]), int(q_start[s + 1])
+        n = q1 - q0
+        if n < 1:
+            continue
+        if n > L:
+            raise ValueError(f"sequence {s}: {n} queries but only {L} cached tokens")
+        for kvh in range(num_heads // group):
+            keys, values = gather_sequence(k_cache, v_cache, block_tables[s], L, kvh, block_size, etype)
+            for j in range(n):
+                p = L - n + j
+                for h in range(kvh * group, (kvh + 1) * group):
+                    a = decode_probabilities(to_float64(q[q0 + j, h], etype), keys[:p + 1], scale)
+                    out[q0 + j, h] = a @ values[:p + 1]
     return out
 
 

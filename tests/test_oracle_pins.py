@@ -422,3 +422,80 @@ def test_decode_unchanged_after_a_group_is_swapped_and_resumed():
     oracle.swap_in(ps.k_cache, ps.v_cache, host, in_pairs, inplace=True)
     after = oracle.decode(st.q, ps.k_cache, ps.v_cache, tables(), lens, 0.25, 4, "f32")
     np.testing.assert_array_equal(after, before)
+
+
+# ----------------------------------------------------------------------------
+# Prompt phase ([notes-zh] §2.1-§2.2)
+# ----------------------------------------------------------------------------
+
+def _prefill_case(lengths, queries, Hq=4, Hkv=2, d=8, B=4, etype="f32", seed=11):
+    rng = np.random.default_rng(seed)
+    S = len(lengths)
+    nblk = [-(-L // B) for L in lengths]
+    NB = sum(nblk) + 3
+    perm = rng.permutation(NB)
+    tables = np.full((S, max(nblk)), perm[-1], dtype=np.int32)
+    pos = 0
+    for s in range(S):
+        tables[s, :nblk[s]] = perm[pos:pos + nblk[s]]
+        pos += nblk[s]
+    k = rng.standard_normal((NB, Hkv, B, d)).astype(np.float32)
+    v = rng.standard_normal((NB, Hkv, d, B)).astype(np.float32)
+    q_start = np.concatenate([[0], np.cumsum(queries)]).astype(np.int32)
+    q = rng.standard_normal((int(q_start[-1]), Hq, d)).astype(np.float32)
+    return q, q_start, k, v, tables, np.array(lengths, np.int32)
+
+
+def test_prefill_single_query_is_decode():
+    q, q_start, k, v, tables, lens = _prefill_case([5, 9, 16, 1], [1, 1, 1, 1])
+    got = oracle.prefill(q, q_start, k, v, tables, lens, 0.3, 4, "f32")
+    want = oracle.decode(q, k, v, tables, lens, 0.3, 4, "f32")
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("queries", [None, (3, 9, 1)])
+def test_prefill_matches_torch_sdpa_with_causal_positions(queries):
+    # whole prompts (n = L) against the library's causal attention, and the
+    # last n < L tokens of each context against an explicit position mask
+    lengths = [7, 13, 5]
+    queries = lengths if queries is None else list(queries)
+    q, q_start, k, v, tables, lens = _prefill_case(lengths, queries, Hq=6, Hkv=3, d=16, B=4)
+    got = oracle.prefill(q, q_start, k, v, tables, lens, 0.25, 4, "f32")
+    g = 2
+    for s, (L, n) in enumerate(zip(lengths, queries)):
+        rows = slice(int(q_start[s]), int(q_start[s + 1]))
+        for h in range(6):
+            keys, values = oracle.gather_sequence(k, v, tables[s], L, h // g, 4, "f32")
+            qq = torch.from_numpy(q[rows, h].astype(np.float64))[None, None]
+            kk = torch.from_numpy(keys)[None, None]
+            vv = torch.from_numpy(values)[None, None]
+            if n == L:
+                ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, is_causal=True, scale=0.25)
+            else:
+                mask = torch.arange(L)[None, :] <= (L - n + torch.arange(n))[:, None]
+                ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, attn_mask=mask, scale=0.25)
+            np.testing.assert_allclose(got[rows, h], ref[0, 0].numpy(), rtol=0, atol=1e-12)
+
+
+def test_prefill_bruteforce_and_pool_permutation():
+    lengths, queries = [6, 3], [4, 3]
+    q, q_start, k, v, tables, lens = _prefill_case(lengths, queries, Hq=2, Hkv=1, d=3, B=2)
+    got = oracle.prefill(q, q_start, k, v, tables, lens, 0.7, 2, "f32")
+    for s, (L, n) in enumerate(zip(lengths, queries)):
+        for j in range(n):
+            p = L - n + j
+            for h in range(2):
+                scores = []
+                for t in range(p + 1):
+                    blk, off = int(tables[s][t // 2]), t % 2
+                    scores.append(0.7 * sum(float(q[q_start[s] + j, h, c]) * float(k[blk, 0, off, c]) for c in range(3)))
+                m = max(scores)
+                w = [math.exp(x - m) for x in scores]
+                z = sum(w)
+                for c in range(3):
+                    o = sum(w[t] / z * float(v[int(tables[s][t // 2]), 0, c, t % 2]) for t in range(p + 1))
+                    assert abs(got[q_start[s] + j, h, c] - o) < 1e-12
+    perm = np.random.default_rng(3).permutation(k.shape[0])
+    inv = np.argsort(perm)
+    again = oracle.prefill(q, q_start, k[perm], v[perm], inv[tables].astype(np.int32), lens, 0.7, 2, "f32")
+    np.testing.assert_array_equal(again, got)
