@@ -26,7 +26,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, vendor figure
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_131_amd", "csrc", f)
-                  for f in ("pa_kernels.hip", "pa_api.cpp", "pa_internal.h")]
+                  for f in ("pa_kernels.hip", "pa_prefill.hip", "pa_api.cpp", "pa_internal.h", "pa_device.h")]
 
 WORKLOAD_TEXT = {
     "llama3_8b": "Llama-3-8B-shaped GQA decode: 256 seqs, 32 q / 8 kv heads, head_dim 128, block 16, bf16, "

@@ -163,6 +163,34 @@ pa_status pa_write_decode(void* out, const void* q, const void* k_new, const voi
                           int32_t max_context_len, float scale, int32_t partition_size, void* workspace,
                           size_t workspace_bytes, pa_dtype dtype, pa_dtype out_dtype, void* stream);
 
+/*
+ * pa_prefill -- prompt-phase attention over the paged cache ([notes-zh] §2.2:
+ * every prompt token is processed at once; §2.1: token i attends to tokens
+ * 1..i, here 0-based positions).
+ *   q: [total_q][num_heads][head_dim] of dtype, the queries of all sequences
+ *     packed: sequence s owns rows q_start[s] .. q_start[s+1]-1 (q_start:
+ *     device int32 [num_seqs + 1], non-decreasing, from 0 to total_q).
+ *   With n queries and L = context_lens[s], query j sits at position
+ *   L - n + j (the last n tokens of the context, whose K/V the caller has
+ *   already stored, e.g. with pa_write_kv; n = L for a whole prompt, fewer
+ *   when its first tokens were cached before) and attends to tokens
+ *   0 .. L - n + j through block_tables[s]:
+ *     out[row][h] = sum_t a_t v_t,  a = softmax_t(scale * q[row][h] . k_t),
+ *   grouped heads as in pa_decode, fp32 accumulation.
+ *   out: [total_q][num_heads][head_dim] of out_dtype.
+ *   16-bit dtype only (fp32 gives PA_ERR_UNSUPPORTED); head_dim 64 or 128;
+ *   block_size a power of two in [8, 128]. Sequences with n <= 0, n > L, L
+ *   beyond max_blocks_per_seq*block_size or rows outside [0, total_q) are
+ *   skipped (their rows untouched).
+ *   No workspace.
+ */
+pa_status pa_prefill(void* out, const void* q, const int32_t* q_start, int32_t total_q,
+                     const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                     const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                     int32_t num_blocks, int32_t max_blocks_per_seq, float scale,
+                     pa_dtype dtype, pa_dtype out_dtype, void* stream);
+
 /* Workspace bytes pa_decode needs for these sizes (0 when it needs none).
  * Returns 0 as well for arguments pa_decode would reject. Pure host function. */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,

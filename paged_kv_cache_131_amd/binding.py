@@ -35,6 +35,8 @@ SIGNATURES = {
                                _i32, _p, _sz, _i32, _i32, _p]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_copy_blocks": (_i32, [_p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p]),
+    "pa_prefill": (_i32, [_p, _p, _p, _i32, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+                          _i32, _p]),
     "pa_swap_out": (_i32, [_p, _i32, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p]),
     "pa_swap_in": (_i32, [_p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p]),
     "pa_status_string": (ctypes.c_char_p, [_i32]),
@@ -258,3 +260,22 @@ def pa_swap_in(k_cache, v_cache, host, block_mapping, stream=None) -> None:
     _check("pa_swap_in", lib.pa_swap_in(_dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
                                         host.data_ptr(), slots, ptr, P, Hkv, d, B, NB, DTYPE_CODE[dt],
                                         _stream(stream)))
+
+
+def pa_prefill(out, q, q_start, k_cache, v_cache, block_tables, context_lens, scale, stream=None) -> None:
+    """q, out [total_q][num_heads][head_dim]; q_start [num_seqs + 1] int32: sequence s owns rows
+    q_start[s] .. q_start[s+1]-1, the last tokens of its context_lens[s]."""
+    lib = load_library()
+    TQ, Hq, d = q.shape
+    NB, Hkv, B, _ = k_cache.shape
+    if out.shape != q.shape or v_cache.shape != (NB, Hkv, d, B) or k_cache.shape[3] != d:
+        raise ValueError("inconsistent shapes")
+    S = context_lens.shape[0]
+    if q_start.shape != (S + 1,) or block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("q_start must be [num_seqs + 1], block_tables [num_seqs][max_blocks]")
+    dt = k_cache.dtype
+    _check("pa_prefill", lib.pa_prefill(
+        _dev(out, "out"), _dev(q, "q", dt), _dev(q_start, "q_start", torch.int32), TQ, _dev(k_cache, "k_cache", dt),
+        _dev(v_cache, "v_cache", dt), _dev(block_tables, "block_tables", torch.int32),
+        _dev(context_lens, "context_lens", torch.int32), S, Hq, Hkv, d, B, NB, block_tables.shape[1], float(scale),
+        DTYPE_CODE[dt], DTYPE_CODE[out.dtype], _stream(stream)))

@@ -12,7 +12,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = [os.path.join(HERE, "csrc", "pa_kernels.hip"), os.path.join(HERE, "csrc", "pa_api.cpp")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("pa_kernels.hip", "pa_prefill.hip", "pa_api.cpp")]
 LIBRARY = os.path.join(HERE, "libpagedattn.so")
 ARCH = "gfx950"
 FLAGS = [

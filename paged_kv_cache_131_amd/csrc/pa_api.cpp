@@ -14,7 +14,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 4;
+constexpr int kAbiVersion = 5;
 constexpr size_t kAlign = 256;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -202,6 +202,56 @@ pa_status pa_write_kv(const void* k_new, const void* v_new, void* k_cache, void*
   const hipError_t e = pa::launch_write_kv(k_new, v_new, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads,
                                            head_dim, block_size, num_blocks, elem_bytes(dtype),
                                            static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+pa_status pa_prefill(void* out, const void* q, const int32_t* q_start, int32_t total_q, const void* k_cache,
+                     const void* v_cache, const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                     int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                     int32_t num_blocks, int32_t max_blocks_per_seq, float scale, pa_dtype dtype, pa_dtype out_dtype,
+                     void* stream) {
+  if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return PA_ERR_INVALID_ARG;
+  if (num_seqs < 0 || total_q < 0 || num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads)
+    return PA_ERR_INVALID_ARG;
+  if (num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
+  if (num_blocks < 1 || max_blocks_per_seq < 1 || !std::isfinite(scale)) return PA_ERR_INVALID_ARG;
+  const int log2b = log2_exact(block_size);
+  if (block_size < 8 || block_size > 128 || log2b < 0) return PA_ERR_UNSUPPORTED;
+  if ((long long)max_blocks_per_seq * block_size > INT_MAX) return PA_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (dtype == PA_F32) return PA_ERR_UNSUPPORTED;
+  const int group = num_heads / num_kv_heads;
+  if (group > pa::kMaxGroup) return PA_ERR_UNSUPPORTED;
+  if (num_seqs > pa::kMaxBalancedSeqs) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || total_q == 0) return PA_OK;
+  if (!out || !q || !q_start || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 4) ||
+      !aligned(q_start, 4) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return PA_ERR_INVALID_ARG;
+  pa::PrefillParams p{};
+  p.out = out;
+  p.q = q;
+  p.q_start = q_start;
+  p.total_q = total_q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = group;
+  p.block_size = block_size;
+  p.log2_block = log2b;
+  p.num_blocks = num_blocks;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.qt = 16 / group;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.out_dtype = out_dtype;
+  const long long tiles = ((long long)total_q + p.qt - 1) / p.qt + num_seqs;
+  if (tiles > INT_MAX) return PA_ERR_UNSUPPORTED;
+  const int elem = dtype == PA_F16 ? pa::kF16 : pa::kBF16;
+  const hipError_t e = pa::launch_prefill(p, elem, head_dim, (unsigned)tiles, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

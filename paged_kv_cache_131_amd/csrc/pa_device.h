@@ -1,0 +1,159 @@
+// Device helpers shared by the HIP kernels of libpagedattn (decode, write,
+// copy, swap, prefill): element types and their MFMA operands, 16-byte
+// loads, output rounding and the block-table lookups of one 32-token chunk.
+// Included by each .hip source into its own anonymous namespace.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ u32x4 load16(const void* ptr) {
+  return *reinterpret_cast<const u32x4*>(ptr);
+}
+
+// K/V tiles are read exactly once per launch: stream them past the caches.
+__device__ __forceinline__ u32x4 load16_stream(const void* ptr) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// Element types
+// ---------------------------------------------------------------------------
+template <int E>
+struct ElemT;
+
+template <>
+struct ElemT<kF32> {
+  using raw = uint32_t;
+  static constexpr int kVec = 4;  // elements per 16 bytes
+  __device__ static void widen(u32x4 w, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(w[i]);
+  }
+  // zero the elements of tokens >= nvalid (one token per element)
+  __device__ static u32x4 keep_first(u32x4 w, int nvalid) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = i < nvalid ? w[i] : 0u;
+    return w;
+  }
+};
+
+template <>
+struct ElemT<kF16> {
+  using raw = uint16_t;
+  using op8 = f16x8;
+  using scalar = _Float16;
+  static constexpr int kVec = 8;
+  __device__ static void widen(u32x4 w, float* f) {
+    const f16x8 h = __builtin_bit_cast(f16x8, w);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = static_cast<float>(h[i]);
+  }
+  __device__ static u32x4 keep_first(u32x4 w, int nvalid) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t m = 2 * i + 1 < nvalid ? 0xffffffffu : (2 * i < nvalid ? 0x0000ffffu : 0u);
+      w[i] &= m;
+    }
+    return w;
+  }
+};
+
+template <>
+struct ElemT<kBF16> {
+  using raw = uint16_t;
+  using op8 = bf16x8;
+  using scalar = __bf16;
+  static constexpr int kVec = 8;
+  __device__ static void widen(u32x4 w, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ static u32x4 keep_first(u32x4 w, int nvalid) { return ElemT<kF16>::keep_first(w, nvalid); }
+};
+
+__device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_16x16x32(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void store_out(void* out, size_t idx, float v, int out_dtype) {
+  if (out_dtype == kF32) {
+    static_cast<float*>(out)[idx] = v;
+  } else if (out_dtype == kF16) {
+    static_cast<_Float16*>(out)[idx] = static_cast<_Float16>(v);
+  } else {
+    static_cast<__bf16*>(out)[idx] = static_cast<__bf16>(v);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Block-table lookups for one 32-token chunk. A chunk spans at most four
+// blocks (block_size >= 8); ids are read with wave-uniform addresses and the
+// logical block is clamped to the segment's last block, so tokens past the
+// context never index past the table's valid entries. Ids are clamped into
+// the pool.
+// ---------------------------------------------------------------------------
+struct ChunkIds {
+  int lb0;
+  int id0, id1, id2, id3;
+};
+
+// The block table is read-only for the whole launch; reading it through the
+// constant address space lets wave-uniform reads use scalar loads, which are
+// counted apart from the K/V vector loads in flight.
+typedef const __attribute__((address_space(4))) int32_t const_i32;
+
+__device__ __forceinline__ int table_entry(const int32_t* tbl, int lb, int lbl) {
+  const const_i32* t = (const const_i32*)tbl;
+  return t[min(lb, lbl)];
+}
+
+// Raw entries of the (up to four) blocks of the chunk starting at `cs`,
+// loaded unconditionally and used (clamped) only when picked, so the loads
+// stay in flight until then.
+__device__ __forceinline__ ChunkIds load_chunk_ids(const int32_t* tbl, int cs, int lbl, int log2_block) {
+  ChunkIds c;
+  c.lb0 = cs >> log2_block;
+  c.id0 = table_entry(tbl, c.lb0, lbl);
+  c.id1 = table_entry(tbl, c.lb0 + 1, lbl);
+  c.id2 = table_entry(tbl, c.lb0 + 2, lbl);
+  c.id3 = table_entry(tbl, c.lb0 + 3, lbl);
+  return c;
+}
+
+// The table entry of token tok's block, as stored.
+__device__ __forceinline__ int pick_entry(ChunkIds c, int tok, int log2_block, int lbl) {
+  const int k = min(tok >> log2_block, lbl) - c.lb0;
+  int id = c.id0;
+  id = k >= 1 ? c.id1 : id;
+  id = k >= 2 ? c.id2 : id;
+  id = k >= 3 ? c.id3 : id;
+  return id;
+}
+
+__device__ __forceinline__ int pick_block(ChunkIds c, int tok, int log2_block, int lbl, int num_blocks) {
+  return min(max(pick_entry(c, tok, log2_block, lbl), 0), num_blocks - 1);
+}
+
+}  // namespace
+}  // namespace pa

@@ -68,6 +68,32 @@ hipError_t launch_write_kv(const void* k_new, const void* v_new, void* k_cache, 
                            const int32_t* slots, int num_tokens, int num_kv_heads, int head_dim,
                            int block_size, int num_blocks, int elem_bytes, hipStream_t stream);
 
+struct PrefillParams {
+  void* out;
+  const void* q;               // [total_q][num_heads][head_dim]
+  const int32_t* q_start;      // [num_seqs + 1]
+  int32_t total_q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t group;
+  int32_t block_size;
+  int32_t log2_block;
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  int32_t qt;                  // query tokens per tile: the 16 MFMA columns hold qt x group (query, head) pairs
+  float scale_log2;
+  int32_t out_dtype;
+};
+
+// Prompt-phase attention: grid (tiles, num_kv_heads), tiles an upper bound of
+// sum over sequences of ceil(queries / qt).
+hipError_t launch_prefill(const PrefillParams& p, int elem, int head_dim, unsigned tiles, hipStream_t stream);
+
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* mapping, int num_pairs,
                               int num_blocks, size_t block_bytes, hipStream_t stream);
 

@@ -523,3 +523,100 @@ def make_shared_prefix_workload(prefix_len: int = 1024, cfg: DecodeConfig = SHAR
             k_cache[last, :, off:, :] = pv
             v_cache[last, :, :, off:] = pv
     return DecodeWorkload(cfg, q, k_cache, v_cache, tables, lens, k_new, v_new, slots, num_blocks, poison_block, used)
+
+
+# --------------------------------------------------------------------------
+# Prompt phase: a batch of prompts whose K/V is in the pool.
+# --------------------------------------------------------------------------
+
+PREFILL = DecodeConfig("prefill", 7, 32, 32, 8, 128, 16, "bf16", 1.0, ("lognormal", 800.0, 1.0, 16, 8192), 8192)
+
+
+@dataclass
+class PrefillWorkload:
+    """Prompt-phase inputs. The pool holds all context_lens[s] tokens of each
+    sequence; its n_s queries, the context's last n_s tokens (n_s = L for a
+    whole prompt), are packed in q rows q_start[s] .. q_start[s+1]-1."""
+    cfg: DecodeConfig
+    q: np.ndarray
+    q_start: np.ndarray
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    block_tables: np.ndarray
+    context_lens: np.ndarray
+    num_blocks: int
+    poison_block: int
+    used_blocks: np.ndarray
+
+    @property
+    def total_q(self) -> int:
+        return int(self.q_start[-1])
+
+    @property
+    def queries(self) -> np.ndarray:
+        return np.diff(self.q_start)
+
+    def pairs(self) -> int:
+        """(query, cached token) pairs a causal pass scores: query j of n at
+        position L - n + j sees L - n + j + 1 tokens."""
+        n = self.queries.astype(np.int64)
+        L = self.context_lens.astype(np.int64)
+        return int((n * (L - n) + n * (n + 1) // 2).sum())
+
+    def flops(self) -> int:
+        """QK and PV products: 2 * head_dim flops each per (pair, query head)."""
+        return self.pairs() * self.cfg.num_heads * self.cfg.head_dim * 4
+
+    def kv_bytes(self) -> int:
+        c = self.cfg
+        return int(self.context_lens.astype(np.int64).sum()) * c.num_kv_heads * c.head_dim * 2 * ELEMENT_BYTES[c.etype]
+
+
+def make_prefill_workload(cfg: DecodeConfig = PREFILL, lengths=None, queries=None, poison: bool = True,
+                          values: bool = True, contiguous: bool = False) -> PrefillWorkload:
+    """Draw a prompt-phase batch: context lengths from the config's law (or
+    given), `queries` per sequence (default: the whole context, 0 <= n <= L),
+    blocks handed out in the seeded shuffled order (in order with
+    contiguous=True). Unused blocks and the slots past each context are
+    poisoned."""
+    seqs = np.random.SeedSequence(1000 + cfg.index).spawn(5)
+    rng_len, rng_pool = np.random.default_rng(seqs[0]), np.random.default_rng(seqs[1])
+    lens = draw_lengths(cfg, rng_len) if lengths is None else np.asarray(lengths, dtype=np.int32)
+    if lens.shape != (cfg.num_seqs,) or lens.min() < 1:
+        raise ValueError("one positive length per sequence is required")
+    n = lens.copy() if queries is None else np.asarray(queries, dtype=np.int32)
+    if n.shape != lens.shape or n.min() < 0 or np.any(n > lens):
+        raise ValueError("queries must satisfy 0 <= n <= L per sequence")
+    q_start = np.concatenate([[0], np.cumsum(n.astype(np.int64))]).astype(np.int32)
+    B = cfg.block_size
+    nblk = -(-lens.astype(np.int64) // B)
+    need = int(nblk.sum())
+    num_blocks = cfg.pool_blocks if cfg.pool_blocks else math.ceil(1.1 * need)
+    if num_blocks <= need:
+        raise ValueError("pool too small to leave a spare block for poisoned padding")
+    perm = np.arange(num_blocks, dtype=np.int32) if contiguous else rng_pool.permutation(num_blocks).astype(np.int32)
+    max_blocks = max(-(-cfg.max_len // B), int(nblk.max()))
+    poison_block = int(perm[need])
+    tables = np.full((cfg.num_seqs, max_blocks), poison_block, dtype=np.int32)
+    pos = 0
+    for s in range(cfg.num_seqs):
+        tables[s, :nblk[s]] = perm[pos:pos + nblk[s]]
+        pos += int(nblk[s])
+    used = perm[:need]
+    if not values:
+        return PrefillWorkload(cfg, None, q_start, None, None, tables, lens.copy(), num_blocks, poison_block, used)
+    Hkv, d = cfg.num_kv_heads, cfg.head_dim
+    q = random_stored(seqs[2], (int(q_start[-1]), cfg.num_heads, d), cfg.etype, cfg.value_scale)
+    k_cache = random_stored(seqs[3], (num_blocks, Hkv, B, d), cfg.etype, cfg.value_scale)
+    v_cache = random_stored(seqs[4], (num_blocks, Hkv, d, B), cfg.etype, cfg.value_scale)
+    if poison:
+        pv = poison_value(cfg.etype)
+        k_cache[perm[need:]] = pv
+        v_cache[perm[need:]] = pv
+        for s in range(cfg.num_seqs):
+            off = int(lens[s]) % B
+            if off:
+                last = tables[s, nblk[s] - 1]
+                k_cache[last, :, off:, :] = pv
+                v_cache[last, :, :, off:] = pv
+    return PrefillWorkload(cfg, q, q_start, k_cache, v_cache, tables, lens.copy(), num_blocks, poison_block, used)

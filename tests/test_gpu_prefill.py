@@ -1,0 +1,169 @@
+"""Parity of prompt-phase attention (pa_prefill, through the C ABI) with the
+CPU oracle: max-abs error <= 2e-3 for 16-bit inputs (fp32 accumulation), plus
+one unit in the last place of the reference for 16-bit outputs. Small batches
+are compared whole; the full-size batch on sampled query rows, each checked
+against the oracle's decode of that single query over the context up to its
+own position (causal attention of the token at position p is exactly decode
+over p + 1 tokens)."""
+
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_cache_131_amd import binding as pb
+from paged_kv_cache_131_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+TOL = 2e-3
+OUT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def check(got, ref, label, out_etype):
+    g = got.float().cpu().numpy().astype(np.float64)
+    mask = ~np.isnan(ref)
+    assert mask.any()
+    err = np.abs(g[mask] - ref[mask])
+    bound = TOL
+    if out_etype != "f32":
+        ulp = np.spacing(np.abs(ref[mask]).astype(np.float16 if out_etype == "f16" else np.float32))
+        if out_etype == "bf16":
+            ulp = ulp.astype(np.float64) * 65536.0
+        bound = TOL + ulp
+    say(f"  {label}: max |gpu - oracle| = {float(err.max()):.3e} over {mask.sum()} values")
+    assert np.all(np.isfinite(g[mask])), f"{label}: non-finite output"
+    assert np.all(err <= bound), f"{label}: error {float(err.max())} above tolerance"
+
+
+def run_prefill(w, out_etype="f32", q_start=None, context_lens=None, sentinel=None):
+    et = w.cfg.etype
+    q = pb.to_device(w.q, et, DEV)
+    out = torch.empty(q.shape, dtype=OUT[out_etype], device=DEV)
+    if sentinel is not None:
+        out.fill_(sentinel)
+    pb.pa_prefill(out, q, pb.int32_to_device(w.q_start if q_start is None else q_start, DEV),
+                  pb.to_device(w.k_cache, et, DEV), pb.to_device(w.v_cache, et, DEV),
+                  pb.int32_to_device(w.block_tables, DEV),
+                  pb.int32_to_device(w.context_lens if context_lens is None else context_lens, DEV), w.cfg.scale)
+    torch.cuda.synchronize()
+    return out
+
+
+def cfg_of(etype, Hq, Hkv, d, B, lengths, index=40):
+    return dataclasses.replace(wl.PREFILL, name="prefill_small", index=index, num_seqs=len(lengths),
+                               num_heads=Hq, num_kv_heads=Hkv, head_dim=d, block_size=B, etype=etype,
+                               lengths=("fixed", tuple(lengths)), max_len=max(lengths))
+
+
+LENS = [1, 2, 31, 32, 33, 100, 257, 300]
+WHOLE = LENS
+CHUNKED = [1, 1, 7, 32, 1, 37, 64, 129]
+
+
+@pytest.mark.parametrize("etype,Hq,Hkv,d,B", [
+    ("f16", 4, 4, 64, 16),      # g = 1: 16 queries per tile
+    ("bf16", 8, 2, 128, 16),    # g = 4
+    ("bf16", 16, 2, 128, 32),   # g = 8: 2 queries per tile
+    ("f16", 6, 2, 64, 8),       # g = 3: 15 of 16 columns used, 4 blocks per chunk
+    ("bf16", 5, 1, 128, 128),   # g = 5: 3 queries per tile, chunks inside one block
+    ("f16", 2, 1, 128, 64),     # g = 2
+])
+@pytest.mark.parametrize("whole", [True, False])
+def test_prefill_matches_oracle(etype, Hq, Hkv, d, B, whole):
+    say(f"prefill {etype} Hq={Hq} Hkv={Hkv} d={d} B={B} whole={whole}")
+    w = wl.make_prefill_workload(cfg_of(etype, Hq, Hkv, d, B, LENS), queries=WHOLE if whole else CHUNKED)
+    ref = oracle.prefill(w.q, w.q_start, w.k_cache, w.v_cache, w.block_tables, w.context_lens, w.cfg.scale, B, etype)
+    for out_etype in ("f32", etype):
+        check(run_prefill(w, out_etype), ref, f"out {out_etype}", out_etype)
+
+
+def test_prefill_headline_shapes_small():
+    """Llama-3-8B head shapes (32 query heads, 8 KV heads, d 128, B 16, bf16)
+    on a small ragged batch with a zero-query sequence."""
+    say("prefill llama3-8b shapes, small")
+    lens = [5, 48, 160, 97]
+    w = wl.make_prefill_workload(cfg_of("bf16", 32, 8, 128, 16, lens, index=41), queries=[5, 0, 160, 40])
+    ref = oracle.prefill(w.q, w.q_start, w.k_cache, w.v_cache, w.block_tables, w.context_lens, w.cfg.scale, 16,
+                         "bf16")
+    check(run_prefill(w, "bf16"), ref, "out bf16", "bf16")
+
+
+def test_prefill_skips_sequences_outside_preconditions():
+    """A sequence with more queries than cached tokens, or a context beyond
+    its block table, is skipped: its rows keep what they held."""
+    say("prefill skipped sequences")
+    lens = [40, 70, 33]
+    w = wl.make_prefill_workload(cfg_of("f16", 4, 2, 64, 16, lens, index=42), queries=[40, 20, 33])
+    cl = w.context_lens.copy()
+    cl[0] = 39                                          # 40 queries, 39 tokens
+    cl[2] = w.block_tables.shape[1] * 16 + 1            # beyond the table
+    got = run_prefill(w, "f32", context_lens=cl, sentinel=7.0)
+    ref = oracle.prefill(w.q, w.q_start, w.k_cache, w.v_cache, w.block_tables, w.context_lens, w.cfg.scale, 16,
+                         "f16", seqs=[1])
+    check(got, ref, "kept sequence", "f32")
+    g = got.cpu().numpy()
+    q0 = w.q_start
+    assert np.all(g[q0[0]:q0[1]] == 7.0) and np.all(g[q0[2]:q0[3]] == 7.0)
+
+
+def test_prefill_after_write_kv():
+    """The prompt's K/V stored token by token with pa_write_kv into an
+    otherwise poisoned pool, then attended with pa_prefill."""
+    say("prefill after write_kv")
+    lens = [23, 64, 150]
+    w = wl.make_prefill_workload(cfg_of("bf16", 8, 2, 128, 16, lens, index=43))
+    B, Hkv, d = 16, 2, 128
+    pv = wl.poison_value("bf16")
+    k0 = np.full_like(w.k_cache, pv)
+    v0 = np.full_like(w.v_cache, pv)
+    # token t of sequence s goes to slot table[t // B] * B + t % B, K/V drawn fresh
+    slots = np.concatenate([w.block_tables[s, np.arange(L) // B].astype(np.int64) * B + np.arange(L) % B
+                            for s, L in enumerate(lens)]).astype(np.int32)
+    ks, vs = np.random.SeedSequence(99).spawn(2)
+    kn = wl.random_stored(ks, (len(slots), Hkv, d), "bf16", 1.0)
+    vn = wl.random_stored(vs, (len(slots), Hkv, d), "bf16", 1.0)
+    kd, vd = pb.to_device(k0, "bf16", DEV), pb.to_device(v0, "bf16", DEV)
+    pb.pa_write_kv(pb.to_device(kn, "bf16", DEV), pb.to_device(vn, "bf16", DEV), kd, vd,
+                   pb.int32_to_device(slots, DEV))
+    kr, vr = oracle.write_kv(k0, v0, kn, vn, slots, B)
+    q = pb.to_device(w.q, "bf16", DEV)
+    out = torch.empty(q.shape, dtype=torch.float32, device=DEV)
+    pb.pa_prefill(out, q, pb.int32_to_device(w.q_start, DEV), kd, vd, pb.int32_to_device(w.block_tables, DEV),
+                  pb.int32_to_device(w.context_lens, DEV), w.cfg.scale)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(w.q, w.q_start, kr, vr, w.block_tables, w.context_lens, w.cfg.scale, B, "bf16")
+    check(out, ref, "prefill over written pool", "f32")
+
+
+def test_prefill_full_size_sampled():
+    """The 32-prompt Llama-3-8B batch (lognormal lengths, median 800) at full
+    size, in the launch the benchmark times; sampled rows against the oracle,
+    every output finite."""
+    w = wl.make_prefill_workload()
+    say(f"prefill full size: {w.cfg.num_seqs} prompts, {w.total_q} queries, max L {w.context_lens.max()}")
+    got = run_prefill(w, "bf16")
+    g = got.float().cpu().numpy()
+    assert np.all(np.isfinite(g))
+    rng = np.random.default_rng(3)
+    longest = int(np.argmax(w.context_lens))
+    rows = [(longest, 0), (longest, int(w.context_lens[longest]) - 1), (0, 0)]
+    for s in rng.choice(w.cfg.num_seqs, size=13, replace=False):
+        n = int(w.queries[s])
+        rows.append((int(s), int(rng.integers(0, n))))
+    B = w.cfg.block_size
+    for s, j in rows:
+        L, n = int(w.context_lens[s]), int(w.queries[s])
+        p = L - n + j
+        row = int(w.q_start[s]) + j
+        ref = oracle.decode(w.q[row:row + 1], w.k_cache, w.v_cache, w.block_tables[s:s + 1],
+                            np.array([p + 1], np.int32), w.cfg.scale, B, "bf16")
+        check(got[row:row + 1], ref, f"seq {s} query {j} (position {p})", "bf16")

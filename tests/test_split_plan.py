@@ -127,3 +127,43 @@ def test_partition_stream_runs_each_partition_once(W, pc):
         for w in {r[0] for r in runs}:
             mine = [(s, k) for (ww, s, k) in runs if ww == w]
             assert mine == sorted(mine)
+
+
+def prefill_tile_map(q_start, total_q, qt, grid):
+    """The prompt-phase kernel's tile map: workgroup x takes tile T-1-x of the
+    tiles laid end to end over the sequences (ceil(n / qt) each; none for a
+    sequence whose rows are not inside [0, total_q) in order)."""
+    S = len(q_start) - 1
+    nt = [(b - a + qt - 1) // qt if (a >= 0 and b > a and b <= total_q) else 0
+          for a, b in zip(q_start[:-1], q_start[1:])]
+    pref = np.concatenate([[0], np.cumsum(nt)]).astype(np.int64)
+    T = int(pref[-1])
+    out = []
+    for x in range(grid):
+        if x >= T:
+            continue
+        tile = T - 1 - x
+        s = int(np.searchsorted(pref, tile, side="right") - 1)
+        out.append((s, tile - int(pref[s])))
+    assert S >= 0
+    return out, nt
+
+
+@pytest.mark.parametrize("g", [1, 2, 3, 4, 5, 8])
+def test_prefill_tile_map_covers_each_tile_once(g):
+    qt = max(1, 16 // g)
+    rng = np.random.default_rng(g)
+    for trial in range(50):
+        S = int(rng.integers(1, 200))
+        n = rng.integers(0, 300, size=S)
+        if trial % 4 == 0:
+            n[rng.integers(0, S)] = 0
+        q_start = np.concatenate([[0], np.cumsum(n)]).astype(np.int64)
+        total_q = int(q_start[-1])
+        grid = -(-total_q // qt) + S               # the host's launch bound
+        tiles, nt = prefill_tile_map(q_start.tolist(), total_q, qt, grid)
+        assert sorted(tiles) == [(s, k) for s in range(S) for k in range(nt[s])]
+        # the tile's queries stay inside the sequence's rows and its 16 columns
+        for s, k in tiles:
+            nq = min(qt, int(n[s]) - k * qt)
+            assert 1 <= nq <= qt and nq * g <= 16
