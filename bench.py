@@ -42,7 +42,11 @@ WORKLOAD_TEXT = {
                    "128, block 16, bf16",
     "shared_prefix": "shared prefix: 256 requests mapping one 1024-token prompt prefix plus own suffixes of U[16, 512] "
                      "tokens, 32 q / 8 kv heads, head_dim 128, block 16, bf16",
+    "prefill": "prompt phase: 32 whole prompts, lengths lognormal(median 800, sigma 1) clipped to [16, 8192], causal "
+               "attention over their K/V in the paged pool, 32 q / 8 kv heads, head_dim 128, block 16, bf16, "
+               "shuffled pool",
 }
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}   # MI355X dense matrix peak
 
 
 def kernel_hash() -> str:
@@ -134,7 +138,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, workload: str, calibratio
                 if name.startswith("__amd_rocclr_copyBuffer"):
                     calib = max(calib, v)
                     continue
-                for k in TWO_CALL_KERNELS:
+                for k in TWO_CALL_KERNELS + ("prefill_kernel",):
                     if f"::{k}<" in name:
                         vals[k].append(v)
         return {k: float(np.mean(v)) for k, v in vals.items()}, calib
@@ -153,6 +157,8 @@ def summarize_counters(fetch_csv: str, write_csv: str, workload: str, calibratio
     for key, ks in (("+".join(FUSED_KERNELS), FUSED_KERNELS), ("+".join(TWO_CALL_KERNELS), TWO_CALL_KERNELS)):
         if all(k in kernels for k in ks):
             entry[key] = sum(kernels[k]["traffic_bytes"] for k in ks)
+    if "prefill_kernel" in kernels:
+        entry["prefill_kernel"] = kernels["prefill_kernel"]["traffic_bytes"]
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
@@ -294,6 +300,99 @@ def swap_sweep(torch, pb, total_mib: int, reps: int) -> dict:
     return res
 
 
+def prefill_cpu_baseline(w, budget_s: float) -> dict:
+    """The oracle on the shortest prompts first until the time budget is
+    spent (at least one), BLAS pinned to one thread."""
+    import oracle
+
+    from threadpoolctl import threadpool_limits
+
+    c = w.cfg
+    order = np.argsort(w.context_lens, kind="stable")
+    done, pairs = 0, 0
+    n = w.queries.astype(np.int64)
+    L = w.context_lens.astype(np.int64)
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        while done < c.num_seqs:
+            s = int(order[done])
+            oracle.prefill(w.q, w.q_start, w.k_cache, w.v_cache, w.block_tables, w.context_lens, c.scale,
+                           c.block_size, c.etype, seqs=[s])
+            pairs += int(n[s] * (L[s] - n[s]) + n[s] * (n[s] + 1) // 2)
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = time.perf_counter() - t0
+    flops = pairs * c.num_heads * c.head_dim * 4
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"the {done} shortest of {c.num_seqs} prompts, all heads, {dt:.1f} s, float64 NumPy oracle"}
+
+
+def prefill_main(args, torch, pb, wl, dev) -> int:
+    """One step = pa_prefill over the whole batch (K/V already in the pool)."""
+    import dataclasses
+    cfg = wl.PREFILL if not args.block_size else dataclasses.replace(wl.PREFILL, block_size=args.block_size)
+    t0 = time.perf_counter()
+    w = wl.make_prefill_workload(cfg, contiguous=args.contiguous)
+    gen_s = time.perf_counter() - t0
+    et = cfg.etype
+    q = pb.to_device(w.q, et, dev)
+    out = torch.empty(q.shape, dtype=q.dtype, device=dev)
+    qs, kc, vc = pb.int32_to_device(w.q_start, dev), pb.to_device(w.k_cache, et, dev), pb.to_device(w.v_cache, et, dev)
+    bt, cl = pb.int32_to_device(w.block_tables, dev), pb.int32_to_device(w.context_lens, dev)
+
+    def step():
+        pb.pa_prefill(out, q, qs, kc, vc, bt, cl, cfg.scale)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    call_ms = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step = elapsed * 1e3 / args.steps
+    flops = w.flops()
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (call_ms * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[et]
+    result = {
+        "metric": "prompt-phase attention over the paged cache: achieved TFLOP/s at 1 GPU",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": et,
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT["prefill"], "num_seqs": cfg.num_seqs, "total_queries": w.total_q,
+                   "max_context_len": int(w.context_lens.max()), "block_size": cfg.block_size,
+                   "pool": "contiguous" if args.contiguous else "shuffled"},
+        "flops": flops,
+        "flops_rule": "4 * head_dim per (query head, query, visible cached token): QK and PV products",
+        "tokens_per_s": round(w.total_q / (ms_per_step * 1e-3), 1),
+        "prefill": {"call": "pa_prefill", "avg_ms": round(call_ms, 5), "kv_bytes": w.kv_bytes(),
+                    "timed": "HIP events on the launch stream around the timed steps, divided by the steps"},
+        "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(achieved, 1), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic_for("prefill_kernel", "prefill")},
+        "input_generation_s": round(gen_s, 2),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = prefill_cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -334,6 +433,8 @@ def main() -> int:
     if args.swap_sweep:
         print(json.dumps({"swap_sweep": swap_sweep(torch, pb, args.swap_sweep, 5)}), flush=True)
         return 0
+    if args.workload == "prefill":
+        return prefill_main(args, torch, pb, wl, dev)
     if args.workload in ("parallel_sampling", "beam_search", "shared_prefix") and (args.block_size or args.contiguous):
         raise SystemExit("--block-size/--contiguous apply to the drawn-length workloads")
     if args.workload == "parallel_sampling":
