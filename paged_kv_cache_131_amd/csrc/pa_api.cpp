@@ -248,7 +248,8 @@ pa_status pa_prefill(void* out, const void* q, const int32_t* q_start, int32_t t
   p.qt = 16 / group;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.out_dtype = out_dtype;
-  const long long tiles = ((long long)total_q + p.qt - 1) / p.qt + num_seqs;
+  const int qb = pa::prefill_queries_per_tile(group);
+  const long long tiles = ((long long)total_q + qb - 1) / qb + num_seqs;
   if (tiles > INT_MAX) return PA_ERR_UNSUPPORTED;
   const int elem = dtype == PA_F16 ? pa::kF16 : pa::kBF16;
   const hipError_t e = pa::launch_prefill(p, elem, head_dim, (unsigned)tiles, static_cast<hipStream_t>(stream));

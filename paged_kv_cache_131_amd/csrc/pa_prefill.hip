@@ -4,13 +4,23 @@
 // phase: all prompt tokens at once, a matrix-matrix product), K and V found
 // through the sequence's block table.
 //
-// One wave per (tile, KV head): a tile is qt consecutive queries of one
-// sequence, and the 16 columns of the MFMA tiles hold its (query, head) pairs
-// of the KV head's group. The wave walks the context in 32-token chunks up to
-// the tile's last position with an fp32 online softmax; a chunk's K rows and
-// V columns are 16-byte loads straight from the pool, as in decode, and the
-// causal limit is a per-column mask. P enters PV as a rounded 16-bit part plus
-// its rounding residual (two MFMAs), which keeps the products fp32-accurate.
+// A workgroup of four waves takes a tile of consecutive queries of one
+// sequence and one KV head. The context is walked in 32-token chunks up to the
+// tile's last position; each chunk's K rows and V columns are brought into a
+// three-stage LDS ring by direct global-to-LDS loads, a quarter per wave, two
+// chunks ahead of use, so the four waves share one copy of every K/V byte.
+// Each wave owns NG groups of 16 MFMA columns, a column being one (query, head)
+// pair of the KV head's group; QK^T and PV are 16x16x32 MFMAs whose operands
+// come from the ring, with an fp32 online softmax between them and the causal
+// limit as a per-column mask. P enters PV as a rounded 16-bit part plus its
+// rounding residual (two MFMAs), which keeps the products fp32-accurate.
+//
+// LDS layout of one stage, in 16-byte units (swizzled so that the 16 lanes of
+// an MFMA operand read fall in distinct banks):
+//   K: token t of the chunk, head-dim segment s (8 elements) at unit
+//      t * D/8 + (s ^ fk(t));
+//   V, after K's 32*D/8 units: channel c, token group u (8 tokens) at unit
+//      c * 4 + (u ^ fv(c)).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -21,23 +31,264 @@
 namespace pa {
 namespace {
 
-// Tiles of sequence s; a sequence whose rows do not lie inside
-// [0, total_q) in order gets none.
-__device__ __forceinline__ int seq_tiles(const PrefillParams& p, int s) {
-  const int a = p.q_start[s], b = p.q_start[s + 1];
-  return (a >= 0 && b > a && b <= p.total_q) ? (b - a + p.qt - 1) / p.qt : 0;
+constexpr int kPrefillWaves = 4;
+constexpr int kPrefillGroups = 1;  // 16-column groups per wave
+constexpr float kRescaleSlack = 8.f;  // log2 units
+
+typedef __attribute__((address_space(3))) const void lds_void;
+
+// One LDS array per ring stage.
+template <int S, int D>
+__device__ __forceinline__ uint16_t* stage_buf() {
+  __shared__ __attribute__((aligned(16))) uint16_t buf[2 * kChunk * D];
+  return buf;
 }
 
-template <int E, int D>
-__global__ __launch_bounds__(64) void prefill_kernel(PrefillParams p) {
+// 16 bytes per lane from global memory straight into LDS: lane l of the wave
+// writes bytes [16 l, 16 l + 16) from LDS byte address `lds` on (M0 holds the
+// wave's base). Issued as inline assembly so that the compiler does not track
+// it: its own waits would otherwise drain every ring load before any LDS
+// read. The ring's explicit waits (wait_and_barrier) cover these loads.
+// M0 is reserved to the compiler, which warns that it may not honour the
+// clobber; no code it generates for this kernel reads M0, and each load sets
+// it itself.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void load_lds16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+}
+// The same from a wave-uniform base plus a 32-bit per-lane byte offset.
+__device__ __forceinline__ void load_lds16(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void*)p);
+}
+
+__device__ __forceinline__ int k_swizzle(int t, int D) { return ((t & 3) | ((t >> 1) & 12)) & (D / 8 - 1); }
+__device__ __forceinline__ int v_swizzle(int c) { return (c >> 2) & 3; }
+
+// Wait until at most N of this wave's vector memory operations are in flight,
+// then meet the other waves; LDS accesses are not moved across it.
+template <int N>
+__device__ __forceinline__ void wait_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Tiles of sequence s; a sequence whose rows do not lie inside
+// [0, total_q) in order gets none.
+__device__ __forceinline__ int seq_tiles(const PrefillParams& p, int s, int qb) {
+  const int a = p.q_start[s], b = p.q_start[s + 1];
+  return (a >= 0 && b > a && b <= p.total_q) ? (b - a + qb - 1) / qb : 0;
+}
+
+template <int E, int D, int NG>
+struct PrefillTile {
   using Tr = ElemT<E>;
   using op8 = typename Tr::op8;
   using scalar = typename Tr::scalar;
   using raw = typename Tr::raw;
-  constexpr int MQ = D / 32;  // QK k-steps
-  constexpr int NT = D / 16;  // PV column tiles
-  const int lane = threadIdx.x, col = lane & 15, grp = lane >> 4;
-  const int kvh = blockIdx.y, g = p.group, qt = p.qt, Hq = p.num_heads, Hkv = p.num_kv_heads;
+  static constexpr int MQ = D / 32;                        // QK k-steps
+  static constexpr int NT = D / 16;                        // PV column tiles
+  static constexpr int KU = kChunk * D / 8;                // 16-byte units of K (and of V) per chunk
+  static constexpr int LPW = 2 * KU / 64 / kPrefillWaves;  // direct loads per wave per chunk
+
+  const PrefillParams& p;
+  int lane, col, grp, wave, kvh;
+  const int32_t* tbl;
+  int lbl, p_last, nch;
+  // ring loads: this wave's instructions, per lane the byte offset inside the
+  // block (without the chunk's offset) and, for V, which of the chunk's blocks
+  uint32_t block_bytes;
+  uint32_t k_off[LPW / 2], v_off[LPW / 2];
+  int k_blk[LPW / 2], v_blk[LPW / 2];
+  int pos_w, last_w;  // first position and last chunk of this wave's queries (-1: none)
+  op8 qop[NG][MQ];
+  int pcol[NG];
+  f32x4 o[NG][NT];
+  float m_run[NG], l_run[NG];
+
+  __device__ explicit PrefillTile(const PrefillParams& pp) : p(pp) {}
+
+  // Loop-invariant parts of the ring loads. K instruction i covers whole
+  // tokens (64 units, 4 or 8 tokens), so it reads one block; a V instruction
+  // spans the chunk's 32 tokens, so each lane finds its own block.
+  __device__ void init_loads() {
+    const int lg = p.log2_block, B = p.block_size;
+    block_bytes = (uint32_t)p.num_kv_heads * (uint32_t)B * D * 2u;
+#pragma unroll
+    for (int ii = 0; ii < LPW / 2; ++ii) {
+      const int i = wave * (LPW / 2) + ii;
+      const int u = i * 64 + lane;
+      const int t = u / (D / 8);
+      const int seg = (u % (D / 8)) ^ k_swizzle(t, D);
+      k_off[ii] = (uint32_t)(((kvh * B + (t & (B - 1))) * D + 8 * seg) * 2);
+      k_blk[ii] = __builtin_amdgcn_readfirstlane((i * 64 / (D / 8)) >> lg);
+      const int c = u >> 2;
+      const int tg = (u & 3) ^ v_swizzle(c);
+      v_off[ii] = (uint32_t)(((kvh * D + c) * B + ((8 * tg) & (B - 1))) * 2);
+      v_blk[ii] = (8 * tg) >> lg;
+    }
+  }
+
+  // Direct loads of the chunk starting at `cs` into stage S: this wave's
+  // instructions i write units i*64 + lane.
+  template <int S>
+  __device__ void issue(int cs, const ChunkIds& c) {
+    const int last = p.num_blocks - 1;
+    const int id0 = min(max(c.id0, 0), last), id1 = min(max(c.id1, 0), last);
+    const int id2 = min(max(c.id2, 0), last), id3 = min(max(c.id3, 0), last);
+    const uint32_t in_block = (uint32_t)(cs & (p.block_size - 1));  // chunk's first token inside its block
+    const char* kc = static_cast<const char*>(p.k_cache) + (size_t)in_block * (D * 2);
+    const char* vc = static_cast<const char*>(p.v_cache) + (size_t)in_block * 2;
+    const uint16_t* st = stage_buf<S, D>();
+#pragma unroll
+    for (int ii = 0; ii < LPW / 2; ++ii) {
+      const int i = wave * (LPW / 2) + ii;
+      const int kb = k_blk[ii];
+      const int id = kb == 0 ? id0 : (kb == 1 ? id1 : (kb == 2 ? id2 : id3));
+      load_lds16(kc + (size_t)id * block_bytes, k_off[ii], lds_address(st + i * 512));
+    }
+#pragma unroll
+    for (int ii = 0; ii < LPW / 2; ++ii) {
+      const int i = wave * (LPW / 2) + ii;
+      const int vb = v_blk[ii];
+      const int id = vb == 0 ? id0 : (vb == 1 ? id1 : (vb == 2 ? id2 : id3));
+      load_lds16(vc + (size_t)id * block_bytes + v_off[ii], lds_address(st + kChunk * D + i * 512));
+    }
+  }
+
+  template <int S>
+  __device__ void compute(int cs) {
+    const uint16_t* st = stage_buf<S, D>();
+    // K operand: row `col` of the MFMA is token 8*(col/4) + 4c + col%4, so the
+    // scores land where PV wants its P operand
+    u32x4 ka[2][MQ];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int t = 8 * (col >> 2) + 4 * c + (col & 3);
+#pragma unroll
+      for (int m = 0; m < MQ; ++m) {
+        const int seg = (4 * m + grp) ^ k_swizzle(t, D);
+        ka[c][m] = *reinterpret_cast<const u32x4*>(st + (t * (D / 8) + seg) * 8);
+      }
+    }
+    float sv[NG][8];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      f32x4 sc0 = f32x4{0.f, 0.f, 0.f, 0.f}, sc1 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < MQ; ++m) {
+        sc0 = mfma_16x16x32(__builtin_bit_cast(op8, ka[0][m]), qop[gi][m], sc0);
+        sc1 = mfma_16x16x32(__builtin_bit_cast(op8, ka[1][m]), qop[gi][m], sc1);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sv[gi][i] = sc0[i] * p.scale_log2;
+        sv[gi][4 + i] = sc1[i] * p.scale_log2;
+      }
+    }
+    // V operand: tokens cs + 8*grp .. +7 of channel col + 16 j
+    u32x4 vr[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int c = col + 16 * j;
+      vr[j] = *reinterpret_cast<const u32x4*>(st + kChunk * D + (c * 4 + (grp ^ v_swizzle(c))) * 8);
+    }
+    if (cs + kChunk - 1 > p_last) {  // tokens past the tile's last position: no V
+      const int nvalid = p_last + 1 - (cs + 8 * grp);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) vr[j] = Tr::keep_first(vr[j], nvalid);
+    }
+    const bool masked = cs + kChunk - 1 > pos_w;
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      if (masked) {  // causal limit inside this chunk
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sv[gi][e] = (cs + 8 * grp + e <= pcol[gi]) ? sv[gi][e] : kNegInf;
+      }
+      float cmax = kNegInf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) cmax = fmaxf(cmax, sv[gi][e]);
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+      // The reference maximum moves only when a score exceeds it by more than
+      // 2^8: exponentials stay <= 256 and the output is rescaled rarely. The
+      // result does not depend on the reference (it cancels in o / l).
+      const bool grow = cmax > m_run[gi] + kRescaleSlack;
+      if (__any(grow)) {
+        const float m_new = grow ? cmax : m_run[gi];
+        const float alpha = fast_exp2(m_run[gi] - m_new);
+        l_run[gi] *= alpha;
+        m_run[gi] = m_new;
+        // output rows of this lane are columns 4*grp+i; their factor lives in lane 4*grp+i
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float ai = __shfl(alpha, 4 * grp + i);
+#pragma unroll
+          for (int j = 0; j < NT; ++j) o[gi][j][i] *= ai;
+        }
+      }
+      float pe[8], psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pe[e] = fast_exp2(sv[gi][e] - m_run[gi]);
+        psum += pe[e];
+      }
+      l_run[gi] += psum;
+      op8 phi, plo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const scalar hi = static_cast<scalar>(pe[e]);
+        phi[e] = hi;
+        plo[e] = static_cast<scalar>(pe[e] - static_cast<float>(hi));
+      }
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        o[gi][j] = mfma_16x16x32(phi, __builtin_bit_cast(op8, vr[j]), o[gi][j]);
+        o[gi][j] = mfma_16x16x32(plo, __builtin_bit_cast(op8, vr[j]), o[gi][j]);
+      }
+    }
+  }
+
+  // One chunk of the ring: stage S holds chunk ci. False past the last chunk.
+  template <int S>
+  __device__ bool step(int ci, ChunkIds& ids_next) {
+    if (ci >= nch) return false;
+    if (ci + 1 < nch) {
+      wait_and_barrier<LPW>();  // this wave's loads of chunk ci landed; chunk ci+1's may fly
+    } else {
+      wait_and_barrier<0>();
+    }
+    // every wave is past chunk ci-1, whose stage takes chunk ci+2
+    if (ci + 2 < nch) {
+      const ChunkIds ids = ids_next;
+      ids_next = load_chunk_ids(tbl, min(ci + 3, nch - 1) * kChunk, lbl, p.log2_block);
+      this->template issue<(S + 2) % 3>((ci + 2) * kChunk, ids);
+    }
+    if (ci <= last_w) this->template compute<S>(ci * kChunk);
+    return true;
+  }
+};
+
+template <int E, int D, int NG>
+__global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(PrefillParams p) {
+  using Tile = PrefillTile<E, D, NG>;
+  using op8 = typename Tile::op8;
+  using raw = typename Tile::raw;
+  constexpr int MQ = Tile::MQ, NT = Tile::NT;
+  Tile T(p);
+  T.lane = threadIdx.x & 63;
+  T.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  T.col = T.lane & 15;
+  T.grp = T.lane >> 4;
+  T.kvh = blockIdx.y;
+  const int lane = T.lane, col = T.col, grp = T.grp, wave = T.wave;
+  const int g = p.group, qt = p.qt, Hq = p.num_heads;
+  const int qw = NG * qt, qb = kPrefillWaves * qw;  // queries per wave, per tile
 
   // tile map: every wave scans the query counts (the longest tiles, the last
   // of each sequence, are handed out first)
@@ -45,18 +296,18 @@ __global__ __launch_bounds__(64) void prefill_kernel(PrefillParams p) {
   const int per = (S + 63) >> 6;
   const int s_lo = min(lane * per, S), s_hi = min(s_lo + per, S);
   int mine = 0;
-  for (int s = s_lo; s < s_hi; ++s) mine += seq_tiles(p, s);
+  for (int s = s_lo; s < s_hi; ++s) mine += seq_tiles(p, s, qb);
   int incl = mine;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
     const int t = __shfl_up(incl, d);
     if (lane >= d) incl += t;
   }
-  const int T = __shfl(incl, 63);
+  const int ntiles = __shfl(incl, 63);
   const int excl = incl - mine;
   const int x = blockIdx.x;
-  if (x >= T) return;
-  const int tile = T - 1 - x;
+  if (x >= ntiles) return;
+  const int tile = ntiles - 1 - x;
   const unsigned long long ball = __ballot(tile >= excl && tile < incl);
   if (ball == 0) return;  // counts past int range only
   const int owner = __builtin_ctzll(ball);
@@ -64,7 +315,7 @@ __global__ __launch_bounds__(64) void prefill_kernel(PrefillParams p) {
   if (lane == owner) {
     int c = excl;
     for (int s = s_lo; s < s_hi; ++s) {
-      const int nt = seq_tiles(p, s);
+      const int nt = seq_tiles(p, s, qb);
       if (tile < c + nt) {
         s_found = s;
         k_found = tile - c;
@@ -75,164 +326,102 @@ __global__ __launch_bounds__(64) void prefill_kernel(PrefillParams p) {
   }
   const int s = __builtin_amdgcn_readfirstlane(__shfl(s_found, owner));
   const int k = __builtin_amdgcn_readfirstlane(__shfl(k_found, owner));
-  if (k >= seq_tiles(p, s)) return;
+  if (k >= seq_tiles(p, s, qb)) return;
   const int q0 = p.q_start[s], n = p.q_start[s + 1] - q0, L = p.context_lens[s];
-  if (n > L || L > (p.max_blocks_per_seq << p.log2_block)) return;  // precondition violated
-  const int j0 = k * qt, nq = min(qt, n - j0);
-  const int pos0 = L - n + j0, p_max = pos0 + nq - 1;
+  // precondition violated: the whole workgroup leaves together
+  if (n > L || L > (p.max_blocks_per_seq << p.log2_block)) return;
+  const int j0 = k * qb, nq = min(qb, n - j0);
+  const int pos0 = L - n + j0;
+  T.p_last = pos0 + nq - 1;
+  T.nch = T.p_last / kChunk + 1;
+  T.tbl = p.block_tables + (size_t)s * p.max_blocks_per_seq;
+  T.lbl = T.p_last >> p.log2_block;
+  const int nq_w = min(max(nq - wave * qw, 0), qw);
+  T.pos_w = pos0 + wave * qw;
+  T.last_w = nq_w > 0 ? (T.pos_w + nq_w - 1) / kChunk : -1;
+  T.init_loads();
 
-  // column (query qi, head hh); columns past the tile read q = 0 at p_max
+  // columns (query qi, head hh) of each group; columns past the tile read q = 0
   const int qi = col / g, hh = col - qi * g;
-  const bool cvalid = qi < nq;
-  const int pcol = cvalid ? pos0 + qi : p_max;
-  op8 qop[MQ];
-  {
-    const raw* qrow = static_cast<const raw*>(p.q) + ((size_t)(q0 + j0 + (cvalid ? qi : 0)) * Hq + kvh * g + hh) * D;
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    const int jq = gi * qt + qi;  // query within the wave
+    const bool cvalid = qi < qt && jq < nq_w;
+    T.pcol[gi] = cvalid ? T.pos_w + jq : T.pos_w + nq_w - 1;
+    const raw* qrow = static_cast<const raw*>(p.q) +
+                      ((size_t)(q0 + j0 + wave * qw + (cvalid ? jq : 0)) * Hq + T.kvh * g + hh) * D;
 #pragma unroll
     for (int m = 0; m < MQ; ++m) {
       u32x4 w = {0u, 0u, 0u, 0u};
       if (cvalid) w = load16(qrow + 32 * m + 8 * grp);
-      qop[m] = __builtin_bit_cast(op8, w);
+      T.qop[gi][m] = __builtin_bit_cast(op8, w);
     }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) T.o[gi][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    T.m_run[gi] = kNegInf;
+    T.l_run[gi] = 0.f;
   }
+  // the q loads complete here, so the ring's waits count ring loads only; the
+  // builtin form tells the compiler they are done
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
-  const int lg = p.log2_block, B = p.block_size;
-  const int32_t* tbl = p.block_tables + (size_t)s * p.max_blocks_per_seq;
-  const int lbl = p_max >> lg;
-  const int nch = p_max / kChunk + 1;
-  const raw* __restrict__ kc = static_cast<const raw*>(p.k_cache);
-  const raw* __restrict__ vc = static_cast<const raw*>(p.v_cache);
-
-  u32x4 ka[2][MQ], vr[NT];
-  auto load_k = [&](int cs, const ChunkIds& ids) {
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int tok = cs + 8 * (col >> 2) + 4 * c + (col & 3);
-      const int phys = pick_block(ids, tok, lg, lbl, p.num_blocks);
-      const raw* row = kc + (((size_t)phys * Hkv + kvh) * B + (tok & (B - 1))) * D + 8 * grp;
-#pragma unroll
-      for (int m = 0; m < MQ; ++m) ka[c][m] = load16(row + 32 * m);
-    }
-  };
-  auto load_v = [&](int cs, const ChunkIds& ids) {
-    const int tv = cs + 8 * grp;
-    const int physv = pick_block(ids, tv, lg, lbl, p.num_blocks);
-    const raw* vb = vc + (((size_t)physv * Hkv + kvh) * D + col) * B + (tv & (B - 1));
-#pragma unroll
-    for (int j = 0; j < NT; ++j) vr[j] = load16(vb + (size_t)16 * j * B);
-  };
-
-  ChunkIds ids1 = load_chunk_ids(tbl, min(1, nch - 1) * kChunk, lbl, lg);
+  const int nch = T.nch;
   {
-    const ChunkIds ids0 = load_chunk_ids(tbl, 0, lbl, lg);
-    load_k(0, ids0);
-    load_v(0, ids0);
+    const ChunkIds ids0 = load_chunk_ids(T.tbl, 0, T.lbl, p.log2_block);
+    T.template issue<0>(0, ids0);
   }
-  f32x4 o[NT];
-#pragma unroll
-  for (int j = 0; j < NT; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegInf, l_run = 0.f;
-
-  for (int ci = 0; ci < nch; ++ci) {
-    const int cs = ci * kChunk;
-    const int cs_next = min(ci + 1, nch - 1) * kChunk;
-    const ChunkIds ids2 = load_chunk_ids(tbl, min(ci + 2, nch - 1) * kChunk, lbl, lg);
-    // scores: the lane holds tokens cs + 8*grp + 0..7 of column `col`
-    f32x4 sc0 = f32x4{0.f, 0.f, 0.f, 0.f}, sc1 = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int m = 0; m < MQ; ++m) {
-      sc0 = mfma_16x16x32(__builtin_bit_cast(op8, ka[0][m]), qop[m], sc0);
-      sc1 = mfma_16x16x32(__builtin_bit_cast(op8, ka[1][m]), qop[m], sc1);
-    }
-    load_k(cs_next, ids1);  // unconditional: the last chunk re-reads itself
-    float sv[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sv[i] = sc0[i] * p.scale_log2;
-      sv[4 + i] = sc1[i] * p.scale_log2;
-    }
-    if (cs + kChunk - 1 > pos0) {  // causal limit inside this chunk
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sv[e] = (cs + 8 * grp + e <= pcol) ? sv[e] : kNegInf;
-    }
-    float cmax = kNegInf;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) cmax = fmaxf(cmax, sv[e]);
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-    const float m_new = fmaxf(m_run, cmax);
-    const float alpha = fast_exp2(m_run - m_new);
-    float pe[8];
-    float psum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pe[e] = fast_exp2(sv[e] - m_new);
-      psum += pe[e];
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    if (__any(alpha != 1.f)) {
-      // output rows of this lane are columns 4*grp+i; their factor lives in lane 4*grp+i
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float ai = __shfl(alpha, 4 * grp + i);
-#pragma unroll
-        for (int j = 0; j < NT; ++j) o[j][i] *= ai;
-      }
-    }
-    op8 phi, plo;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const scalar hi = static_cast<scalar>(pe[e]);
-      phi[e] = hi;
-      plo[e] = static_cast<scalar>(pe[e] - static_cast<float>(hi));
-    }
-    if (cs + kChunk - 1 > p_max) {  // tokens past the tile's last position: no V
-      const int nvalid = p_max + 1 - (cs + 8 * grp);
-#pragma unroll
-      for (int j = 0; j < NT; ++j) vr[j] = Tr::keep_first(vr[j], nvalid);
-    }
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      o[j] = mfma_16x16x32(phi, __builtin_bit_cast(op8, vr[j]), o[j]);
-      o[j] = mfma_16x16x32(plo, __builtin_bit_cast(op8, vr[j]), o[j]);
-    }
-    load_v(cs_next, ids1);
-    ids1 = ids2;
+  ChunkIds ids_next = load_chunk_ids(T.tbl, min(2, nch - 1) * kChunk, T.lbl, p.log2_block);
+  if (nch > 1) {
+    const ChunkIds ids1 = load_chunk_ids(T.tbl, kChunk, T.lbl, p.log2_block);
+    T.template issue<1>(kChunk, ids1);
+  }
+  for (int ci = 0;; ci += 3) {
+    if (!T.template step<0>(ci, ids_next)) break;
+    if (!T.template step<1>(ci + 1, ids_next)) break;
+    if (!T.template step<2>(ci + 2, ids_next)) break;
   }
 
   // rows of this lane: columns r = 4*grp + i, i.e. query r / g, head r % g
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 4 * grp + i;
-    const float lr = __shfl(l_tot, r);
-    const int qr = r / g;
-    if (qr < nq) {
-      const size_t base = ((size_t)(q0 + j0 + qr) * Hq + kvh * g + (r - qr * g)) * D + col;
+  for (int gi = 0; gi < NG; ++gi) {
+    float l_tot = T.l_run[gi] + __shfl_xor(T.l_run[gi], 16);
+    l_tot += __shfl_xor(l_tot, 32);
 #pragma unroll
-      for (int j = 0; j < NT; ++j) store_out(p.out, base + 16 * j, o[j][i] / lr, p.out_dtype);
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * grp + i;
+      const float lr = __shfl(l_tot, r);
+      const int qr = r / g;
+      const int jq = gi * qt + qr;
+      if (qr < qt && jq < nq_w) {
+        const size_t base = ((size_t)(q0 + j0 + wave * qw + jq) * Hq + T.kvh * g + (r - qr * g)) * D + col;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) store_out(p.out, base + 16 * j, T.o[gi][j][i] / lr, p.out_dtype);
+      }
     }
   }
 }
 
 const void* prefill_fn(int elem, int head_dim) {
-  if (elem == kBF16) return head_dim == 64 ? reinterpret_cast<const void*>(&prefill_kernel<kBF16, 64>)
-                                           : reinterpret_cast<const void*>(&prefill_kernel<kBF16, 128>);
-  if (elem == kF16) return head_dim == 64 ? reinterpret_cast<const void*>(&prefill_kernel<kF16, 64>)
-                                          : reinterpret_cast<const void*>(&prefill_kernel<kF16, 128>);
+  constexpr int G = kPrefillGroups;
+  if (elem == kBF16) return head_dim == 64 ? reinterpret_cast<const void*>(&prefill_kernel<kBF16, 64, G>)
+                                           : reinterpret_cast<const void*>(&prefill_kernel<kBF16, 128, G>);
+  if (elem == kF16) return head_dim == 64 ? reinterpret_cast<const void*>(&prefill_kernel<kF16, 64, G>)
+                                          : reinterpret_cast<const void*>(&prefill_kernel<kF16, 128, G>);
   return nullptr;
 }
 
 }  // namespace
+
+int prefill_queries_per_tile(int group) { return kPrefillWaves * kPrefillGroups * (16 / group); }
 
 hipError_t launch_prefill(const PrefillParams& p, int elem, int head_dim, unsigned tiles, hipStream_t stream) {
   const void* fn = prefill_fn(elem, head_dim);
   if (!fn) return hipErrorInvalidDeviceFunction;
   PrefillParams args = p;
   void* kargs[] = {&args};
-  return hipLaunchKernel(fn, dim3(tiles, (unsigned)p.num_kv_heads, 1), dim3(64, 1, 1), kargs, 0, stream);
+  return hipLaunchKernel(fn, dim3(tiles, (unsigned)p.num_kv_heads, 1), dim3(64 * kPrefillWaves, 1, 1), kargs, 0,
+                         stream);
 }
 
 }  // namespace pa
