@@ -25,8 +25,12 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, vendor figure
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_131_amd", "csrc", f)
-                  for f in ("pa_kernels.hip", "pa_prefill.hip", "pa_api.cpp", "pa_internal.h", "pa_device.h")]
+_CSRC = os.path.join(ROOT, "paged_kv_cache_131_amd", "csrc")
+# sources whose change invalidates a recorded traffic figure, per workload kind
+KERNEL_SOURCES = {
+    "decode": [os.path.join(_CSRC, f) for f in ("pa_kernels.hip", "pa_api.cpp", "pa_internal.h", "pa_device.h")],
+    "prefill": [os.path.join(_CSRC, f) for f in ("pa_prefill.hip", "pa_api.cpp", "pa_internal.h", "pa_device.h")],
+}
 
 WORKLOAD_TEXT = {
     "llama3_8b": "Llama-3-8B-shaped GQA decode: 256 seqs, 32 q / 8 kv heads, head_dim 128, block 16, bf16, "
@@ -49,9 +53,9 @@ WORKLOAD_TEXT = {
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}   # MI355X dense matrix peak
 
 
-def kernel_hash() -> str:
+def kernel_hash(workload: str) -> str:
     h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
+    for path in KERNEL_SOURCES["prefill" if workload == "prefill" else "decode"]:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -113,7 +117,7 @@ def traffic_for(kernel: str, workload: str):
     except (OSError, ValueError):
         return None
     entry = rec.get(workload, {})
-    if entry.get("kernel_hash") != kernel_hash():
+    if entry.get("kernel_hash") != kernel_hash(workload):
         return None
     return entry.get(kernel)
 
@@ -150,7 +154,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, workload: str, calibratio
     kernels = {k: {"fetch_kib_per_launch": round(fetch[k], 1), "write_kib_per_launch": round(write[k], 1),
                    "traffic_bytes": int(round((fetch[k] * fs + write[k] * ws) * 1024))}
                for k in fetch if k in write}
-    entry = {"kernel_hash": kernel_hash(), "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
+    entry = {"kernel_hash": kernel_hash(workload), "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
              "calibration": f"one {calibration_mib} MiB device-to-device torch copy (__amd_rocclr_copyBuffer) in "
                             f"the same run: FETCH_SIZE {fcal:.1f} KiB, WRITE_SIZE {wcal:.1f} KiB",
              "kernels": kernels}
@@ -300,6 +304,18 @@ def swap_sweep(torch, pb, total_mib: int, reps: int) -> dict:
     return res
 
 
+def calibration_copy(args, torch, dev) -> None:
+    """One plain device copy of known size, run before the timed launches, for
+    the traffic counters' calibration."""
+    if args.calibration_copy_mib:
+        n = args.calibration_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+
 def prefill_cpu_baseline(w, budget_s: float) -> dict:
     """The oracle on the shortest prompts first until the time budget is
     spent (at least one), BLAS pinned to one thread."""
@@ -340,6 +356,7 @@ def prefill_main(args, torch, pb, wl, dev) -> int:
     out = torch.empty(q.shape, dtype=q.dtype, device=dev)
     qs, kc, vc = pb.int32_to_device(w.q_start, dev), pb.to_device(w.k_cache, et, dev), pb.to_device(w.v_cache, et, dev)
     bt, cl = pb.int32_to_device(w.block_tables, dev), pb.int32_to_device(w.context_lens, dev)
+    calibration_copy(args, torch, dev)
 
     def step():
         pb.pa_prefill(out, q, qs, kc, vc, bt, cl, cfg.scale)
@@ -457,13 +474,7 @@ def main() -> int:
     out = torch.empty(q.shape, dtype=torch.float32, device=dev)
     max_len = c.max_len
 
-    if args.calibration_copy_mib:
-        n = args.calibration_copy_mib << 20
-        src = torch.ones(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    calibration_copy(args, torch, dev)
 
     fused = not args.two_calls
     if fused and args.algo != "auto":

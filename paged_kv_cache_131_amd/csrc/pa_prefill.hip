@@ -50,10 +50,8 @@ __device__ __forceinline__ uint16_t* stage_buf() {
 // it: its own waits would otherwise drain every ring load before any LDS
 // read. The ring's explicit waits (wait_and_barrier) cover these loads.
 // M0 is reserved to the compiler, which warns that it may not honour the
-// clobber; no code it generates for this kernel reads M0, and each load sets
-// it itself.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
+// clobber (the build silences that warning for this file); no code it
+// generates for this kernel reads M0, and each load sets it itself.
 __device__ __forceinline__ void load_lds16(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
 }
@@ -62,7 +60,6 @@ __device__ __forceinline__ void load_lds16(const void* base, uint32_t off, uint3
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
                : "memory", "m0");
 }
-#pragma clang diagnostic pop
 
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void*)p);
@@ -285,7 +282,15 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(PrefillPara
   T.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   T.col = T.lane & 15;
   T.grp = T.lane >> 4;
-  T.kvh = blockIdx.y;
+  // XCD-aware order: the hardware hands workgroup L = x + y * X to XCD L % 8.
+  // Each XCD takes a contiguous range of work items w = kvh * X + x, so the
+  // tiles it runs together (consecutive tiles of one sequence and KV head)
+  // share their K/V in that XCD's L2.
+  const unsigned X = gridDim.x, N = X * gridDim.y;
+  const unsigned lin = blockIdx.x + blockIdx.y * X;
+  const unsigned xcd = lin % 8, q8 = N / 8, rem = N % 8;
+  const unsigned w = xcd * q8 + min(xcd, rem) + lin / 8;
+  T.kvh = (int)(w / X);
   const int lane = T.lane, col = T.col, grp = T.grp, wave = T.wave;
   const int g = p.group, qt = p.qt, Hq = p.num_heads;
   const int qw = NG * qt, qb = kPrefillWaves * qw;  // queries per wave, per tile
@@ -305,7 +310,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(PrefillPara
   }
   const int ntiles = __shfl(incl, 63);
   const int excl = incl - mine;
-  const int x = blockIdx.x;
+  const int x = (int)(w % X);
   if (x >= ntiles) return;
   const int tile = ntiles - 1 - x;
   const unsigned long long ball = __ballot(tile >= excl && tile < incl);
