@@ -246,7 +246,10 @@ pa_status pa_prefill(void* out, const void* q, const int32_t* q_start, int32_t t
   p.num_blocks = num_blocks;
   p.max_blocks_per_seq = max_blocks_per_seq;
   p.qt = 16 / group;
-  p.scale_log2 = scale * 1.4426950408889634f;
+  // the kernel scales by a positive factor: the sign goes onto q (exact), and
+  // a zero scale becomes q = 0 (every score 0) with factor 1
+  p.q_sign = scale > 0.f ? 1 : (scale < 0.f ? -1 : 0);
+  p.scale_log2 = (scale != 0.f ? std::fabs(scale) : 1.f) * 1.4426950408889634f;
   p.out_dtype = out_dtype;
   const int qb = pa::prefill_queries_per_tile(group);
   const long long tiles = ((long long)total_q + qb - 1) / qb + num_seqs;

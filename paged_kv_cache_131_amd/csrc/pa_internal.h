@@ -86,7 +86,8 @@ struct PrefillParams {
   int32_t num_blocks;
   int32_t max_blocks_per_seq;
   int32_t qt;                  // query tokens per tile: the 16 MFMA columns hold qt x group (query, head) pairs
-  float scale_log2;
+  float scale_log2;             // |scale| * log2(e), > 0
+  int32_t q_sign;               // sign of the scale: q enters as q, -q, or 0
   int32_t out_dtype;
 };
 

@@ -75,6 +75,22 @@ __device__ __forceinline__ void wait_and_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// Max and sum of x over lanes l, l^16, l^32, l^48 (the four lanes holding one
+// MFMA column), by lane-swap instructions.
+__device__ __forceinline__ float max_over_column(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float sum_over_column(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Tiles of sequence s; a sequence whose rows do not lie inside
 // [0, total_q) in order gets none.
 __device__ __forceinline__ int seq_tiles(const PrefillParams& p, int s, int qb) {
@@ -183,9 +199,9 @@ struct PrefillTile {
         sc1 = mfma_16x16x32(__builtin_bit_cast(op8, ka[1][m]), qop[gi][m], sc1);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sv[gi][i] = sc0[i] * p.scale_log2;
-        sv[gi][4 + i] = sc1[i] * p.scale_log2;
+      for (int i = 0; i < 4; ++i) {  // raw scores; the positive scale is applied in the exponent
+        sv[gi][i] = sc0[i];
+        sv[gi][4 + i] = sc1[i];
       }
     }
     // V operand: tokens cs + 8*grp .. +7 of channel col + 16 j
@@ -210,8 +226,7 @@ struct PrefillTile {
       float cmax = kNegInf;
 #pragma unroll
       for (int e = 0; e < 8; ++e) cmax = fmaxf(cmax, sv[gi][e]);
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+      cmax = max_over_column(cmax) * p.scale_log2;
       // The reference maximum moves only when a score exceeds it by more than
       // 2^8: exponentials stay <= 256 and the output is rescaled rarely. The
       // result does not depend on the reference (it cancels in o / l).
@@ -232,7 +247,7 @@ struct PrefillTile {
       float pe[8], psum = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        pe[e] = fast_exp2(sv[gi][e] - m_run[gi]);
+        pe[e] = fast_exp2(__builtin_fmaf(sv[gi][e], p.scale_log2, -m_run[gi]));
         psum += pe[e];
       }
       l_run[gi] += psum;
@@ -358,7 +373,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(PrefillPara
 #pragma unroll
     for (int m = 0; m < MQ; ++m) {
       u32x4 w = {0u, 0u, 0u, 0u};
-      if (cvalid) w = load16(qrow + 32 * m + 8 * grp);
+      if (cvalid && p.q_sign != 0) w = load16(qrow + 32 * m + 8 * grp);
+      if (p.q_sign < 0) w ^= 0x80008000u;  // -q, exactly: the scale enters as |scale|
       T.qop[gi][m] = __builtin_bit_cast(op8, w);
     }
 #pragma unroll
@@ -390,8 +406,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(PrefillPara
   // rows of this lane: columns r = 4*grp + i, i.e. query r / g, head r % g
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {
-    float l_tot = T.l_run[gi] + __shfl_xor(T.l_run[gi], 16);
-    l_tot += __shfl_xor(l_tot, 32);
+    const float l_tot = sum_over_column(T.l_run[gi]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * grp + i;

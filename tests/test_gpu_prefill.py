@@ -167,3 +167,21 @@ def test_prefill_full_size_sampled():
         ref = oracle.decode(w.q[row:row + 1], w.k_cache, w.v_cache, w.block_tables[s:s + 1],
                             np.array([p + 1], np.int32), w.cfg.scale, B, "bf16")
         check(got[row:row + 1], ref, f"seq {s} query {j} (position {p})", "bf16")
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 2.5])
+def test_prefill_any_scale(scale):
+    """The kernel applies a positive factor in the exponent; a negative scale
+    enters as -q and a zero scale as q = 0 (uniform weights)."""
+    say(f"prefill scale {scale}")
+    lens = [9, 40, 77]
+    w = wl.make_prefill_workload(cfg_of("bf16", 8, 2, 64, 16, lens, index=44), queries=[9, 17, 77])
+    et = "bf16"
+    q = pb.to_device(w.q, et, DEV)
+    out = torch.empty(q.shape, dtype=torch.float32, device=DEV)
+    pb.pa_prefill(out, q, pb.int32_to_device(w.q_start, DEV), pb.to_device(w.k_cache, et, DEV),
+                  pb.to_device(w.v_cache, et, DEV), pb.int32_to_device(w.block_tables, DEV),
+                  pb.int32_to_device(w.context_lens, DEV), scale)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(w.q, w.q_start, w.k_cache, w.v_cache, w.block_tables, w.context_lens, scale, 16, et)
+    check(out, ref, f"scale {scale}", "f32")
