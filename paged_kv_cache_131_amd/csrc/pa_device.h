@@ -16,6 +16,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_inff();
 
@@ -71,6 +73,15 @@ struct ElemT<kF16> {
     }
     return w;
   }
+  // p = hi + lo: hi the nearest 16-bit values, lo the residuals rounded
+  __device__ static void split(const float* p, op8& hi, op8& lo) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const _Float16 h = static_cast<_Float16>(p[e]);
+      hi[e] = h;
+      lo[e] = static_cast<_Float16>(p[e] - static_cast<float>(h));
+    }
+  }
 };
 
 template <>
@@ -87,6 +98,21 @@ struct ElemT<kBF16> {
     }
   }
   __device__ static u32x4 keep_first(u32x4 w, int nvalid) { return ElemT<kF16>::keep_first(w, nvalid); }
+  // p = hi + lo: hi the nearest bf16 values (one packed conversion per pair,
+  // unpacked by shifts), lo the residuals rounded
+  __device__ static void split(const float* p, op8& hi, op8& lo) {
+    u32x4 h, l;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t hh = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{p[2 * i], p[2 * i + 1]}), bf16x2));
+      const float r0 = p[2 * i] - __uint_as_float(hh << 16);
+      const float r1 = p[2 * i + 1] - __uint_as_float(hh & 0xffff0000u);
+      h[i] = hh;
+      l[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{r0, r1}), bf16x2));
+    }
+    hi = __builtin_bit_cast(op8, h);
+    lo = __builtin_bit_cast(op8, l);
+  }
 };
 
 __device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {

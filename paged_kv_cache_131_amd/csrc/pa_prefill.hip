@@ -116,8 +116,10 @@ struct PrefillTile {
   // ring loads: this wave's instructions, per lane the byte offset inside the
   // block (without the chunk's offset) and, for V, which of the chunk's blocks
   uint32_t block_bytes;
-  uint32_t k_off[LPW / 2], v_off[LPW / 2];
-  int k_blk[LPW / 2], v_blk[LPW / 2];
+  uint32_t k_off[LPW / 2];
+  int k_blk[LPW / 2];
+  const char* v_src[LPW / 2];  // V: the lane's address in block 0 of the pool
+  bool v_ge1[LPW / 2], v_ge2[LPW / 2], v_ge3[LPW / 2];  // V: block index >= 1, 2, 3
   int pos_w, last_w;  // first position and last chunk of this wave's queries (-1: none)
   op8 qop[NG][MQ];
   int pcol[NG];
@@ -142,8 +144,11 @@ struct PrefillTile {
       k_blk[ii] = __builtin_amdgcn_readfirstlane((i * 64 / (D / 8)) >> lg);
       const int c = u >> 2;
       const int tg = (u & 3) ^ v_swizzle(c);
-      v_off[ii] = (uint32_t)(((kvh * D + c) * B + ((8 * tg) & (B - 1))) * 2);
-      v_blk[ii] = (8 * tg) >> lg;
+      v_src[ii] = static_cast<const char*>(p.v_cache) + ((kvh * D + c) * B + ((8 * tg) & (B - 1))) * 2;
+      const int vb = (8 * tg) >> lg;
+      v_ge1[ii] = vb >= 1;
+      v_ge2[ii] = vb >= 2;
+      v_ge3[ii] = vb >= 3;
     }
   }
 
@@ -156,7 +161,6 @@ struct PrefillTile {
     const int id2 = min(max(c.id2, 0), last), id3 = min(max(c.id3, 0), last);
     const uint32_t in_block = (uint32_t)(cs & (p.block_size - 1));  // chunk's first token inside its block
     const char* kc = static_cast<const char*>(p.k_cache) + (size_t)in_block * (D * 2);
-    const char* vc = static_cast<const char*>(p.v_cache) + (size_t)in_block * 2;
     const uint16_t* st = stage_buf<S, D>();
 #pragma unroll
     for (int ii = 0; ii < LPW / 2; ++ii) {
@@ -168,9 +172,8 @@ struct PrefillTile {
 #pragma unroll
     for (int ii = 0; ii < LPW / 2; ++ii) {
       const int i = wave * (LPW / 2) + ii;
-      const int vb = v_blk[ii];
-      const int id = vb == 0 ? id0 : (vb == 1 ? id1 : (vb == 2 ? id2 : id3));
-      load_lds16(vc + (size_t)id * block_bytes + v_off[ii], lds_address(st + kChunk * D + i * 512));
+      const uint32_t id = (uint32_t)(v_ge3[ii] ? id3 : (v_ge2[ii] ? id2 : (v_ge1[ii] ? id1 : id0)));
+      load_lds16(v_src[ii] + ((uint64_t)id * block_bytes + in_block * 2), lds_address(st + kChunk * D + i * 512));
     }
   }
 
@@ -244,20 +247,15 @@ struct PrefillTile {
           for (int j = 0; j < NT; ++j) o[gi][j][i] *= ai;
         }
       }
-      float pe[8], psum = 0.f;
+      float pe[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pe[e] = fast_exp2(__builtin_fmaf(sv[gi][e], p.scale_log2, -m_run[gi]));
-        psum += pe[e];
-      }
+      for (int e = 0; e < 8; ++e) pe[e] = fast_exp2(__builtin_fmaf(sv[gi][e], p.scale_log2, -m_run[gi]));
+      float psum = pe[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) psum += pe[e];
       l_run[gi] += psum;
       op8 phi, plo;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const scalar hi = static_cast<scalar>(pe[e]);
-        phi[e] = hi;
-        plo[e] = static_cast<scalar>(pe[e] - static_cast<float>(hi));
-      }
+      Tr::split(pe, phi, plo);
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
         o[gi][j] = mfma_16x16x32(phi, __builtin_bit_cast(op8, vr[j]), o[gi][j]);
