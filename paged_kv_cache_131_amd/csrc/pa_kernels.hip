@@ -808,15 +808,25 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
   // Balanced split or fixed-partition stream: every worker scans the lengths
   // itself (S <= kMaxBalancedSeqs), so no planning launch is needed.
   const int S = p.num_seqs;
+  // lengths to LDS, four coalesced loads in flight per lane at a time
+  for (int s0 = 0; s0 < S; s0 += 256) {
+    int v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = s0 + 64 * i + lane;
+      v[i] = s < S ? p.context_lens[s] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = s0 + 64 * i + lane;
+      if (s < S) g_lens[s] = v[i];
+    }
+  }
+  __syncthreads();
   const int per = (S + 63) >> 6;
   const int s_lo = min(lane * per, S), s_hi = min(s_lo + per, S);
   long long mine = 0;
-  for (int s = s_lo; s < s_hi; ++s) {
-    const int L_raw = p.context_lens[s];
-    g_lens[s] = L_raw;
-    mine += num_chunks(capped_len(p, L_raw));
-  }
-  __syncthreads();
+  for (int s = s_lo; s < s_hi; ++s) mine += num_chunks(capped_len(p, g_lens[s]));
   long long incl = mine;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -1083,18 +1093,22 @@ __global__ __launch_bounds__(64 * W) void merge_kernel(DecodeParams p) {
       vn[j] = vs[e];
     }
   }
-  if (p.merge) merge_sequence<D, W>(p, sm, s, head0, nh, tid, L, meta_first, meta_n);
+  // the slot's block-table entry is requested before the merge's loads
   const int slot = (p.k_new && blockIdx.z == 0) ? new_token_slot(p, s, L) : -1;
+  if (p.merge) merge_sequence<D, W>(p, sm, s, head0, nh, tid, L, meta_first, meta_n);
   if (slot >= 0) {
     const int B = p.block_size, phys = slot / B, off = slot % B;
     U* kd = const_cast<U*>(static_cast<const U*>(p.k_cache)) + (((size_t)phys * Hkv + kvh) * B + off) * D;
     U* vd = const_cast<U*>(static_cast<const U*>(p.v_cache)) + ((size_t)phys * Hkv + kvh) * D * B + off;
+    // non-temporal: the V column dirties one cache line per element, and
+    // left in the cache those partial lines were written back during the
+    // next decode's stream, slowing it by about 5%
 #pragma unroll
     for (int j = 0; j < NE; ++j) {
       const int e = tid + 64 * W * j;
       if (e < D) {
-        kd[e] = static_cast<U>(kn[j]);
-        vd[(size_t)e * B] = static_cast<U>(vn[j]);
+        __builtin_nontemporal_store(static_cast<U>(kn[j]), kd + e);
+        __builtin_nontemporal_store(static_cast<U>(vn[j]), vd + (size_t)e * B);
       }
     }
   }
@@ -1116,9 +1130,11 @@ __global__ __launch_bounds__(64) void write_kv_kernel(const U* __restrict__ k_ne
   const U* vr = v_new + ((size_t)n * Hkv + h) * D;
   U* kd = k_cache + (((size_t)phys * Hkv + h) * B + off) * D;
   U* vd = v_cache + ((size_t)phys * Hkv + h) * D * B + off;
+  // non-temporal, like the fused write's store: the V column's partial lines
+  // must not linger in the cache into the decode that reads the pool next
   for (int i = threadIdx.x; i < D; i += 64) {
-    kd[i] = kr[i];
-    vd[(size_t)i * B] = vr[i];
+    __builtin_nontemporal_store(kr[i], kd + i);
+    __builtin_nontemporal_store(vr[i], vd + (size_t)i * B);
   }
 }
 
