@@ -96,20 +96,26 @@ constexpr int kMaxDevices = 64;
 constexpr int kMfmaWavesPerCu = 4;
 std::mutex g_mutex;
 int g_cus[kMaxDevices];
+int g_lds_per_cu[kMaxDevices];
 int g_waves[kMaxDevices][3][2][3][9];  // [device][elem][head_dim 64/128][algo][G]
 
 // Balanced-split workers for one launch (all KV heads). The MFMA engine runs
 // one wave per SIMD: measured on MI355X, more resident waves of it split the
 // same bytes-in-flight over more pieces and lose bandwidth; the vector engine,
 // with more VALU work per byte, wants every resident wave.
-int workers_target(int elem, int head_dim, int algo, int G) {
+// Also sets *lds_per_workgroup: the CU's LDS over its resident workgroups.
+int workers_target(int elem, int head_dim, int algo, int G, size_t* lds_per_workgroup) {
   int dev = 0;
+  *lds_per_workgroup = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 2048;
   std::lock_guard<std::mutex> lock(g_mutex);
   if (g_cus[dev] == 0) {
-    int cus = 0;
+    int cus = 0, lds = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+    if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess || lds < 1)
+      lds = 65536;
     g_cus[dev] = cus;
+    g_lds_per_cu[dev] = lds;
   }
   int& waves = g_waves[dev][elem][head_dim == 128][algo][G];
   if (waves == 0) {
@@ -117,6 +123,7 @@ int workers_target(int elem, int head_dim, int algo, int G) {
     if (waves < 1) waves = 8;
     if (algo == pa::kAlgoMfma && waves > kMfmaWavesPerCu) waves = kMfmaWavesPerCu;
   }
+  *lds_per_workgroup = (size_t)g_lds_per_cu[dev] / (size_t)waves;
   return g_cus[dev] * waves;
 }
 
@@ -367,10 +374,11 @@ static pa_status decode_impl(void* out, const void* q, const void* k_new, const 
 
   const int elem = dtype == PA_F32 ? pa::kF32 : (dtype == PA_F16 ? pa::kF16 : pa::kBF16);
   long long workers;
+  size_t lds_per_workgroup = 0;
+  const int target = workers_target(elem, head_dim, kernel_algo, G, &lds_per_workgroup);
   if (pl.mode == pa::kModeBalanced || pl.mode == pa::kModeFixedStream) {
     // rounded down: every worker of the grid must be resident at once, or
     // the ones left over start only when others finish
-    const int target = workers_target(elem, head_dim, kernel_algo, G);
     workers = target / num_kv_heads;
     const long long cap = pl.mode == pa::kModeBalanced ? pl.max_workers : (long long)num_seqs * pl.max_parts;
     if (workers > cap) workers = cap;
@@ -380,7 +388,7 @@ static pa_status decode_impl(void* out, const void* q, const void* k_new, const 
     if (workers > INT_MAX) return PA_ERR_UNSUPPORTED;
   }
   const hipError_t e = pa::launch_decode(p, elem, head_dim, kernel_algo, G, (unsigned)workers, pl.slots > 0,
-                                         static_cast<hipStream_t>(stream));
+                                         lds_per_workgroup, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

@@ -52,15 +52,22 @@ struct DecodeParams {
   int32_t max_parts;    // fixed mode: partitions per sequence (grid.x = num_seqs*max_parts)
   int32_t out_dtype;    // Elem of `out`
   int32_t merge;        // set by launch_decode: some sequence is split and needs merging
+  int32_t lens_pad;     // set by launch_decode: ints of dynamic LDS holding the lengths
+  int32_t res_slots;    // set by launch_decode: finished segments the LDS result buffer holds
 };
+
+// Most finished segments a decode workgroup keeps in LDS before storing them.
+constexpr int kMaxResultSlots = 32;
 
 // Launch the decode kernel for (elem, head_dim, algo, group bucket G),
 // grid = (workers per KV head, num_kv_heads), 64 threads per workgroup, then,
 // when `merge` is set or the call brings new tokens (k_new), the closing
 // kernel (grid = (num_seqs, num_kv_heads)) that combines the partial results
 // of split sequences and stores the new tokens into the cache.
+// lds_per_workgroup: the share of a CU's LDS one decode workgroup may take
+// (the CU's LDS over the resident workgroups per CU the worker count assumes).
 hipError_t launch_decode(const DecodeParams& p, int elem, int head_dim, int algo, int G,
-                         unsigned workers, bool merge, hipStream_t stream);
+                         unsigned workers, bool merge, size_t lds_per_workgroup, hipStream_t stream);
 // Resident waves per CU of that kernel (0 if unknown).
 int decode_waves_per_cu(int elem, int head_dim, int algo, int G);
 

@@ -43,10 +43,11 @@ __device__ __forceinline__ int len_uniform(const DecodeParams& p, int s) {
   return lens[__builtin_amdgcn_readfirstlane(s)];
 }
 
-// The workers of the balanced split and of the partition stream copy every
-// stored length into LDS at their start (num_seqs entries of dynamic shared
-// memory) and walk their sequences from there.
-extern __shared__ int32_t g_lens[];
+// Dynamic shared memory of a decode workgroup: the stored lengths
+// (lens_pad ints; the balanced split and the partition stream copy every
+// length there at their start and walk their sequences from it), then the
+// result buffer of res_slots finished segments.
+extern __shared__ __align__(16) int32_t g_lens[];
 
 __device__ __forceinline__ int lds_len(int s) { return __builtin_amdgcn_readfirstlane(g_lens[s]); }
 
@@ -677,34 +678,101 @@ __device__ __forceinline__ ChunkIds ids_at(const DecodeParams& p, Pos x, const S
   return load_chunk_ids(p.block_tables + (size_t)g.s * p.max_blocks_per_seq, x.cs, g.lbl, p.log2_block);
 }
 
+// Finished segments wait in LDS and are stored to memory when the worker's
+// stream ends (or when the buffer is full). A store issued in the middle of
+// the stream is counted with the K/V loads in flight, so the wait for the
+// next load issued after it also waits for the store, which under the
+// stream's load takes several microseconds: stored at every segment end, a
+// step of 512-token partitions spent a fifth of its time there.
+// Slot k: values [g][D] (normalised outputs of a whole sequence, or the
+// unnormalised partial of a piece), (m, l) of each head, and a record
+// {sequence, pieces, partial-result slot, first slot, 1 if the split record
+// is written}.
+constexpr int kResRec = 5;
+
+struct ResultBuf {
+  float* vals;
+  float* ml;
+  int* rec;
+  int n;
+};
+
+__device__ __forceinline__ ResultBuf result_buffer(const DecodeParams& p, int D) {
+  ResultBuf rb;
+  rb.vals = reinterpret_cast<float*>(g_lens + p.lens_pad);
+  rb.ml = rb.vals + (size_t)p.res_slots * p.group * D;
+  rb.rec = reinterpret_cast<int*>(rb.ml + (size_t)p.res_slots * p.group * 2);
+  rb.n = 0;
+  return rb;
+}
+
+// Store every buffered result: whole sequences to `out`, pieces of split
+// ones to the workspace, and the split records.
+template <int D>
+__device__ void flush_results(const DecodeParams& p, ResultBuf& rb, int kvh, int lane) {
+  const int gq = p.group, Hq = p.num_heads, n4 = gq * D / 4;
+  const size_t head0 = (size_t)kvh * gq;
+  const bool out_vec = p.out_dtype == kF32 && (reinterpret_cast<uintptr_t>(p.out) & 15) == 0;
+  for (int k = 0; k < rb.n; ++k) {
+    const int* r = rb.rec + kResRec * k;
+    const int s = __builtin_amdgcn_readfirstlane(r[0]), np = __builtin_amdgcn_readfirstlane(r[1]);
+    const int slot = __builtin_amdgcn_readfirstlane(r[2]);
+    const float* v = rb.vals + (size_t)k * gq * D;
+    if (r[4] && lane == 0) {
+      p.ws_meta[2 * s] = r[3];
+      p.ws_meta[2 * s + 1] = np;
+    }
+    if (np == 1) {
+      const size_t base = ((size_t)s * Hq + head0) * D;
+      if (out_vec) {
+        for (int i = lane; i < n4; i += 64)
+          reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + base)[i] = reinterpret_cast<const f32x4*>(v)[i];
+      } else {
+        for (int idx = lane; idx < gq * D; idx += 64) store_out(p.out, base + idx, v[idx], p.out_dtype);
+      }
+    } else {
+      const size_t row0 = (size_t)slot * Hq + head0;
+      for (int i = lane; i < n4; i += 64)
+        reinterpret_cast<f32x4*>(p.ws_acc + row0 * D)[i] = reinterpret_cast<const f32x4*>(v)[i];
+      for (int i = lane; i < 2 * gq; i += 64) p.ws_ml[row0 * 2 + i] = rb.ml[(size_t)k * gq * 2 + i];
+    }
+  }
+  rb.n = 0;
+}
+
 template <class Eng, int D>
 __device__ void segment_epilogue(const DecodeParams& p, const typename Eng::Smem& sm, const Segment& g, int kvh,
-                                 int lane) {
-  const int gq = p.group, Hq = p.num_heads;
-  const size_t head0 = (size_t)kvh * gq;
-  // the piece holding a sequence's first token records where its pieces are
-  // (single pieces too, so the merge kernel never reads a stale record)
-  if (p.mode == kModeBalanced && g.t0 == 0 && kvh == 0 && lane == 0) {
-    p.ws_meta[2 * g.s] = g.first_slot;
-    p.ws_meta[2 * g.s + 1] = g.npieces;
-  }
+                                 int lane, ResultBuf& rb) {
+  if (rb.n == p.res_slots) flush_results<D>(p, rb, kvh, lane);
+  const int gq = p.group;
+  const int k = rb.n;
+  float* v = rb.vals + (size_t)k * gq * D;
   if (g.npieces == 1) {
-    const size_t base = ((size_t)g.s * Hq + head0) * D;
     for (int idx = lane; idx < gq * D; idx += 64) {
       const int h = idx / D, dd = idx % D;
-      store_out(p.out, base + idx, Eng::o_val(sm, h, dd, gq) / Eng::l_val(sm, h), p.out_dtype);
+      v[idx] = Eng::o_val(sm, h, dd, gq) / Eng::l_val(sm, h);
     }
   } else {
-    const size_t row0 = (size_t)g.slot * Hq + head0;
     for (int idx = lane; idx < gq * D; idx += 64) {
       const int h = idx / D, dd = idx % D;
-      p.ws_acc[row0 * D + idx] = Eng::o_val(sm, h, dd, gq);
+      v[idx] = Eng::o_val(sm, h, dd, gq);
     }
     for (int h = lane; h < gq; h += 64) {
-      p.ws_ml[(row0 + h) * 2] = Eng::m_val(sm, h);
-      p.ws_ml[(row0 + h) * 2 + 1] = Eng::l_val(sm, h);
+      rb.ml[((size_t)k * gq + h) * 2] = Eng::m_val(sm, h);
+      rb.ml[((size_t)k * gq + h) * 2 + 1] = Eng::l_val(sm, h);
     }
   }
+  if (lane == 0) {
+    int* r = rb.rec + kResRec * k;
+    r[0] = g.s;
+    r[1] = g.npieces;
+    r[2] = g.slot;
+    r[3] = g.first_slot;
+    // the piece holding a sequence's first token records where its pieces
+    // are (single pieces too, so the merge kernel never reads a stale record)
+    r[4] = p.mode == kModeBalanced && g.t0 == 0 && kvh == 0;
+  }
+  rb.n = k + 1;
   __syncthreads();
 }
 
@@ -718,6 +786,7 @@ __device__ void run_stream(const DecodeParams& p, typename Eng::Smem& sm, Segmen
   static_assert(Eng::kSub == 1, "the chunk stream assumes one 32-token chunk per step");
   Segment A = src.next(p);
   if (!A.valid) return;
+  ResultBuf rb = result_buffer(p, D);
   Segment B = src.next(p);
   Segment C = B.valid ? src.next(p) : invalid_segment();
   Eng eng;
@@ -741,7 +810,7 @@ __device__ void run_stream(const DecodeParams& p, typename Eng::Smem& sm, Segmen
     eng.step(f, p, sm, kvh, lane, p0.cs, A, p1.cs, &ids1, n1);
     if (leaving || at_end) {
       eng.finish(sm, lane);
-      segment_epilogue<Eng, D>(p, sm, A, kvh, lane);
+      segment_epilogue<Eng, D>(p, sm, A, kvh, lane, rb);
       if (at_end) break;
       A = B;
       B = C;
@@ -755,6 +824,7 @@ __device__ void run_stream(const DecodeParams& p, typename Eng::Smem& sm, Segmen
     p2 = advance(p2, A, B, C);
     ids1 = ids2;
   }
+  flush_results<D>(p, rb, kvh, lane);
 }
 
 // Workgroups are handed to the 8 XCDs (each with its own L2) in turn by
@@ -1197,17 +1267,40 @@ const void* decode_fn(int elem, int head_dim, int algo, int G) {
 
 }  // namespace
 
+size_t decode_static_lds(int elem, int head_dim, int algo, int G) {
+  if (algo == kAlgoMfma) {
+    if (elem == kF32) return 0;
+    return head_dim == 64 ? sizeof(MfmaEngine<kBF16, 64, kMfmaSub>::Smem) : sizeof(MfmaEngine<kBF16, 128, kMfmaSub>::Smem);
+  }
+  const int D = head_dim;
+  switch (G) {
+    case 1: return D == 64 ? sizeof(VecEngine<kF32, 64, 1>::Smem) : sizeof(VecEngine<kF32, 128, 1>::Smem);
+    case 2: return D == 64 ? sizeof(VecEngine<kF32, 64, 2>::Smem) : sizeof(VecEngine<kF32, 128, 2>::Smem);
+    case 4: return D == 64 ? sizeof(VecEngine<kF32, 64, 4>::Smem) : sizeof(VecEngine<kF32, 128, 4>::Smem);
+    default: return D == 64 ? sizeof(VecEngine<kF32, 64, 8>::Smem) : sizeof(VecEngine<kF32, 128, 8>::Smem);
+  }
+}
+
 hipError_t launch_decode(const DecodeParams& p, int elem, int head_dim, int algo, int G, unsigned workers,
-                         bool merge, hipStream_t stream) {
+                         bool merge, size_t lds_per_workgroup, hipStream_t stream) {
   const void* fn = decode_fn(elem, head_dim, algo, G);
   if (!fn) return hipErrorInvalidDeviceFunction;
   DecodeParams args = p;
   args.merge = merge ? 1 : 0;
+  // dynamic LDS: the lengths (balanced split and partition stream), then as
+  // many result slots as the workgroup's share of the CU's LDS leaves room
+  // for (at least one; one segment per workgroup needs no more)
+  args.lens_pad = p.mode == kModeFixed ? 0 : (p.num_seqs + 3) / 4 * 4;
+  const size_t lens_bytes = (size_t)args.lens_pad * sizeof(int32_t);
+  const size_t slot_bytes = ((size_t)p.group * head_dim + 2 * (size_t)p.group + kResRec) * sizeof(float);
+  const size_t fixed = decode_static_lds(elem, head_dim, algo, G) + lens_bytes;
+  size_t slots = lds_per_workgroup > fixed ? (lds_per_workgroup - fixed) / slot_bytes : 0;
+  if (p.mode == kModeFixed || slots < 1) slots = 1;
+  if (slots > (size_t)kMaxResultSlots) slots = kMaxResultSlots;
+  args.res_slots = (int)slots;
   void* kargs[] = {&args};
-  // the balanced split and the partition stream keep every length in LDS
-  const size_t lens_lds = p.mode == kModeFixed ? 0 : (size_t)p.num_seqs * sizeof(int32_t);
-  hipError_t e =
-      hipLaunchKernel(fn, dim3(workers, (unsigned)p.num_kv_heads, 1), dim3(64, 1, 1), kargs, lens_lds, stream);
+  hipError_t e = hipLaunchKernel(fn, dim3(workers, (unsigned)p.num_kv_heads, 1), dim3(64, 1, 1), kargs,
+                                 lens_bytes + slots * slot_bytes, stream);
   // the closing launch merges split sequences and stores the fused write
   if (e != hipSuccess || (!merge && !p.k_new)) return e;
   // few pieces per sequence (balanced split): one wave per (sequence, KV
