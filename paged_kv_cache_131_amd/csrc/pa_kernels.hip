@@ -1303,9 +1303,10 @@ hipError_t launch_decode(const DecodeParams& p, int elem, int head_dim, int algo
                                  lens_bytes + slots * slot_bytes, stream);
   // the closing launch merges split sequences and stores the fused write
   if (e != hipSuccess || (!merge && !p.k_new)) return e;
-  // few pieces per sequence (balanced split): one wave per (sequence, KV
-  // head); fixed partitions: four waves per (sequence, query head)
-  const bool wide = p.mode != kModeBalanced && merge && p.max_parts > 4;
+  // few pieces per sequence: one wave per (sequence, KV head); many (fixed
+  // partitions, or a balanced split of few sequences over many workers):
+  // four waves per (sequence, query head)
+  const bool wide = merge && (p.mode == kModeBalanced ? (long long)workers > 4LL * p.num_seqs : p.max_parts > 4);
   const void* mf;
   if (wide) {
     if (elem == kF32)
