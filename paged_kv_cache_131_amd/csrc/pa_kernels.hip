@@ -786,16 +786,18 @@ __device__ void run_stream(const DecodeParams& p, typename Eng::Smem& sm, Segmen
   static_assert(Eng::kSub == 1, "the chunk stream assumes one 32-token chunk per step");
   Segment A = src.next(p);
   if (!A.valid) return;
-  ResultBuf rb = result_buffer(p, D);
-  Segment B = src.next(p);
-  Segment C = B.valid ? src.next(p) : invalid_segment();
+  // the first chunk's block ids and q are requested before the next
+  // segments are walked
+  Pos p0{0, A.t0};
+  const ChunkIds ids0 = ids_at(p, p0, A, A, A);
   Eng eng;
   typename Eng::Q q, qn;
   eng.load_q(q, p, A.s, kvh, lane);
-  Pos p0{0, A.t0};
+  ResultBuf rb = result_buffer(p, D);
+  Segment B = src.next(p);
+  Segment C = B.valid ? src.next(p) : invalid_segment();
   Pos p1 = advance(p0, A, B, C);
   Pos p2 = advance(p1, A, B, C);
-  const ChunkIds ids0 = ids_at(p, p0, A, B, C);
   ChunkIds ids1 = ids_at(p, p1, A, B, C);
   typename Eng::Frag f;
   eng.load_k(f, p, kvh, lane, p0.cs, &ids0, A);

@@ -360,6 +360,22 @@ def test_more_sequences_than_the_length_scan_takes(part):
     check(out[seqs], ref[seqs], 2e-3, f"4200 sequences part={part}")
 
 
+@pytest.mark.parametrize("name,Hq,Hkv,d,hi", [("short-gqa", 8, 2, 128, 40), ("short-mha", 16, 16, 64, 8)])
+def test_result_buffer_overflow(name, Hq, Hkv, d, hi):
+    # thousands of short sequences give each worker more finished segments
+    # than its LDS result buffer holds, so results are also stored mid-stream
+    cfg = wl.DecodeConfig(name, 33, 4096, Hq, Hkv, d, 16, "bf16", 1.0, ("uniform", 1, hi), hi)
+    say(f"result buffer overflow {name}")
+    w = wl.make_decode_workload(cfg)
+    dv = Dev(w)
+    dv.write()
+    kr, vr = host_after_write(w)
+    seqs = list(range(0, 4096, 7)) + [4095]
+    ref = oracle.decode(w.q, kr, vr, w.block_tables, w.context_lens, cfg.scale, 16, "bf16", seqs=seqs)
+    out = dv.decode(partition_size=-1).cpu().numpy()
+    check(out[seqs], ref[seqs], 2e-3, f"{name} all segments")
+
+
 @pytest.mark.parametrize("part", [32, 64, -1])
 def test_long_piece_lists(part):
     # 282 and 257 partitions of 32 tokens: more pieces than the merge stages
