@@ -690,6 +690,15 @@ __device__ __forceinline__ ChunkIds ids_at(const DecodeParams& p, Pos x, const S
 // is written}.
 constexpr int kResRec = 5;
 
+template <bool NT>
+__device__ __forceinline__ void store16(f32x4* dst, f32x4 v) {
+  if (NT) {
+    __builtin_nontemporal_store(v, dst);
+  } else {
+    *dst = v;
+  }
+}
+
 struct ResultBuf {
   float* vals;
   float* ml;
@@ -707,8 +716,12 @@ __device__ __forceinline__ ResultBuf result_buffer(const DecodeParams& p, int D)
 }
 
 // Store every buffered result: whole sequences to `out`, pieces of split
-// ones to the workspace, and the split records.
-template <int D>
+// ones to the workspace, and the split records. NT: non-temporal stores, for
+// a buffer that filled up mid-stream (they complete sooner under the
+// stream's load, so the load waits behind them are shorter: 512-token
+// partitions at the long-context shape 939 -> 913 us); at the stream's end
+// ordinary stores.
+template <int D, bool NT>
 __device__ void flush_results(const DecodeParams& p, ResultBuf& rb, int kvh, int lane) {
   const int gq = p.group, Hq = p.num_heads, n4 = gq * D / 4;
   const size_t head0 = (size_t)kvh * gq;
@@ -726,14 +739,14 @@ __device__ void flush_results(const DecodeParams& p, ResultBuf& rb, int kvh, int
       const size_t base = ((size_t)s * Hq + head0) * D;
       if (out_vec) {
         for (int i = lane; i < n4; i += 64)
-          reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + base)[i] = reinterpret_cast<const f32x4*>(v)[i];
+          store16<NT>(reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + base) + i, reinterpret_cast<const f32x4*>(v)[i]);
       } else {
         for (int idx = lane; idx < gq * D; idx += 64) store_out(p.out, base + idx, v[idx], p.out_dtype);
       }
     } else {
       const size_t row0 = (size_t)slot * Hq + head0;
       for (int i = lane; i < n4; i += 64)
-        reinterpret_cast<f32x4*>(p.ws_acc + row0 * D)[i] = reinterpret_cast<const f32x4*>(v)[i];
+        store16<NT>(reinterpret_cast<f32x4*>(p.ws_acc + row0 * D) + i, reinterpret_cast<const f32x4*>(v)[i]);
       for (int i = lane; i < 2 * gq; i += 64) p.ws_ml[row0 * 2 + i] = rb.ml[(size_t)k * gq * 2 + i];
     }
   }
@@ -743,7 +756,7 @@ __device__ void flush_results(const DecodeParams& p, ResultBuf& rb, int kvh, int
 template <class Eng, int D>
 __device__ void segment_epilogue(const DecodeParams& p, const typename Eng::Smem& sm, const Segment& g, int kvh,
                                  int lane, ResultBuf& rb) {
-  if (rb.n == p.res_slots) flush_results<D>(p, rb, kvh, lane);
+  if (rb.n == p.res_slots) flush_results<D, true>(p, rb, kvh, lane);
   const int gq = p.group;
   const int k = rb.n;
   float* v = rb.vals + (size_t)k * gq * D;
@@ -826,7 +839,7 @@ __device__ void run_stream(const DecodeParams& p, typename Eng::Smem& sm, Segmen
     p2 = advance(p2, A, B, C);
     ids1 = ids2;
   }
-  flush_results<D>(p, rb, kvh, lane);
+  flush_results<D, false>(p, rb, kvh, lane);
 }
 
 // Workgroups are handed to the 8 XCDs (each with its own L2) in turn by
