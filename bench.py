@@ -304,6 +304,26 @@ def swap_sweep(torch, pb, total_mib: int, reps: int) -> dict:
     return res
 
 
+def cold_calls(step, n: int, torch, dev) -> dict:
+    """n single steps, each after an untimed 1 GiB write of scratch memory
+    (evicts the L2s and the Infinity Cache), each timed by its own event pair
+    on the launch stream: the per-call time with nothing of the inputs
+    cached."""
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    times = []
+    for _ in range(n):
+        scratch.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step()
+        e1.record()
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del scratch
+    return {"calls": n, "median_ms": round(float(np.median(times)), 5), "min_ms": round(float(min(times)), 5),
+            "timed": "one event pair per call, each after an untimed 1 GiB scratch write"}
+
+
 def calibration_copy(args, torch, dev) -> None:
     """One plain device copy of known size, run before the timed launches, for
     the traffic counters' calibration."""
@@ -424,6 +444,8 @@ def main() -> int:
                     help="hand out the pool's blocks in order instead of the seeded shuffled order")
     ap.add_argument("--two-calls", action="store_true", help="time pa_write_kv + pa_decode instead of the fused call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", type=int, default=20, metavar="N",
+                    help="also time N single steps, each after evicting the caches (0: skip)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run one plain device copy of this size first (traffic counter calibration)")
     ap.add_argument("--swap-sweep", type=int, default=0, metavar="MIB",
@@ -503,6 +525,8 @@ def main() -> int:
     elapsed = time.perf_counter() - t0
     call_ms = ev0.elapsed_time(ev1) / args.steps
 
+    cold = cold_calls(step, args.cold, torch, dev) if args.cold else None
+
     db = decode_bytes(cfg, c.context_lens)
     wb = write_bytes(cfg, len(c.context_lens), fused)
     if c.unique_kv != db["kv"]:
@@ -556,6 +580,11 @@ def main() -> int:
         "input_generation_s": round(c.gen_s, 2),
         **c.extra,
     }
+    if cold:
+        med, mn = cold["median_ms"], cold["min_ms"]
+        cold["GBps_median"] = round(launch_bytes / (med * 1e-3) / 1e9, 1)
+        cold["GBps_min_time"] = round(launch_bytes / (mn * 1e-3) / 1e9, 1)
+        result["cold_cache"] = cold
     if not args.no_cpu_baseline and c.w is not None:
         result["cpu_baseline"] = cpu_baseline(c.w, args.cpu_budget)
     print(json.dumps(result), flush=True)
