@@ -258,7 +258,7 @@ pa_status pa_prefill(void* out, const void* q, const int32_t* q_start, int32_t t
   p.q_sign = scale > 0.f ? 1 : (scale < 0.f ? -1 : 0);
   p.scale_log2 = (scale != 0.f ? std::fabs(scale) : 1.f) * 1.4426950408889634f;
   p.out_dtype = out_dtype;
-  const int qb = pa::prefill_queries_per_tile(group);
+  const int qb = pa::prefill_queries_per_tile(group, head_dim);
   const long long tiles = ((long long)total_q + qb - 1) / qb + num_seqs;
   if (tiles > INT_MAX) return PA_ERR_UNSUPPORTED;
   const int elem = dtype == PA_F16 ? pa::kF16 : pa::kBF16;

@@ -99,8 +99,8 @@ struct PrefillParams {
 };
 
 // Prompt-phase attention: grid (tiles, num_kv_heads), tiles an upper bound of
-// sum over sequences of ceil(queries / prefill_queries_per_tile(group)).
-int prefill_queries_per_tile(int group);
+// sum over sequences of ceil(queries / prefill_queries_per_tile(group, head_dim)).
+int prefill_queries_per_tile(int group, int head_dim);
 hipError_t launch_prefill(const PrefillParams& p, int elem, int head_dim, unsigned tiles, hipStream_t stream);
 
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* mapping, int num_pairs,

@@ -32,7 +32,12 @@ namespace pa {
 namespace {
 
 constexpr int kPrefillWaves = 4;
-constexpr int kPrefillGroups = 1;  // 16-column groups per wave
+// 16-column groups per wave: two at head_dim 128 (the K and V operands read
+// from LDS serve twice the columns; 197 VGPRs, two waves per SIMD; +17% at 32
+// query / 8 KV heads, +1 to +11% at groups 1, 2, 3, 8), one at head_dim 64
+// (two lost 6% at 32/8 heads).
+template <int D>
+constexpr int prefill_groups() { return D == 128 ? 2 : 1; }
 constexpr float kRescaleSlack = 8.f;  // log2 units
 
 typedef __attribute__((address_space(3))) const void lds_void;
@@ -421,17 +426,20 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(PrefillPara
 }
 
 const void* prefill_fn(int elem, int head_dim) {
-  constexpr int G = kPrefillGroups;
-  if (elem == kBF16) return head_dim == 64 ? reinterpret_cast<const void*>(&prefill_kernel<kBF16, 64, G>)
-                                           : reinterpret_cast<const void*>(&prefill_kernel<kBF16, 128, G>);
-  if (elem == kF16) return head_dim == 64 ? reinterpret_cast<const void*>(&prefill_kernel<kF16, 64, G>)
-                                          : reinterpret_cast<const void*>(&prefill_kernel<kF16, 128, G>);
+  constexpr int G64 = prefill_groups<64>(), G128 = prefill_groups<128>();
+  if (elem == kBF16) return head_dim == 64 ? reinterpret_cast<const void*>(&prefill_kernel<kBF16, 64, G64>)
+                                           : reinterpret_cast<const void*>(&prefill_kernel<kBF16, 128, G128>);
+  if (elem == kF16) return head_dim == 64 ? reinterpret_cast<const void*>(&prefill_kernel<kF16, 64, G64>)
+                                          : reinterpret_cast<const void*>(&prefill_kernel<kF16, 128, G128>);
   return nullptr;
 }
 
 }  // namespace
 
-int prefill_queries_per_tile(int group) { return kPrefillWaves * kPrefillGroups * (16 / group); }
+int prefill_queries_per_tile(int group, int head_dim) {
+  const int ng = head_dim == 128 ? prefill_groups<128>() : prefill_groups<64>();
+  return kPrefillWaves * ng * (16 / group);
+}
 
 hipError_t launch_prefill(const PrefillParams& p, int elem, int head_dim, unsigned tiles, hipStream_t stream) {
   const void* fn = prefill_fn(elem, head_dim);
