@@ -128,7 +128,10 @@ __device__ __forceinline__ int num_chunks(int L) { return L > 0 ? (L + kChunk - 
 // two PV results are added at the end, so P enters the product with ~16
 // significant bits instead of 8.
 // ---------------------------------------------------------------------------
-template <int E, int D, int SUB>
+// TV: V loads keep their lines in the caches (blocks larger than a chunk:
+// each chunk reads half or less of every 128-byte V row, and the next chunk
+// reads the rest of it); else they stream past them.
+template <int E, int D, int SUB, bool TV>
 struct MfmaEngine {
   using Tr = ElemT<E>;
   using op8 = typename Tr::op8;
@@ -227,7 +230,7 @@ struct MfmaEngine {
       const int physv = pick_block(ids[u], tv, lg, lbl, p.num_blocks);
       const raw* vb = vc + (((size_t)physv * Hkv + kvh) * D + col) * B + (tv & (B - 1));
 #pragma unroll
-      for (int j = 0; j < NT; ++j) f.vr[u][j] = load16_stream(vb + (size_t)16 * j * B);
+      for (int j = 0; j < NT; ++j) f.vr[u][j] = TV ? load16(vb + (size_t)16 * j * B) : load16_stream(vb + (size_t)16 * j * B);
     }
   }
 
@@ -1266,12 +1269,18 @@ const void* vec_kernel_d(int D, int G) {
   return D == 64 ? vec_kernel<E, 64>(G) : (D == 128 ? vec_kernel<E, 128>(G) : nullptr);
 }
 
-const void* decode_fn(int elem, int head_dim, int algo, int G) {
+template <int E, bool TV>
+const void* mfma_kernel_d(int D) {
+  return D == 64 ? kernel_of<MfmaEngine<E, 64, kMfmaSub, TV>, 64>()
+                 : (D == 128 ? kernel_of<MfmaEngine<E, 128, kMfmaSub, TV>, 128>() : nullptr);
+}
+
+// block_size selects the MFMA engine's V-load policy (blocks larger than a chunk keep V lines)
+const void* decode_fn(int elem, int head_dim, int algo, int G, int block_size = kChunk) {
   if (algo == kAlgoMfma) {
-    if (elem == kBF16) return head_dim == 64 ? kernel_of<MfmaEngine<kBF16, 64, kMfmaSub>, 64>()
-                                             : (head_dim == 128 ? kernel_of<MfmaEngine<kBF16, 128, kMfmaSub>, 128>() : nullptr);
-    if (elem == kF16) return head_dim == 64 ? kernel_of<MfmaEngine<kF16, 64, kMfmaSub>, 64>()
-                                            : (head_dim == 128 ? kernel_of<MfmaEngine<kF16, 128, kMfmaSub>, 128>() : nullptr);
+    const bool tv = block_size > kChunk;
+    if (elem == kBF16) return tv ? mfma_kernel_d<kBF16, true>(head_dim) : mfma_kernel_d<kBF16, false>(head_dim);
+    if (elem == kF16) return tv ? mfma_kernel_d<kF16, true>(head_dim) : mfma_kernel_d<kF16, false>(head_dim);
     return nullptr;
   }
   if (elem == kF32) return vec_kernel_d<kF32>(head_dim, G);
@@ -1285,7 +1294,8 @@ const void* decode_fn(int elem, int head_dim, int algo, int G) {
 size_t decode_static_lds(int elem, int head_dim, int algo, int G) {
   if (algo == kAlgoMfma) {
     if (elem == kF32) return 0;
-    return head_dim == 64 ? sizeof(MfmaEngine<kBF16, 64, kMfmaSub>::Smem) : sizeof(MfmaEngine<kBF16, 128, kMfmaSub>::Smem);
+    return head_dim == 64 ? sizeof(MfmaEngine<kBF16, 64, kMfmaSub, false>::Smem)
+                          : sizeof(MfmaEngine<kBF16, 128, kMfmaSub, false>::Smem);
   }
   const int D = head_dim;
   switch (G) {
@@ -1298,7 +1308,7 @@ size_t decode_static_lds(int elem, int head_dim, int algo, int G) {
 
 hipError_t launch_decode(const DecodeParams& p, int elem, int head_dim, int algo, int G, unsigned workers,
                          bool merge, size_t lds_per_workgroup, hipStream_t stream) {
-  const void* fn = decode_fn(elem, head_dim, algo, G);
+  const void* fn = decode_fn(elem, head_dim, algo, G, p.block_size);
   if (!fn) return hipErrorInvalidDeviceFunction;
   DecodeParams args = p;
   args.merge = merge ? 1 : 0;
