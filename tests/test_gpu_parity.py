@@ -244,6 +244,8 @@ GRID = [
     ("f32", 64, 16, 16, 2, "vector", -1),     # g = 8 vector
     ("f32", 128, 32, 4, 4, "vector", 32),
     ("f16", 64, 16, 64, 8, "mfma", -1),       # g = 8 MFMA
+    ("bf16", 128, 128, 32, 8, "mfma", -1),    # blocks larger than a chunk: V lines kept
+    ("bf16", 64, 64, 16, 4, "mfma", -1),
 ]
 
 
