@@ -24,7 +24,13 @@
  * blocks, each holding K and V for block_size tokens, [notes-zh] §5.1-§5.2;
  * the in-block order is this library's choice):
  *   k_cache: [num_blocks][num_kv_heads][block_size][head_dim]  (token rows)
- *   v_cache: [num_blocks][num_kv_heads][head_dim][block_size]  (token columns)
+ *   v_cache: [num_blocks][num_kv_heads][block_size/Bs][head_dim][Bs]
+ *            (token columns of sub-tiles: Bs = 32 when block_size is a
+ *            multiple of 32 above 32, else Bs = block_size, i.e. a plain
+ *            [head_dim][block_size] tile). Channel c of in-block token t is
+ *            element ((t / Bs) * head_dim + c) * Bs + t % Bs of the
+ *            head_dim*block_size elements of (block, KV head); a 32-token
+ *            piece of a block's V is then always whole rows.
  * Token t of a sequence lives in physical block block_tables[s][t / block_size]
  * at offset t % block_size ([deep-dive] §14 and §17), i.e. slot
  * physical_block * block_size + offset.
@@ -74,7 +80,7 @@ typedef enum pa_algo { PA_ALGO_AUTO = 0, PA_ALGO_VECTOR = 1, PA_ALGO_MFMA = 2 } 
  *                  A negative slot or one >= num_blocks*block_size is skipped.
  *   For every written token n and head h:
  *     k_cache[slot/B][h][slot%B][:] = k_new[n][h][:]
- *     v_cache[slot/B][h][:][slot%B] = v_new[n][h][:]
+ *     V channel c of (slot/B, h) at in-block token slot%B (layout above) = v_new[n][h][c]
  *   Bit-exact data movement (NaN payloads included). Two tokens naming the
  *   same slot in one call is a precondition violation (the winner is
  *   unspecified). num_tokens == 0 is a no-op. Any head_dim >= 1 and

@@ -19,5 +19,6 @@ from .paged_attention import (  # noqa: F401
     swap_in,
     swap_out,
     to_float64,
+    v_slot,
     write_kv,
 )

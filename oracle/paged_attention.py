@@ -14,7 +14,11 @@ Sources (web pages on the SOSP'23 PagedAttention paper):
 
 Storage conventions (the library's ABI; the pages fix none of this):
   k_cache  [num_blocks][num_kv_heads][block_size][head_dim]   token-major tile
-  v_cache  [num_blocks][num_kv_heads][head_dim][block_size]   token-minor tile
+  v_cache  [num_blocks][num_kv_heads][head_dim][block_size]   token-minor tile,
+           as an array shape; inside each tile the elements are sub-tiles
+           [block_size/Bs][head_dim][Bs] with Bs = 32 when block_size is a
+           multiple of 32 above 32, else Bs = block_size (plain
+           [head_dim][block_size]; see v_slot)
   q        [num_seqs][num_heads][head_dim]
   block_tables [num_seqs][max_blocks_per_seq] int32, context_lens [num_seqs]
 Element types: "f32" (numpy float32), "f16" (numpy float16) and "bf16"
@@ -64,6 +68,18 @@ def translate(block_table_row, token_index: int, block_size: int):
     return int(block_table_row[logical_block]), offset
 
 
+def v_slot(block_size: int, head_dim: int, offset: int):
+    """Where the channels of in-block token `offset` lie in a V tile held as
+    a [head_dim][block_size] array: the tile's elements are sub-tiles
+    [block_size/Bs][head_dim][Bs], Bs = 32 for a multiple of 32 above 32,
+    else Bs = block_size, so channel c of the token is flat element
+    ((offset // Bs) * head_dim + c) * Bs + offset % Bs. Returns (rows,
+    columns) index arrays of that array."""
+    sub = 32 if block_size > 32 and block_size % 32 == 0 else block_size
+    flat = ((offset // sub) * head_dim + np.arange(head_dim)) * sub + offset % sub
+    return flat // block_size, flat % block_size
+
+
 def write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, block_size, inplace=False):
     """Slot-mapped store of new K/V rows ("fused reshape and block write",
     [review-kr] §3-2(5); new KV goes into its physical block, [notes-zh] §5.3).
@@ -80,9 +96,10 @@ def write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, block_size, inplace=F
         if slot < 0:
             continue
         phys, off = divmod(int(slot), block_size)
+        rows, cols = v_slot(block_size, v_out.shape[2], off)
         for h in range(k_out.shape[1]):
             k_out[phys, h, off, :] = k_new[n, h, :]
-            v_out[phys, h, :, off] = v_new[n, h, :]
+            v_out[phys, h, rows, cols] = v_new[n, h, :]
     return k_out, v_out
 
 
@@ -140,7 +157,8 @@ def gather_sequence(k_cache, v_cache, block_table_row, context_len, kv_head,
     for t in range(context_len):
         phys, off = translate(block_table_row, t, block_size)
         keys[t] = to_float64(k_cache[phys, kv_head, off, :], etype)
-        values[t] = to_float64(v_cache[phys, kv_head, :, off], etype)
+        rows, cols = v_slot(block_size, head_dim, off)
+        values[t] = to_float64(v_cache[phys, kv_head, rows, cols], etype)
     return keys, values
 
 
@@ -258,7 +276,8 @@ def decode_blockwise(q, k_cache, v_cache, block_tables, context_lens, scale,
                 phys = int(block_tables[s][j])
                 used = min(block_size, L - j * block_size)
                 Kj = to_float64(k_cache[phys, kvh, :used, :], etype)      # [used][d]
-                Vj = to_float64(v_cache[phys, kvh, :, :used], etype)      # [d][used]
+                cols_of = [v_slot(block_size, head_dim, off) for off in range(used)]
+                Vj = np.stack([to_float64(v_cache[phys, kvh, r, c], etype) for r, c in cols_of], axis=1)  # [d][used]
                 block_scores.append(scale * (Kj @ qv))
                 block_values.append(Vj)
             top = max(sc.max() for sc in block_scores)
@@ -334,11 +353,13 @@ def bruteforce_decode(q, k_cache, v_cache, block_tables, context_lens, scale,
             top = max(scores)
             weights = [math.exp(x - top) for x in scores]
             total = sum(weights)
+            sub = 32 if block_size > 32 and block_size % 32 == 0 else block_size
             for i in range(head_dim):
                 acc = 0.0
                 for t in range(L):
                     phys = int(block_tables[s][t // block_size])
                     off = t % block_size
-                    acc += weights[t] * vf[phys][kvh][i][off]
+                    flat = ((off // sub) * head_dim + i) * sub + off % sub
+                    acc += weights[t] * vf[phys][kvh][flat // block_size][flat % block_size]
                 out[s][h][i] = acc / total
     return np.array(out, dtype=np.float64)

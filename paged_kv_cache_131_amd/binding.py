@@ -90,7 +90,8 @@ def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
 
 
 def pa_write_kv(k_new, v_new, k_cache, v_cache, slot_mapping, stream=None) -> None:
-    """k_new/v_new [T][Hkv][d]; k_cache [NB][Hkv][B][d]; v_cache [NB][Hkv][d][B]; slot_mapping [T] int32."""
+    """k_new/v_new [T][Hkv][d]; k_cache [NB][Hkv][B][d]; v_cache [NB][Hkv][d][B] (elements in the
+    header's V order: 32-token sub-tiles for block sizes that are multiples of 32 above 32); slot_mapping [T] int32."""
     lib = load_library()
     T, Hkv, d = k_new.shape
     NB, _, B, _ = k_cache.shape

@@ -32,6 +32,21 @@ __device__ __forceinline__ u32x4 load16_stream(const void* ptr) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// V tiles are stored as sub-tiles [block_size/Bs][head_dim][Bs]: Bs = 32 for
+// a block_size that is a multiple of 32 above 32, else Bs = block_size (a
+// plain [head_dim][block_size] tile). The element of channel c and in-block
+// token t of (block, KV head) lies at the offset v_elem(...) below; channel
+// c + 1 of the same token is Bs elements further.
+__device__ __forceinline__ int v_subtile(int block_size) {
+  return (block_size > 32 && (block_size & 31) == 0) ? 32 : block_size;
+}
+
+__device__ __forceinline__ size_t v_elem(int block, int num_kv_heads, int kv_head, int head_dim, int block_size,
+                                         int Bs, int c, int t) {
+  return ((size_t)block * num_kv_heads + kv_head) * head_dim * block_size + ((size_t)(t / Bs) * head_dim + c) * Bs +
+         (t % Bs);
+}
+
 // ---------------------------------------------------------------------------
 // Element types
 // ---------------------------------------------------------------------------

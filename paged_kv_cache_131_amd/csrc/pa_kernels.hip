@@ -11,9 +11,11 @@
 //
 // Pool layout (per physical block and KV head, one contiguous tile):
 //   K tile [block_size][head_dim]  -- token rows
-//   V tile [head_dim][block_size]  -- token columns
+//   V tile [block_size/Bs][head_dim][Bs], Bs = min(block_size, 32)  -- token
+//          columns of 32-token sub-tiles ([head_dim][block_size] up to 32)
 // so that both MFMA operands of the two contractions (QK over head_dim, PV
-// over tokens) are 16-byte contiguous loads straight from HBM.
+// over tokens) are 16-byte contiguous loads straight from HBM, and a 32-token
+// chunk's V is whole cache lines at every block size.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -128,10 +130,7 @@ __device__ __forceinline__ int num_chunks(int L) { return L > 0 ? (L + kChunk - 
 // two PV results are added at the end, so P enters the product with ~16
 // significant bits instead of 8.
 // ---------------------------------------------------------------------------
-// TV: V loads keep their lines in the caches (blocks larger than a chunk:
-// each chunk reads half or less of every 128-byte V row, and the next chunk
-// reads the rest of it); else they stream past them.
-template <int E, int D, int SUB, bool TV>
+template <int E, int D, int SUB>
 struct MfmaEngine {
   using Tr = ElemT<E>;
   using op8 = typename Tr::op8;
@@ -223,14 +222,15 @@ struct MfmaEngine {
     const int col = lane & 15, grp = lane >> 4;
     const int B = p.block_size, lg = p.log2_block, Hkv = p.num_kv_heads;
     const raw* __restrict__ vc = static_cast<const raw*>(p.v_cache);
+    const int Bs = v_subtile(B);
     // V: B operand, tokens 8*grp..+7 of each sub-chunk at dd = 16j + col
 #pragma unroll
     for (int u = 0; u < SUB; ++u) {
       const int tv = cs + kChunk * u + 8 * grp;
       const int physv = pick_block(ids[u], tv, lg, lbl, p.num_blocks);
-      const raw* vb = vc + (((size_t)physv * Hkv + kvh) * D + col) * B + (tv & (B - 1));
+      const raw* vb = vc + v_elem(physv, Hkv, kvh, D, B, Bs, col, tv & (B - 1));
 #pragma unroll
-      for (int j = 0; j < NT; ++j) f.vr[u][j] = TV ? load16(vb + (size_t)16 * j * B) : load16_stream(vb + (size_t)16 * j * B);
+      for (int j = 0; j < NT; ++j) f.vr[u][j] = load16_stream(vb + (size_t)16 * j * Bs);
     }
   }
 
@@ -454,9 +454,10 @@ struct VecEngine {
     const int tg = lane % LPD, ddl = lane / LPD;
     const int tv = cs + tg * VEC;
     const int physv = pick_block(ids, tv, lg, lbl, p.num_blocks);
-    const raw* vb = vc + (((size_t)physv * Hkv + kvh) * D + ddl) * B + (tv & (B - 1));
+    const int Bs = v_subtile(B);
+    const raw* vb = vc + v_elem(physv, Hkv, kvh, D, B, Bs, ddl, tv & (B - 1));
 #pragma unroll
-    for (int st = 0; st < VSTEPS; ++st) f.vr[st] = load16_stream(vb + (size_t)st * DPS * B);
+    for (int st = 0; st < VSTEPS; ++st) f.vr[st] = load16_stream(vb + (size_t)st * DPS * Bs);
   }
 
   __device__ void step(Frag& f, const DecodeParams& p, Smem& sm, int kvh, int lane, int cs, const Segment& cur,
@@ -1185,9 +1186,9 @@ __global__ __launch_bounds__(64 * W) void merge_kernel(DecodeParams p) {
   const int slot = (p.k_new && blockIdx.z == 0) ? new_token_slot(p, s, L) : -1;
   if (p.merge) merge_sequence<D, W>(p, sm, s, head0, nh, tid, L, meta_first, meta_n);
   if (slot >= 0) {
-    const int B = p.block_size, phys = slot / B, off = slot % B;
+    const int B = p.block_size, phys = slot / B, off = slot % B, Bs = v_subtile(B);
     U* kd = const_cast<U*>(static_cast<const U*>(p.k_cache)) + (((size_t)phys * Hkv + kvh) * B + off) * D;
-    U* vd = const_cast<U*>(static_cast<const U*>(p.v_cache)) + ((size_t)phys * Hkv + kvh) * D * B + off;
+    U* vd = const_cast<U*>(static_cast<const U*>(p.v_cache)) + v_elem(phys, Hkv, kvh, D, B, Bs, 0, off);
     // non-temporal: the V column dirties one cache line per element, and
     // left in the cache those partial lines were written back during the
     // next decode's stream, slowing it by about 5%
@@ -1196,7 +1197,7 @@ __global__ __launch_bounds__(64 * W) void merge_kernel(DecodeParams p) {
       const int e = tid + 64 * W * j;
       if (e < D) {
         __builtin_nontemporal_store(static_cast<U>(kn[j]), kd + e);
-        __builtin_nontemporal_store(static_cast<U>(vn[j]), vd + (size_t)e * B);
+        __builtin_nontemporal_store(static_cast<U>(vn[j]), vd + (size_t)e * Bs);
       }
     }
   }
@@ -1213,16 +1214,16 @@ __global__ __launch_bounds__(64) void write_kv_kernel(const U* __restrict__ k_ne
   const int n = blockIdx.x, h = blockIdx.y;
   const int slot = slots[n];
   if (slot < 0 || (long long)slot >= total_slots) return;
-  const int phys = slot / B, off = slot % B;
+  const int phys = slot / B, off = slot % B, Bs = v_subtile(B);
   const U* kr = k_new + ((size_t)n * Hkv + h) * D;
   const U* vr = v_new + ((size_t)n * Hkv + h) * D;
   U* kd = k_cache + (((size_t)phys * Hkv + h) * B + off) * D;
-  U* vd = v_cache + ((size_t)phys * Hkv + h) * D * B + off;
+  U* vd = v_cache + v_elem(phys, Hkv, h, D, B, Bs, 0, off);
   // non-temporal, like the fused write's store: the V column's partial lines
   // must not linger in the cache into the decode that reads the pool next
   for (int i = threadIdx.x; i < D; i += 64) {
     __builtin_nontemporal_store(kr[i], kd + i);
-    __builtin_nontemporal_store(vr[i], vd + (size_t)i * B);
+    __builtin_nontemporal_store(vr[i], vd + (size_t)i * Bs);
   }
 }
 
@@ -1269,18 +1270,12 @@ const void* vec_kernel_d(int D, int G) {
   return D == 64 ? vec_kernel<E, 64>(G) : (D == 128 ? vec_kernel<E, 128>(G) : nullptr);
 }
 
-template <int E, bool TV>
-const void* mfma_kernel_d(int D) {
-  return D == 64 ? kernel_of<MfmaEngine<E, 64, kMfmaSub, TV>, 64>()
-                 : (D == 128 ? kernel_of<MfmaEngine<E, 128, kMfmaSub, TV>, 128>() : nullptr);
-}
-
-// block_size selects the MFMA engine's V-load policy (blocks larger than a chunk keep V lines)
-const void* decode_fn(int elem, int head_dim, int algo, int G, int block_size = kChunk) {
+const void* decode_fn(int elem, int head_dim, int algo, int G) {
   if (algo == kAlgoMfma) {
-    const bool tv = block_size > kChunk;
-    if (elem == kBF16) return tv ? mfma_kernel_d<kBF16, true>(head_dim) : mfma_kernel_d<kBF16, false>(head_dim);
-    if (elem == kF16) return tv ? mfma_kernel_d<kF16, true>(head_dim) : mfma_kernel_d<kF16, false>(head_dim);
+    if (elem == kBF16) return head_dim == 64 ? kernel_of<MfmaEngine<kBF16, 64, kMfmaSub>, 64>()
+                                             : (head_dim == 128 ? kernel_of<MfmaEngine<kBF16, 128, kMfmaSub>, 128>() : nullptr);
+    if (elem == kF16) return head_dim == 64 ? kernel_of<MfmaEngine<kF16, 64, kMfmaSub>, 64>()
+                                            : (head_dim == 128 ? kernel_of<MfmaEngine<kF16, 128, kMfmaSub>, 128>() : nullptr);
     return nullptr;
   }
   if (elem == kF32) return vec_kernel_d<kF32>(head_dim, G);
@@ -1294,8 +1289,7 @@ const void* decode_fn(int elem, int head_dim, int algo, int G, int block_size = 
 size_t decode_static_lds(int elem, int head_dim, int algo, int G) {
   if (algo == kAlgoMfma) {
     if (elem == kF32) return 0;
-    return head_dim == 64 ? sizeof(MfmaEngine<kBF16, 64, kMfmaSub, false>::Smem)
-                          : sizeof(MfmaEngine<kBF16, 128, kMfmaSub, false>::Smem);
+    return head_dim == 64 ? sizeof(MfmaEngine<kBF16, 64, kMfmaSub>::Smem) : sizeof(MfmaEngine<kBF16, 128, kMfmaSub>::Smem);
   }
   const int D = head_dim;
   switch (G) {
@@ -1308,7 +1302,7 @@ size_t decode_static_lds(int elem, int head_dim, int algo, int G) {
 
 hipError_t launch_decode(const DecodeParams& p, int elem, int head_dim, int algo, int G, unsigned workers,
                          bool merge, size_t lds_per_workgroup, hipStream_t stream) {
-  const void* fn = decode_fn(elem, head_dim, algo, G, p.block_size);
+  const void* fn = decode_fn(elem, head_dim, algo, G);
   if (!fn) return hipErrorInvalidDeviceFunction;
   DecodeParams args = p;
   args.merge = merge ? 1 : 0;

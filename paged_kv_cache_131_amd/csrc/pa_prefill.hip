@@ -20,7 +20,8 @@
 //   K: token t of the chunk, head-dim segment s (8 elements) at unit
 //      t * D/8 + (s ^ fk(t));
 //   V, after K's 32*D/8 units: channel c, token group u (8 tokens) at unit
-//      c * 4 + (u ^ fv(c)).
+//      c * 4 + (u ^ fv(c)). (In the pool a chunk's V is one 32-token
+//      sub-tile [head_dim][32] of its block, or several whole blocks.)
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -149,7 +150,8 @@ struct PrefillTile {
       k_blk[ii] = __builtin_amdgcn_readfirstlane((i * 64 / (D / 8)) >> lg);
       const int c = u >> 2;
       const int tg = (u & 3) ^ v_swizzle(c);
-      v_src[ii] = static_cast<const char*>(p.v_cache) + ((kvh * D + c) * B + ((8 * tg) & (B - 1))) * 2;
+      const int Bs = v_subtile(B);  // V sub-tiles: channel stride Bs
+      v_src[ii] = static_cast<const char*>(p.v_cache) + ((size_t)kvh * D * B + c * Bs + ((8 * tg) & (Bs - 1))) * 2;
       const int vb = (8 * tg) >> lg;
       v_ge1[ii] = vb >= 1;
       v_ge2[ii] = vb >= 2;
@@ -165,6 +167,8 @@ struct PrefillTile {
     const int id0 = min(max(c.id0, 0), last), id1 = min(max(c.id1, 0), last);
     const int id2 = min(max(c.id2, 0), last), id3 = min(max(c.id3, 0), last);
     const uint32_t in_block = (uint32_t)(cs & (p.block_size - 1));  // chunk's first token inside its block
+    // the chunk's V sub-tile inside the block (blocks larger than the chunk)
+    const uint64_t v_sub = (uint64_t)(in_block / (uint32_t)v_subtile(p.block_size)) * D * v_subtile(p.block_size) * 2;
     const char* kc = static_cast<const char*>(p.k_cache) + (size_t)in_block * (D * 2);
     const uint16_t* st = stage_buf<S, D>();
 #pragma unroll
@@ -178,7 +182,7 @@ struct PrefillTile {
     for (int ii = 0; ii < LPW / 2; ++ii) {
       const int i = wave * (LPW / 2) + ii;
       const uint32_t id = (uint32_t)(v_ge3[ii] ? id3 : (v_ge2[ii] ? id2 : (v_ge1[ii] ? id1 : id0)));
-      load_lds16(v_src[ii] + ((uint64_t)id * block_bytes + in_block * 2), lds_address(st + kChunk * D + i * 512));
+      load_lds16(v_src[ii] + ((uint64_t)id * block_bytes + v_sub), lds_address(st + kChunk * D + i * 512));
     }
   }
 

@@ -73,6 +73,18 @@ def _threads() -> int:
     return max(1, min(16, n))
 
 
+def set_v_tokens(v_cache: np.ndarray, block: int, first: int, value) -> None:
+    """Set in-block tokens first.. of a block's V tiles (every KV head, every
+    channel) to value. A V tile, held as a [head_dim][block_size] array, is
+    stored as sub-tiles [block_size/Bs][head_dim][Bs] with Bs = 32 for a
+    multiple of 32 above 32, else Bs = block_size (plain [head_dim][block_size])."""
+    Hkv, d, B = v_cache.shape[1:]
+    Bs = 32 if B > 32 and B % 32 == 0 else B
+    tiles = v_cache[block].reshape(Hkv, B // Bs, d, Bs)
+    for t in range(first, B):
+        tiles[:, t // Bs, :, t % Bs] = value
+
+
 def random_stored(seq: np.random.SeedSequence, shape, etype: str, value_scale: float) -> np.ndarray:
     """Standard normals * value_scale rounded to `etype`; slice i of 2**22
     values comes from the i-th child of `seq`."""
@@ -236,7 +248,7 @@ def make_decode_workload(cfg: DecodeConfig, lengths=None, poison: bool = True,
             last = tables[s, nblk[s] - 1]
             off = (int(lens[s]) - 1) % B          # the new token's slot and the rest
             k_cache[last, :, off:, :] = pv
-            v_cache[last, :, :, off:] = pv
+            set_v_tokens(v_cache, last, off, pv)
     return DecodeWorkload(cfg, q, k_cache, v_cache, tables, lens.copy(), k_new, v_new,
                           slots, num_blocks, poison_block, used)
 
@@ -312,7 +324,7 @@ class ParallelSamplingWorkload:
                 for p in range(num_prompts):
                     last = self.seqs[p * samples].block_table[-1]
                     self.k_cache[last, :, tail:, :] = pv
-                    self.v_cache[last, :, :, tail:] = pv
+                    set_v_tokens(self.v_cache, last, tail, pv)
         self.step_index = 0
 
     def _dry_run_blocks(self) -> int:
@@ -412,7 +424,7 @@ class BeamSearchWorkload:
                 for g in self.groups:
                     last = g[0].block_table[-1]
                     self.k_cache[last, :, tail:, :] = pv
-                    self.v_cache[last, :, :, tail:] = pv
+                    set_v_tokens(self.v_cache, last, tail, pv)
         self.step_index = 0
 
     @property
@@ -521,7 +533,7 @@ def make_shared_prefix_workload(prefix_len: int = 1024, cfg: DecodeConfig = SHAR
             last = tables[s, (int(lens[s]) - 1) // B]
             off = (int(lens[s]) - 1) % B          # the new token's slot and the rest
             k_cache[last, :, off:, :] = pv
-            v_cache[last, :, :, off:] = pv
+            set_v_tokens(v_cache, last, off, pv)
     return DecodeWorkload(cfg, q, k_cache, v_cache, tables, lens, k_new, v_new, slots, num_blocks, poison_block, used)
 
 
@@ -618,5 +630,5 @@ def make_prefill_workload(cfg: DecodeConfig = PREFILL, lengths=None, queries=Non
             if off:
                 last = tables[s, nblk[s] - 1]
                 k_cache[last, :, off:, :] = pv
-                v_cache[last, :, :, off:] = pv
+                set_v_tokens(v_cache, last, off, pv)
     return PrefillWorkload(cfg, q, q_start, k_cache, v_cache, tables, lens.copy(), num_blocks, poison_block, used)

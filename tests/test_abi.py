@@ -43,7 +43,7 @@ def test_exports_match_header(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.pa_abi_version() == 5
+    assert lib.pa_abi_version() == 6
     assert lib.pa_status_string(OK) == b"ok"
     assert lib.pa_status_string(WORKSPACE) == b"workspace missing or too small"
     assert lib.pa_status_string(123) == b"unknown status"

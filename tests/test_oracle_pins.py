@@ -198,9 +198,13 @@ def paged_from_contiguous(keys, values, block_size, rng, num_blocks=None):
         blocks = perm[pos:pos + need[s]]
         pos += need[s]
         tables[s, :need[s]] = blocks
+        # V tiles hold sub-tiles [B/Bs][d][Bs]: Bs = 32 for multiples of 32 above 32, else B
+        Bs = 32 if block_size > 32 and block_size % 32 == 0 else block_size
         for t in range(K.shape[0]):
             kc[blocks[t // block_size], :, t % block_size, :] = K[t]
-            vc[blocks[t // block_size], :, :, t % block_size] = V[t]
+            off = t % block_size
+            sub = vc[blocks[t // block_size]].reshape(Hkv, block_size // Bs, d, Bs)
+            sub[:, off // Bs, :, off % Bs] = V[t]
     return kc.astype(np.float32), vc.astype(np.float32), tables
 
 
@@ -212,9 +216,9 @@ def random_case(seed, lens, Hq, Hkv, d):
     return rng, q, keys, values
 
 
-@pytest.mark.parametrize("Hq,Hkv,B", [(2, 2, 16), (8, 2, 4), (12, 4, 8)])
+@pytest.mark.parametrize("Hq,Hkv,B", [(2, 2, 16), (8, 2, 4), (12, 4, 8), (4, 2, 64), (2, 1, 128)])
 def test_decode_matches_torch_sdpa_on_contiguous(Hq, Hkv, B):
-    lens = [1, 5, 17, 40]
+    lens = [1, 5, 17, 40] if B <= 32 else [1, 33, 70, 200]
     d = 16
     rng, q, keys, values = random_case(7 + Hq, lens, Hq, Hkv, d)
     kc, vc, tables = paged_from_contiguous(keys, values, B, rng)
@@ -244,6 +248,23 @@ def test_permutation_invariance_and_blockwise_forms():
             part, partials = oracle.decode_partitioned(q, kc, vc, tables, np.array(lens), 0.5, 8, "f32", P)
             np.testing.assert_allclose(part, ref, rtol=0, atol=1e-12)
             assert [len(p) for p in partials[2]] == [-(-33 // P)] * 4
+
+
+def test_bruteforce_and_write_with_sub_tiled_values():
+    # blocks of 64 tokens: V tiles made of two 32-token sub-tiles
+    rng, q, keys, values = random_case(21, [70, 9], 4, 2, 6)
+    kc, vc, tables = paged_from_contiguous(keys, values, 64, rng)
+    args = (q, kc, vc, tables, np.array([70, 9]), 0.4, 64, "f32")
+    np.testing.assert_allclose(oracle.decode(*args), oracle.bruteforce_decode(*args), rtol=0, atol=1e-12)
+    # a write lands channel c of in-block token 45 at flat tile element ((45 // 32) * d + c) * 32 + 45 % 32
+    k0 = np.zeros((3, 2, 64, 6), np.float32)
+    v0 = np.zeros((3, 2, 6, 64), np.float32)
+    vn = rng.standard_normal((1, 2, 6)).astype(np.float32)
+    _, v1 = oracle.write_kv(k0, v0, np.zeros_like(vn), vn, np.array([2 * 64 + 45]), 64)
+    flat = v1[2].reshape(2, -1)
+    for c in range(6):
+        assert (flat[:, (1 * 6 + c) * 32 + 13] == vn[0, :, c]).all()
+    assert np.count_nonzero(v1) == np.count_nonzero(vn)
 
 
 def test_bruteforce_tiny_config_and_all_pool_permutations():
