@@ -34,7 +34,7 @@ namespace {
 
 constexpr int kPrefillWaves = 4;
 // 16-column groups per wave: two at head_dim 128 (the K and V operands read
-// from LDS serve twice the columns; 197 VGPRs, two waves per SIMD; +17% at 32
+// from LDS serve twice the columns; 190 VGPRs, two waves per SIMD; +17% at 32
 // query / 8 KV heads, +1 to +11% at groups 1, 2, 3, 8), one at head_dim 64
 // (two lost 6% at 32/8 heads).
 template <int D>
