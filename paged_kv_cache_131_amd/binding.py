@@ -129,14 +129,19 @@ def pa_decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_c
 _workspaces = {}
 
 
-def workspace_for(device, nbytes: int) -> torch.Tensor:
-    """A workspace of at least nbytes on `device`, reused by calls on that
-    device (calls on one device through this binding are stream-ordered on
-    the current stream)."""
-    key = torch.device(device)
+def workspace_for(device, nbytes: int, stream_handle: int) -> torch.Tensor:
+    """A workspace of at least nbytes on `device` for calls on the stream
+    `stream_handle`, reused by later calls on that stream (they run in order,
+    so they never use it at the same time). Calls on different streams get
+    different workspaces. A workspace is allocated on the stream that uses
+    it, so that when a larger one replaces it, the allocator reuses its memory
+    only after the work already queued on that stream."""
+    dev = torch.device(device)
+    key = (dev, int(stream_handle))
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=key)
+        with torch.cuda.stream(torch.cuda.ExternalStream(int(stream_handle), device=dev)):
+            ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
         _workspaces[key] = ws
     return ws
 
@@ -152,16 +157,17 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_c
     if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
         raise ValueError("block_tables must be [num_seqs][max_blocks], context_lens [num_seqs]")
     dt = k_cache.dtype
+    ptrs = (_dev(out, "out"), _dev(q, "q", dt), _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
+            _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32))
     need = int(lib.pa_decode_workspace_bytes(S, Hq, Hkv, d, int(max_context_len), int(partition_size)))
+    sh = _stream(stream)
     if workspace is None and need:
-        workspace = workspace_for(q.device, need)
+        workspace = workspace_for(q.device, need, sh)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     status = lib.pa_decode_ex(
-        _dev(out, "out"), _dev(q, "q", dt), _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
-        _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
-        S, Hq, Hkv, d, B, NB, block_tables.shape[1], int(max_context_len), float(scale), int(partition_size),
-        ws_ptr, ws_bytes, DTYPE_CODE[dt], DTYPE_CODE[out.dtype], ALGO_CODE[algo], _stream(stream))
+        *ptrs, S, Hq, Hkv, d, B, NB, block_tables.shape[1], int(max_context_len), float(scale), int(partition_size),
+        ws_ptr, ws_bytes, DTYPE_CODE[dt], DTYPE_CODE[out.dtype], ALGO_CODE[algo], sh)
     _check("pa_decode", status)
 
 
@@ -207,17 +213,18 @@ def pa_write_decode(out, q, k_new, v_new, k_cache, v_cache, block_tables, contex
     if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
         raise ValueError("block_tables must be [num_seqs][max_blocks], context_lens [num_seqs]")
     dt = k_cache.dtype
+    ptrs = (_dev(out, "out"), _dev(q, "q", dt), _dev(k_new, "k_new", dt), _dev(v_new, "v_new", dt),
+            _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
+            _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32))
     need = int(lib.pa_decode_workspace_bytes(S, Hq, Hkv, d, int(max_context_len), int(partition_size)))
+    sh = _stream(stream)
     if workspace is None and need:
-        workspace = workspace_for(q.device, need)
+        workspace = workspace_for(q.device, need, sh)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     status = lib.pa_write_decode(
-        _dev(out, "out"), _dev(q, "q", dt), _dev(k_new, "k_new", dt), _dev(v_new, "v_new", dt),
-        _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
-        _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
-        S, Hq, Hkv, d, B, NB, block_tables.shape[1], int(max_context_len), float(scale), int(partition_size),
-        ws_ptr, ws_bytes, DTYPE_CODE[dt], DTYPE_CODE[out.dtype], _stream(stream))
+        *ptrs, S, Hq, Hkv, d, B, NB, block_tables.shape[1], int(max_context_len), float(scale), int(partition_size),
+        ws_ptr, ws_bytes, DTYPE_CODE[dt], DTYPE_CODE[out.dtype], sh)
     _check("pa_write_decode", status)
 
 

@@ -313,6 +313,38 @@ def test_workspace_contents_do_not_matter():
             check(out, ref, 2e-3, f"workspace filled with {fill:#x}, part={part}")
 
 
+def test_calls_on_two_streams_get_their_own_workspaces():
+    # the binding's implicit workspace belongs to one (device, stream): decode
+    # calls queued on two streams at once each give, bit for bit, the result
+    # of the same call made alone
+    ws_a = small_cfg("llama3_8b", num_seqs=64)
+    ws_b = small_cfg("llama3_8b", num_seqs=40)
+    da, db = Dev(wl.make_decode_workload(ws_a)), Dev(wl.make_decode_workload(ws_b))
+    da.write()
+    db.write()
+    ref_a, ref_b = da.decode(), db.decode()
+    assert not torch.isnan(ref_a).any() and not torch.isnan(ref_b).any()
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(4):
+        with torch.cuda.stream(s1):
+            oa = da.decode()
+        with torch.cuda.stream(s2):
+            ob = db.decode()
+        outs.append((oa, ob))
+    torch.cuda.synchronize()
+    w1 = pb._workspaces[(DEV, s1.cuda_stream)]
+    w2 = pb._workspaces[(DEV, s2.cuda_stream)]
+    assert w1.data_ptr() != w2.data_ptr()
+    for i, (oa, ob) in enumerate(outs):
+        assert torch.equal(oa, ref_a), f"stream 1, call {i}"
+        assert torch.equal(ob, ref_b), f"stream 2, call {i}"
+    say("  two streams: 4 + 4 calls bit-identical to the calls made alone")
+
+
 # ---------------------------------------------------------------------------
 # Invariance and determinism
 # ---------------------------------------------------------------------------
