@@ -304,6 +304,55 @@ def swap_sweep(torch, pb, total_mib: int, reps: int) -> dict:
     return res
 
 
+def shape_sweep(torch, pb, wl, reps: int) -> list:
+    """pa_write_decode over a grid of batch sizes and equal context lengths
+    (Llama-3-8B head shape: 32 query / 8 KV heads, head_dim 128, block 16,
+    bf16, shuffled pool, balanced split), up to 4.2 M context tokens per step.
+    K/V values are seeded normal draws on the device (timing only)."""
+    import dataclasses
+
+    dev = torch.device("cuda:0")
+    base = wl.CONFIGS["llama3_8b"]
+    rows = []
+    for S in (1, 4, 16, 64, 256, 1024):
+        for L in (256, 1024, 4096, 16384, 65536):
+            if not 2048 <= S * L <= 4_200_000:
+                continue
+            cfg = dataclasses.replace(base, num_seqs=S, lengths=("fixed", (L,) * S), max_len=L)
+            w = wl.make_decode_workload(cfg, values=False)
+            NB, Hkv, B, d = w.num_blocks, cfg.num_kv_heads, cfg.block_size, cfg.head_dim
+            g = torch.Generator(device=dev)
+            g.manual_seed(0)
+            kc = torch.randn((NB, Hkv, B, d), device=dev, dtype=torch.bfloat16, generator=g)
+            vc = torch.randn((NB, Hkv, d, B), device=dev, dtype=torch.bfloat16, generator=g)
+            q = torch.randn((S, cfg.num_heads, d), device=dev, dtype=torch.bfloat16, generator=g)
+            kn = torch.randn((S, Hkv, d), device=dev, dtype=torch.bfloat16, generator=g)
+            vn = torch.randn((S, Hkv, d), device=dev, dtype=torch.bfloat16, generator=g)
+            bt, cl = pb.int32_to_device(w.block_tables, dev), pb.int32_to_device(w.context_lens, dev)
+            out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+
+            def step():
+                pb.pa_write_decode(out, q, kn, vn, kc, vc, bt, cl, cfg.scale, w.max_context_len)
+
+            for _ in range(10):
+                step()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                step()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / reps * 1000
+            nbytes = decode_bytes(cfg, w.context_lens)["total"] + write_bytes(cfg, S, True)
+            rows.append({"num_seqs": S, "context_len": L, "step_us": round(us, 1), "bytes": nbytes,
+                         "GBps": round(nbytes / us / 1e3), "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 3)})
+            print(json.dumps(rows[-1]), flush=True)
+            del kc, vc
+            torch.cuda.empty_cache()
+    return rows
+
+
 def cold_calls(step, n: int, torch, dev) -> dict:
     """n single steps, each after an untimed 1 GiB write of scratch memory
     (evicts the L2s and the Infinity Cache), each timed by its own event pair
@@ -450,6 +499,8 @@ def main() -> int:
                     help="run one plain device copy of this size first (traffic counter calibration)")
     ap.add_argument("--swap-sweep", type=int, default=0, metavar="MIB",
                     help="measure pa_swap_out/pa_swap_in of MIB MiB of blocks per block size and exit")
+    ap.add_argument("--shape-sweep", action="store_true",
+                    help="time pa_write_decode over a grid of batch sizes and context lengths and exit")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic file from two rocprofv3 counter_collection.csv files and exit")
     args = ap.parse_args()
@@ -471,6 +522,9 @@ def main() -> int:
     dev = torch.device("cuda:0")
     if args.swap_sweep:
         print(json.dumps({"swap_sweep": swap_sweep(torch, pb, args.swap_sweep, 5)}), flush=True)
+        return 0
+    if args.shape_sweep:
+        print(json.dumps({"shape_sweep": shape_sweep(torch, pb, wl, 50)}), flush=True)
         return 0
     if args.workload == "prefill":
         return prefill_main(args, torch, pb, wl, dev)
