@@ -42,15 +42,7 @@ Plan make_plan(int num_seqs, int num_kv_heads, int max_context_len, int partitio
   if (partition_size == PA_PARTITION_AUTO && num_seqs <= pa::kMaxBalancedSeqs) {
     pl.mode = pa::kModeBalanced;
     const long long wmax = (pa::kMaxWorkersTotal + num_kv_heads - 1) / num_kv_heads;
-    const long long chunks = (long long)num_seqs * max_chunks;  // bound of a KV head's chunks
-    // At most 32 pieces per sequence on average, unless every worker still
-    // gets four chunks or more: a batch of one or two sequences split into a
-    // hundred one-chunk pieces spends more in merging them (few sequences:
-    // few merge workgroups) than the extra chunks per worker cost. Measured at
-    // 1 sequence x 4096 tokens: 24.4 us with 128 workers per KV head, 17.9 us
-    // with 32; no change at 4 or more sequences of the same total size.
-    const long long few = (chunks + 3) / 4 > 32LL * num_seqs ? (chunks + 3) / 4 : 32LL * num_seqs;
-    const long long cap = chunks < few ? chunks : few;
+    const long long cap = (long long)num_seqs * max_chunks;
     pl.max_workers = (int)(wmax < cap ? wmax : cap);
     if (pl.max_workers < 1) pl.max_workers = 1;
     pl.slots = (size_t)pl.max_workers + (size_t)num_seqs;

@@ -971,8 +971,9 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
 // wave order. Each wave's first kPre pieces are requested together with the
 // (m, l) pairs, which are staged in LDS up to kMergeTile pieces; longer piece
 // lists take a plain per-output loop. The balanced split leaves few pieces
-// per sequence: one wave per (sequence, KV head). Fixed partitions leave
-// many: four waves per (sequence, query head).
+// per sequence: one wave per (sequence, KV head). Fixed partitions, or a
+// balanced split of few sequences over many workers, leave many: four waves
+// per (sequence, query head), in the 16-byte-load form below.
 constexpr int kMergeTile = 256;
 
 template <int W>
@@ -1000,6 +1001,83 @@ __device__ void merge_long(const DecodeParams& p, int s, int head0, int nh, int 
   }
 }
 
+// The W-wave form with one query head per workgroup (its only use): every
+// lane reads 16 bytes, D/4 lanes per piece, so one wave instruction covers
+// 64/(D/4) pieces and the first kIn instructions (all pieces up to
+// kIn * W * 64/(D/4)) are in flight before the weights are formed. Piece k
+// of wave v's instruction t is (t W + v) 64/(D/4) + lane / (D/4). The lane
+// groups of a wave are then added by lane swaps and the W waves in wave order.
+template <int D, int W>
+__device__ void merge_one_head(const DecodeParams& p, MergeSmem<W>& sm, int s, int head, int tid, int first_slot,
+                               int npieces) {
+  constexpr int LPP = D / 4;     // lanes per piece
+  constexpr int PPW = 64 / LPP;  // pieces per wave instruction
+  constexpr int kIn = 16;
+  const int Hq = p.num_heads;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int po = lane / LPP, d4 = (lane % LPP) * 4;
+  const size_t step = (size_t)Hq * D;
+  const float* base = p.ws_acc + ((size_t)first_slot * Hq + head) * D + d4;
+  f32x4 x[kIn];
+#pragma unroll
+  for (int t = 0; t < kIn; ++t) {
+    const int k = (t * W + wave) * PPW + po;
+    x[t] = k < npieces ? *reinterpret_cast<const f32x4*>(base + (size_t)k * step) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int i = tid; i < npieces; i += 64 * W) {
+    const size_t r = ((size_t)(first_slot + i) * Hq + head) * 2;
+    sm.wgt[0][i] = p.ws_ml[r];
+    sm.ls[0][i] = p.ws_ml[r + 1];
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float M = kNegInf;
+    for (int k = lane; k < npieces; k += 64) M = fmaxf(M, sm.wgt[0][k]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    float den = 0.f;
+    for (int k = lane; k < npieces; k += 64) {
+      const float e = fast_exp2(sm.wgt[0][k] - M);
+      sm.wgt[0][k] = e;
+      den = fmaf(e, sm.ls[0][k], den);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
+    const float inv = 1.f / den;
+    for (int k = lane; k < npieces; k += 64) sm.wgt[0][k] *= inv;
+  }
+  __syncthreads();
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < kIn; ++t) {
+    const int k = (t * W + wave) * PPW + po;
+    if (k < npieces) acc += sm.wgt[0][k] * x[t];
+  }
+#pragma unroll 4
+  for (int k = (kIn * W + wave) * PPW + po; k < npieces; k += W * PPW)
+    acc += sm.wgt[0][k] * *reinterpret_cast<const f32x4*>(base + (size_t)k * step);
+#pragma unroll
+  for (int off = LPP; off < 64; off <<= 1) {
+    acc.x += __shfl_xor(acc.x, off);
+    acc.y += __shfl_xor(acc.y, off);
+    acc.z += __shfl_xor(acc.z, off);
+    acc.w += __shfl_xor(acc.w, off);
+  }
+  if (po == 0) {
+    sm.part[wave][0][d4] = acc.x;
+    sm.part[wave][0][d4 + 1] = acc.y;
+    sm.part[wave][0][d4 + 2] = acc.z;
+    sm.part[wave][0][d4 + 3] = acc.w;
+  }
+  __syncthreads();
+  for (int d = tid; d < D; d += 64 * W) {
+    float o = sm.part[0][0][d];
+#pragma unroll
+    for (int v = 1; v < W; ++v) o += sm.part[v][0][d];
+    store_out(p.out, ((size_t)s * Hq + head) * D + d, o, p.out_dtype);
+  }
+}
+
 // Combines the pieces of query heads head0 .. head0+nh-1 of sequence s when
 // it was split; called by the whole workgroup. L_raw and the split record
 // (meta_first, meta_n; balanced mode) were loaded by the caller.
@@ -1023,6 +1101,12 @@ __device__ void merge_sequence(const DecodeParams& p, MergeSmem<W>& sm, int s, i
   if (npieces > kMergeTile) {
     merge_long<D, W>(p, s, head0, nh, tid, first_slot, npieces);
     return;
+  }
+  if constexpr (W > 1) {
+    if (nh == 1) {
+      merge_one_head<D, W>(p, sm, s, head0, tid, first_slot, npieces);
+      return;
+    }
   }
   const int Hq = p.num_heads;
   const int wave = tid >> 6, lane = tid & 63;

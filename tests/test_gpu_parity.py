@@ -426,17 +426,18 @@ def test_long_piece_lists(part):
 
 def test_balanced_split_with_more_pieces_than_the_merge_stages():
     # one sequence of 1,100 chunks and one KV head: the balanced split gives
-    # it 275 workers of four chunks each, more pieces than the merge stages in
-    # LDS (its plain per-output loop, reached through the split record)
+    # it one piece per resident worker (1,024 on a 256-CU part), more pieces
+    # than the merge stages in LDS (its plain per-output loop, reached
+    # through the split record)
     cfg = wl.DecodeConfig("one-long", 33, 1, 8, 1, 128, 16, "bf16", 1.0, ("fixed", (35200,)), 35200)
     need = pb.pa_decode_workspace_bytes(1, 8, 1, 128, 35200, -1)
-    assert need >= (275 + 1) * 8 * 130 * 4, need  # room for 275 pieces
+    assert need >= (257 + 1) * 8 * 130 * 4, need  # room for more than 256 pieces
     w = wl.make_decode_workload(cfg)
     dv = Dev(w)
     dv.write()
     kr, vr = host_after_write(w)
     ref = oracle.decode(w.q, kr, vr, w.block_tables, w.context_lens, cfg.scale, 16, "bf16")
-    check(dv.decode(partition_size=-1), ref, 2e-3, "one sequence, 275 pieces")
+    check(dv.decode(partition_size=-1), ref, 2e-3, "one sequence, one piece per worker")
 
 
 # ---------------------------------------------------------------------------
