@@ -385,6 +385,27 @@ def calibration_copy(args, torch, dev) -> None:
         del src, dst
 
 
+def copy_reference(torch, dev, mib: int = 2048, reps: int = 5) -> dict:
+    """A plain device-to-device copy of `mib` MiB timed on this GPU (HIP
+    events around `reps` back-to-back copies after one untimed copy): the
+    on-box bandwidth of the simplest streaming kernel, reads plus writes."""
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return {"kernel": f"torch copy_ of {mib} MiB, device to device", "bytes": 2 * n,
+            "ms": round(ms, 4), "GBps": round(2 * n / (ms * 1e-3) / 1e9, 1)}
+
+
 def prefill_cpu_baseline(w, budget_s: float) -> dict:
     """The oracle on the shortest prompts first until the time budget is
     spent (at least one), BLAS pinned to one thread."""
@@ -639,6 +660,10 @@ def main() -> int:
         cold["GBps_median"] = round(launch_bytes / (med * 1e-3) / 1e9, 1)
         cold["GBps_min_time"] = round(launch_bytes / (mn * 1e-3) / 1e9, 1)
         result["cold_cache"] = cold
+    if not args.calibration_copy_mib:  # a counter run's only copy is the calibration copy
+        ref = copy_reference(torch, dev)
+        ref["decode_frac_of_copy"] = round(achieved / ref["GBps"], 4)
+        result["copy_reference"] = ref
     if not args.no_cpu_baseline and c.w is not None:
         result["cpu_baseline"] = cpu_baseline(c.w, args.cpu_budget)
     print(json.dumps(result), flush=True)
