@@ -965,15 +965,12 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
 // Combine the partial results of every split (sequence, KV head): the
 // pieces' maxima and exponential sums give piece k of head h the weight
 // w_k = 2^(m_k - M) / sum_j 2^(m_j - M) l_j with M = max_j m_j (base-2 units),
-// and out = sum_k w_k acc_k. W waves share a (sequence, heads) unit: wave v
-// sums pieces v, v+W, v+2W, ... in ascending order for all its heads at once
-// (many independent loads in flight) and the W partial sums are added in
-// wave order. Each wave's first kPre pieces are requested together with the
-// (m, l) pairs, which are staged in LDS up to kMergeTile pieces; longer piece
-// lists take a plain per-output loop. The balanced split leaves few pieces
-// per sequence: one wave per (sequence, KV head). Fixed partitions, or a
-// balanced split of few sequences over many workers, leave many: four waves
-// per (sequence, query head), in the 16-byte-load form below.
+// and out = sum_k w_k acc_k. The (m, l) pairs are staged in LDS up to
+// kMergeTile pieces; longer piece lists take a plain per-output loop. The
+// balanced split leaves few pieces per sequence: one wave per (sequence, KV
+// head), its first pieces requested together with the (m, l) pairs. Fixed
+// partitions, or a balanced split of few sequences over many workers, leave
+// many: four waves per (sequence, query head), reading 16 bytes per lane.
 constexpr int kMergeTile = 256;
 
 template <int W>
@@ -1078,6 +1075,85 @@ __device__ void merge_one_head(const DecodeParams& p, MergeSmem<W>& sm, int s, i
   }
 }
 
+// The one-wave form (few pieces per sequence): lane l holds output elements
+// l, l + 64, ... of every head; each lane's first kPre pieces are requested
+// together with the (m, l) pairs.
+template <int D>
+__device__ void merge_heads_one_wave(const DecodeParams& p, MergeSmem<1>& sm, int s, int head0, int nh, int tid,
+                                     int first_slot, int npieces) {
+  constexpr int kPre = 4;
+  const int Hq = p.num_heads;
+  const int lane = tid;
+  constexpr int PER = D / 64;
+  const size_t step = (size_t)Hq * D;
+  const float* acc0 = p.ws_acc + ((size_t)first_slot * Hq + head0) * D + lane;
+  float pre[kPre][kMaxGroup][PER];
+#pragma unroll
+  for (int j = 0; j < kPre; ++j)
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h)
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        pre[j][h][i] = (h < nh && j < npieces) ? acc0[(size_t)h * D + j * step + 64 * i] : 0.f;
+  // (m, l) of every (head, piece): m into wgt, l kept in the same slot's pair
+  for (int i = tid; i < nh * npieces; i += 64) {
+    const int h = i / npieces, k = i % npieces;
+    const size_t r = ((size_t)(first_slot + k) * Hq + head0 + h) * 2;
+    sm.wgt[h][k] = p.ws_ml[r];
+    sm.ls[h][k] = p.ws_ml[r + 1];
+  }
+  __syncthreads();
+  // weights: lane h walks head h's pieces
+  if (tid < nh) {
+    float M = kNegInf;
+    for (int k = 0; k < npieces; ++k) M = fmaxf(M, sm.wgt[tid][k]);
+    float den = 0.f;
+    for (int k = 0; k < npieces; ++k) {
+      const float e = fast_exp2(sm.wgt[tid][k] - M);
+      sm.wgt[tid][k] = e;
+      den = fmaf(e, sm.ls[tid][k], den);
+    }
+    const float inv = 1.f / den;
+    for (int k = 0; k < npieces; ++k) sm.wgt[tid][k] *= inv;
+  }
+  __syncthreads();
+  float acc[kMaxGroup][PER];
+#pragma unroll
+  for (int h = 0; h < kMaxGroup; ++h)
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc[h][i] = 0.f;
+#pragma unroll
+  for (int j = 0; j < kPre; ++j) {
+    if (j < npieces) {
+#pragma unroll
+      for (int h = 0; h < kMaxGroup; ++h) {
+        if (h < nh) {
+          const float w = sm.wgt[h][j];
+#pragma unroll
+          for (int i = 0; i < PER; ++i) acc[h][i] = fmaf(w, pre[j][h][i], acc[h][i]);
+        }
+      }
+    }
+  }
+#pragma unroll 2
+  for (int k = kPre; k < npieces; ++k) {
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h) {
+      if (h < nh) {
+        const float w = sm.wgt[h][k];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) acc[h][i] = fmaf(w, acc0[(size_t)h * D + k * step + 64 * i], acc[h][i]);
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < kMaxGroup; ++h)
+    if (h < nh)
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        store_out(p.out, ((size_t)s * Hq + head0 + h) * D + lane + 64 * i, acc[h][i], p.out_dtype);
+}
+
 // Combines the pieces of query heads head0 .. head0+nh-1 of sequence s when
 // it was split; called by the whole workgroup. L_raw and the split record
 // (meta_first, meta_n; balanced mode) were loaded by the caller.
@@ -1085,7 +1161,6 @@ template <int D, int W>
 __device__ void merge_sequence(const DecodeParams& p, MergeSmem<W>& sm, int s, int head0, int nh, int tid, int L_raw,
                                int meta_first, int meta_n) {
   static_assert(D <= 128, "partial-sum tile");
-  constexpr int kPre = W == 1 ? 4 : 2;
   const int L = capped_len(p, L_raw);
   if (L <= 0) return;
   int first_slot, npieces;
@@ -1100,122 +1175,12 @@ __device__ void merge_sequence(const DecodeParams& p, MergeSmem<W>& sm, int s, i
   if (npieces <= 1) return;
   if (npieces > kMergeTile) {
     merge_long<D, W>(p, s, head0, nh, tid, first_slot, npieces);
-    return;
-  }
-  if constexpr (W > 1) {
-    if (nh == 1) {
-      merge_one_head<D, W>(p, sm, s, head0, tid, first_slot, npieces);
-      return;
-    }
-  }
-  const int Hq = p.num_heads;
-  const int wave = tid >> 6, lane = tid & 63;
-  constexpr int PER = D / 64;
-  const size_t step = (size_t)Hq * D;
-  const float* acc0 = p.ws_acc + ((size_t)first_slot * Hq + head0) * D + lane;
-  float pre[kPre][kMaxGroup][PER];
-#pragma unroll
-  for (int j = 0; j < kPre; ++j)
-#pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h)
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const int k = wave + W * j;
-        pre[j][h][i] = (h < nh && k < npieces) ? acc0[(size_t)h * D + k * step + 64 * i] : 0.f;
-      }
-  // (m, l) of every (head, piece): m into wgt, l kept in the same slot's pair
-  for (int i = tid; i < nh * npieces; i += 64 * W) {
-    const int h = i / npieces, k = i % npieces;
-    const size_t r = ((size_t)(first_slot + k) * Hq + head0 + h) * 2;
-    sm.wgt[h][k] = p.ws_ml[r];
-    sm.ls[h][k] = p.ws_ml[r + 1];
-  }
-  __syncthreads();
-  // weights: with one wave (few pieces) lane h walks head h's pieces; with
-  // W waves, wave v handles heads v, v+W, ... with its lanes over the pieces
-  if constexpr (W == 1) {
-    if (tid < nh) {
-      float M = kNegInf;
-      for (int k = 0; k < npieces; ++k) M = fmaxf(M, sm.wgt[tid][k]);
-      float den = 0.f;
-      for (int k = 0; k < npieces; ++k) {
-        const float e = fast_exp2(sm.wgt[tid][k] - M);
-        sm.wgt[tid][k] = e;
-        den = fmaf(e, sm.ls[tid][k], den);
-      }
-      const float inv = 1.f / den;
-      for (int k = 0; k < npieces; ++k) sm.wgt[tid][k] *= inv;
-    }
+  } else if constexpr (W > 1) {
+    // the W-wave launch gives each workgroup one query head
+    if (nh == 1) merge_one_head<D, W>(p, sm, s, head0, tid, first_slot, npieces);
+    else merge_long<D, W>(p, s, head0, nh, tid, first_slot, npieces);
   } else {
-  for (int h = wave; h < nh; h += W) {
-    float M = kNegInf;
-    for (int k = lane; k < npieces; k += 64) M = fmaxf(M, sm.wgt[h][k]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    float den = 0.f;
-    for (int k = lane; k < npieces; k += 64) {
-      const float e = fast_exp2(sm.wgt[h][k] - M);
-      sm.wgt[h][k] = e;
-      den = fmaf(e, sm.ls[h][k], den);
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
-    const float inv = 1.f / den;
-    for (int k = lane; k < npieces; k += 64) sm.wgt[h][k] *= inv;
-  }
-  }
-  __syncthreads();
-  float acc[kMaxGroup][PER];
-#pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h)
-#pragma unroll
-    for (int i = 0; i < PER; ++i) acc[h][i] = 0.f;
-#pragma unroll
-  for (int j = 0; j < kPre; ++j) {
-    const int k = wave + W * j;
-    if (k < npieces) {
-#pragma unroll
-      for (int h = 0; h < kMaxGroup; ++h) {
-        if (h < nh) {
-          const float w = sm.wgt[h][k];
-#pragma unroll
-          for (int i = 0; i < PER; ++i) acc[h][i] = fmaf(w, pre[j][h][i], acc[h][i]);
-        }
-      }
-    }
-  }
-#pragma unroll 2
-  for (int k = wave + W * kPre; k < npieces; k += W) {
-#pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h) {
-      if (h < nh) {
-        const float w = sm.wgt[h][k];
-#pragma unroll
-        for (int i = 0; i < PER; ++i) acc[h][i] = fmaf(w, acc0[(size_t)h * D + k * step + 64 * i], acc[h][i]);
-      }
-    }
-  }
-  if constexpr (W == 1) {
-#pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h)
-      if (h < nh)
-#pragma unroll
-        for (int i = 0; i < PER; ++i)
-          store_out(p.out, ((size_t)s * Hq + head0 + h) * D + lane + 64 * i, acc[h][i], p.out_dtype);
-  } else {
-#pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h)
-      if (h < nh)
-#pragma unroll
-        for (int i = 0; i < PER; ++i) sm.part[wave][h][lane + 64 * i] = acc[h][i];
-    __syncthreads();
-    const int nw = npieces < W ? npieces : W;
-    for (int idx = tid; idx < nh * D; idx += 64 * W) {
-      const int h = idx / D, dd = idx % D;
-      float o = sm.part[0][h][dd];
-      for (int v = 1; v < nw; ++v) o += sm.part[v][h][dd];
-      store_out(p.out, ((size_t)s * Hq + head0 + h) * D + dd, o, p.out_dtype);
-    }
+    merge_heads_one_wave<D>(p, sm, s, head0, nh, tid, first_slot, npieces);
   }
 }
 
