@@ -246,6 +246,8 @@ GRID = [
     ("f16", 64, 16, 64, 8, "mfma", -1),       # g = 8 MFMA
     ("bf16", 128, 128, 32, 8, "mfma", -1),    # blocks larger than a chunk: V lines kept
     ("bf16", 64, 64, 16, 4, "mfma", -1),
+    ("bf16", 128, 16, 24, 4, "mfma", -1),     # g = 6
+    ("f16", 64, 32, 18, 3, "vector", 64),     # g = 6 vector, fixed partitions
 ]
 
 

@@ -76,6 +76,8 @@ CHUNKED = [1, 1, 7, 32, 1, 37, 64, 129]
     ("f16", 6, 2, 64, 8),       # g = 3: 15 of 16 columns used, 4 blocks per chunk
     ("bf16", 5, 1, 128, 128),   # g = 5: 3 queries per tile, chunks inside one block
     ("f16", 2, 1, 128, 64),     # g = 2
+    ("bf16", 12, 2, 128, 16),   # g = 6: 2 queries per tile, 12 of 16 columns used
+    ("f16", 7, 1, 64, 32),      # g = 7: 2 queries per tile, 14 of 16 columns used
 ])
 @pytest.mark.parametrize("whole", [True, False])
 def test_prefill_matches_oracle(etype, Hq, Hkv, d, B, whole):
