@@ -248,6 +248,10 @@ GRID = [
     ("bf16", 64, 64, 16, 4, "mfma", -1),
     ("bf16", 128, 16, 24, 4, "mfma", -1),     # g = 6
     ("f16", 64, 32, 18, 3, "vector", 64),     # g = 6 vector, fixed partitions
+    ("f16", 128, 16, 16, 8, "mfma", 0),       # g = 2 MFMA, no split
+    ("f16", 64, 16, 12, 4, "vector", -1),     # g = 3 vector
+    ("bf16", 128, 16, 10, 2, "vector", 32),   # g = 5 vector, fixed partitions
+    ("bf16", 64, 32, 14, 2, "vector", -1),    # g = 7 vector
 ]
 
 
