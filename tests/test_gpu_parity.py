@@ -252,6 +252,8 @@ GRID = [
     ("f16", 64, 16, 12, 4, "vector", -1),     # g = 3 vector
     ("bf16", 128, 16, 10, 2, "vector", 32),   # g = 5 vector, fixed partitions
     ("bf16", 64, 32, 14, 2, "vector", -1),    # g = 7 vector
+    ("f16", 64, 128, 8, 2, "mfma", 64),       # head_dim 64, 128-token blocks, partitions inside a block
+    ("f32", 128, 64, 8, 1, "vector", -1),     # fp32, 64-token blocks (V sub-tiles), g = 8
 ]
 
 
