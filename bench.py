@@ -82,30 +82,90 @@ def write_bytes(c, T: int, fused: bool) -> int:
     return 2 * T * c.num_kv_heads * c.head_dim * es * 2 + (0 if fused else 4 * T)
 
 
-def cpu_baseline(w, budget_s: float) -> dict:
-    """The oracle, as it stands, on the first sequences of the same workload
-    until the time budget is spent (at least one sequence), BLAS pinned to one
-    thread."""
-    import oracle
+# The oracle job the forked workers of oracle_timed() run: (fn(unit), work(unit)).
+_ORACLE_JOB = None
 
+
+def host_cores() -> int:
+    """Cores this process may run on, capped at 16 (one GPU's share of the
+    host on the GPU machines)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _oracle_worker(job):
+    units, budget_s = job
     from threadpoolctl import threadpool_limits
+
+    fn, work = _ORACLE_JOB
+    done, amount = 0, 0
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        for u in units:
+            fn(u)
+            done += 1
+            amount += work(u)
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    return done, amount
+
+
+def oracle_timed(fn, work, units, budget_s: float, procs: int) -> dict:
+    """Runs fn(u) over `units` in order until the budget is spent (at least
+    one unit per process), BLAS pinned to one thread per process. procs > 1:
+    forked worker processes take units round-robin, each until the budget is
+    spent; the figure is the summed work over the wall time of the whole
+    pool. Called before anything touches the GPU."""
+    global _ORACLE_JOB
+    _ORACLE_JOB = (fn, work)
+    units = list(units)
+    t0 = time.perf_counter()
+    if procs <= 1:
+        done, amount = _oracle_worker((units, budget_s))
+    else:
+        import multiprocessing as mp
+
+        with mp.get_context("fork").Pool(procs) as pool:
+            parts = pool.map(_oracle_worker, [(units[k::procs], budget_s) for k in range(procs)])
+        done, amount = sum(p[0] for p in parts), sum(p[1] for p in parts)
+    dt = time.perf_counter() - t0
+    _ORACLE_JOB = None
+    return {"units": done, "amount": amount, "seconds": dt, "procs": procs}
+
+
+def cpu_baseline(w, budget_s: float) -> dict:
+    """The oracle, as it stands, on the same workload: one sequence (all
+    heads) per unit in batch order, on every host core (forked processes),
+    plus the single-process figure."""
+    import oracle
 
     c = w.cfg
     kr, vr = oracle.write_kv(w.k_cache, w.v_cache, w.k_new, w.v_new, w.slot_mapping, c.block_size)
-    done = 0
-    with threadpool_limits(1):
-        t0 = time.perf_counter()
-        while done < c.num_seqs:
-            oracle.decode(w.q, kr, vr, w.block_tables, w.context_lens, c.scale, c.block_size, c.etype, seqs=[done])
-            done += 1
-            if time.perf_counter() - t0 >= budget_s:
-                break
-        dt = time.perf_counter() - t0
     es = {"f32": 4, "f16": 2, "bf16": 2}[c.etype]
-    kv = int(w.context_lens[:done].astype(np.int64).sum()) * c.num_kv_heads * c.head_dim * 2 * es
-    return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {done} of {c.num_seqs} sequences, all heads, {dt:.1f} s, "
-                      f"{done / dt:.2f} seq/s, float64 NumPy oracle"}
+
+    def fn(s):
+        oracle.decode(w.q, kr, vr, w.block_tables, w.context_lens, c.scale, c.block_size, c.etype, seqs=[s])
+
+    def work(s):
+        return int(w.context_lens[s]) * c.num_kv_heads * c.head_dim * 2 * es
+
+    procs = host_cores()
+    one = oracle_timed(fn, work, range(c.num_seqs), budget_s / 3, 1)
+    many = oracle_timed(fn, work, range(c.num_seqs), budget_s * 2 / 3, procs)
+
+    def fig(r):
+        return r["amount"] / r["seconds"] / 1e9
+
+    return {"value": fig(many), "unit": "GB/s", "cores": procs, "kind": "oracle",
+            "sample": f"{many['units']} of {c.num_seqs} sequences (all heads; worker k takes sequences k, k+{procs}, "
+                      f"...) in {many['seconds']:.1f} s on {procs} forked processes, "
+                      f"{many['units'] / many['seconds']:.2f} seq/s, float64 NumPy oracle",
+            "single_thread": {"value": fig(one), "unit": "GB/s", "cores": 1,
+                              "sample": f"first {one['units']} sequences in {one['seconds']:.1f} s, "
+                                        f"{one['units'] / one['seconds']:.2f} seq/s"}}
 
 
 def traffic_for(kernel: str, workload: str):
@@ -191,12 +251,11 @@ def unique_kv_bytes(c, tables, lens) -> int:
     return sum(reads.values()) * c.num_kv_heads * c.head_dim * 2 * es
 
 
-def decode_case(cfg, wl, pb, dev, contiguous=False, shared_prefix=False) -> Case:
+def decode_case(w, pb, dev, gen_s: float) -> Case:
+    """Device copies of a generated decode workload."""
     c = Case()
-    t0 = time.perf_counter()
-    w = wl.make_shared_prefix_workload() if shared_prefix else wl.make_decode_workload(cfg, contiguous=contiguous)
     cfg = w.cfg
-    c.gen_s = time.perf_counter() - t0
+    c.gen_s = gen_s
     et = cfg.etype
     c.w, c.cfg = w, cfg
     c.kc, c.vc = pb.to_device(w.k_cache, et, dev), pb.to_device(w.v_cache, et, dev)
@@ -407,31 +466,31 @@ def copy_reference(torch, dev, mib: int = 2048, reps: int = 5) -> dict:
 
 
 def prefill_cpu_baseline(w, budget_s: float) -> dict:
-    """The oracle on the shortest prompts first until the time budget is
-    spent (at least one), BLAS pinned to one thread."""
+    """The oracle on whole prompts, shortest first, on every host core
+    (forked processes), plus the single-process figure."""
     import oracle
 
-    from threadpoolctl import threadpool_limits
-
     c = w.cfg
-    order = np.argsort(w.context_lens, kind="stable")
-    done, pairs = 0, 0
+    order = np.argsort(w.context_lens, kind="stable").tolist()
     n = w.queries.astype(np.int64)
     L = w.context_lens.astype(np.int64)
-    with threadpool_limits(1):
-        t0 = time.perf_counter()
-        while done < c.num_seqs:
-            s = int(order[done])
-            oracle.prefill(w.q, w.q_start, w.k_cache, w.v_cache, w.block_tables, w.context_lens, c.scale,
-                           c.block_size, c.etype, seqs=[s])
-            pairs += int(n[s] * (L[s] - n[s]) + n[s] * (n[s] + 1) // 2)
-            done += 1
-            if time.perf_counter() - t0 >= budget_s:
-                break
-        dt = time.perf_counter() - t0
-    flops = pairs * c.num_heads * c.head_dim * 4
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-            "sample": f"the {done} shortest of {c.num_seqs} prompts, all heads, {dt:.1f} s, float64 NumPy oracle"}
+
+    def fn(s):
+        oracle.prefill(w.q, w.q_start, w.k_cache, w.v_cache, w.block_tables, w.context_lens, c.scale,
+                       c.block_size, c.etype, seqs=[s])
+
+    def work(s):
+        pairs = int(n[s] * (L[s] - n[s]) + n[s] * (n[s] + 1) // 2)
+        return pairs * c.num_heads * c.head_dim * 4
+
+    procs = host_cores()
+    one = oracle_timed(fn, work, order, budget_s / 3, 1)
+    many = oracle_timed(fn, work, order, budget_s * 2 / 3, procs)
+    return {"value": many["amount"] / many["seconds"] / 1e12, "unit": "TFLOP/s", "cores": procs, "kind": "oracle",
+            "sample": f"{many['units']} of the shortest of {c.num_seqs} prompts (all heads) in {many['seconds']:.1f} s "
+                      f"on {procs} forked processes, float64 NumPy oracle",
+            "single_thread": {"value": one["amount"] / one["seconds"] / 1e12, "unit": "TFLOP/s", "cores": 1,
+                              "sample": f"the {one['units']} shortest prompts in {one['seconds']:.1f} s"}}
 
 
 def prefill_main(args, torch, pb, wl, dev) -> int:
@@ -441,6 +500,9 @@ def prefill_main(args, torch, pb, wl, dev) -> int:
     t0 = time.perf_counter()
     w = wl.make_prefill_workload(cfg, contiguous=args.contiguous)
     gen_s = time.perf_counter() - t0
+    # the oracle runs before the library is loaded or the GPU touched
+    cpu = None if args.no_cpu_baseline else prefill_cpu_baseline(w, args.cpu_budget)
+    pb.load_library()
     et = cfg.etype
     q = pb.to_device(w.q, et, dev)
     out = torch.empty(q.shape, dtype=q.dtype, device=dev)
@@ -494,8 +556,8 @@ def prefill_main(args, torch, pb, wl, dev) -> int:
                      "traffic": traffic_for("prefill_kernel", "prefill")},
         "input_generation_s": round(gen_s, 2),
     }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = prefill_cpu_baseline(w, args.cpu_budget)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
     return 0
 
@@ -539,30 +601,40 @@ def main() -> int:
     from paged_kv_cache_131_amd import binding as pb
     from paged_kv_cache_131_amd import workloads as wl
 
-    pb.load_library()
     dev = torch.device("cuda:0")
+    if args.workload == "prefill" and not (args.swap_sweep or args.shape_sweep):
+        return prefill_main(args, torch, pb, wl, dev)
+    # a drawn workload is generated first and the oracle's baseline timed on
+    # it before the library is loaded or the GPU touched
+    w0, cpu = None, None
+    if args.workload in ("shared_prefix",) + tuple(wl.CONFIGS) and not (args.swap_sweep or args.shape_sweep):
+        import dataclasses
+        t0 = time.perf_counter()
+        if args.workload == "shared_prefix":
+            w0 = wl.make_shared_prefix_workload()
+        else:
+            cfg0 = wl.CONFIGS[args.workload]
+            if args.block_size:
+                cfg0 = dataclasses.replace(cfg0, block_size=args.block_size)
+            w0 = wl.make_decode_workload(cfg0, contiguous=args.contiguous)
+        gen_s = time.perf_counter() - t0
+        if not args.no_cpu_baseline:
+            cpu = cpu_baseline(w0, args.cpu_budget)
+    pb.load_library()
     if args.swap_sweep:
         print(json.dumps({"swap_sweep": swap_sweep(torch, pb, args.swap_sweep, 5)}), flush=True)
         return 0
     if args.shape_sweep:
         print(json.dumps({"shape_sweep": shape_sweep(torch, pb, wl, 50)}), flush=True)
         return 0
-    if args.workload == "prefill":
-        return prefill_main(args, torch, pb, wl, dev)
     if args.workload in ("parallel_sampling", "beam_search", "shared_prefix") and (args.block_size or args.contiguous):
         raise SystemExit("--block-size/--contiguous apply to the drawn-length workloads")
     if args.workload == "parallel_sampling":
         c = loop_case(wl.ParallelSamplingWorkload(prompt_len=1016), 256, pb, dev, torch, max(args.steps, 10))
     elif args.workload == "beam_search":
         c = loop_case(wl.BeamSearchWorkload(), 64, pb, dev, torch, max(args.steps, 10))
-    elif args.workload == "shared_prefix":
-        c = decode_case(None, wl, pb, dev, shared_prefix=True)
     else:
-        import dataclasses
-        cfg0 = wl.CONFIGS[args.workload]
-        if args.block_size:
-            cfg0 = dataclasses.replace(cfg0, block_size=args.block_size)
-        c = decode_case(cfg0, wl, pb, dev, contiguous=args.contiguous)
+        c = decode_case(w0, pb, dev, gen_s)
     cfg, et = c.cfg, c.cfg.etype
     part = cfg.partition_size if args.partition is None else args.partition
     kc, vc, q, k_new, v_new, slots, bt, cl = c.kc, c.vc, c.q, c.k_new, c.v_new, c.slots, c.bt, c.cl
@@ -664,8 +736,8 @@ def main() -> int:
         ref = copy_reference(torch, dev)
         ref["decode_frac_of_copy"] = round(achieved / ref["GBps"], 4)
         result["copy_reference"] = ref
-    if not args.no_cpu_baseline and c.w is not None:
-        result["cpu_baseline"] = cpu_baseline(c.w, args.cpu_budget)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
     return 0
 
