@@ -15,7 +15,7 @@
  * context_lens, block_mapping and workspace are DEVICE pointers owned by the
  * caller; every one must be 16-byte aligned. The library allocates no memory
  * and keeps no state between calls apart from a per-device cache of device
- * properties. `stream` is a hipStream_t passed as void* (NULL = the default
+ * properties and the fixed per-device array of pa_decode_noalloc. `stream` is a hipStream_t passed as void* (NULL = the default
  * stream); every call only enqueues work on it and returns without
  * synchronising. The status covers host-side argument checks and launch
  * errors; device-side faults surface on a later synchronisation.
@@ -133,6 +133,28 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                     float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
                     pa_dtype dtype, pa_dtype out_dtype, void* stream);
+
+/*
+ * pa_decode_noalloc -- pa_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments without the workspace, the same
+ * kernels and a bit-identical result. Split sequences keep their partial
+ * results in a fixed array of PA_NOALLOC_SCRATCH_BYTES per device that the
+ * library owns (it is held on each device used until the process ends; its
+ * address is looked up on the first call on a device). Calls whose
+ * pa_decode_workspace_bytes exceeds that size return PA_ERR_WORKSPACE before
+ * touching the device (e.g. 512-token partitions of 16 sequences of 128K
+ * tokens with 64 query heads need 136 MB; their balanced split needs 35 MB).
+ * The array needs no initial contents. Every call on one device shares it,
+ * so calls that may overlap in time on one device (several streams, several
+ * host threads) race: serialise them. No memory is allocated by this call.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                            int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                            int32_t partition_size, pa_dtype dtype, pa_dtype out_dtype, void* stream);
 
 /* pa_decode with an explicit kernel family (pa_algo). Same contract. */
 pa_status pa_decode_ex(void* out, const void* q, const void* k_cache, const void* v_cache,

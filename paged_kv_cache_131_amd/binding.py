@@ -31,6 +31,8 @@ SIGNATURES = {
                          _p, _sz, _i32, _i32, _p]),
     "pa_decode_ex": (_i32, [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                             _p, _sz, _i32, _i32, _i32, _p]),
+    "pa_decode_noalloc": (_i32, [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                                 _i32, _i32, _i32, _p]),
     "pa_write_decode": (_i32, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                                _i32, _p, _sz, _i32, _i32, _p]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
@@ -169,6 +171,29 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_c
         *ptrs, S, Hq, Hkv, d, B, NB, block_tables.shape[1], int(max_context_len), float(scale), int(partition_size),
         ws_ptr, ws_bytes, DTYPE_CODE[dt], DTYPE_CODE[out.dtype], ALGO_CODE[algo], sh)
     _check("pa_decode", status)
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # PA_NOALLOC_SCRATCH_BYTES
+
+
+def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+                      partition_size=PA_PARTITION_AUTO, stream=None) -> None:
+    """pa_decode without a workspace argument: split sequences use the library's fixed per-device array
+    (calls that may overlap on one device race on it)."""
+    lib = load_library()
+    S, Hq, d = q.shape
+    NB, Hkv, B, _ = k_cache.shape
+    if out.shape != q.shape or v_cache.shape != (NB, Hkv, d, B) or k_cache.shape[3] != d:
+        raise ValueError("inconsistent shapes")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables must be [num_seqs][max_blocks], context_lens [num_seqs]")
+    dt = k_cache.dtype
+    ptrs = (_dev(out, "out"), _dev(q, "q", dt), _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
+            _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32))
+    status = lib.pa_decode_noalloc(*ptrs, S, Hq, Hkv, d, B, NB, block_tables.shape[1], int(max_context_len),
+                                   float(scale), int(partition_size), DTYPE_CODE[dt], DTYPE_CODE[out.dtype],
+                                   _stream(stream))
+    _check("pa_decode_noalloc", status)
 
 
 # ---------------------------------------------------------------------------

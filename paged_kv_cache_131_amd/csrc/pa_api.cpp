@@ -303,7 +303,7 @@ static pa_status decode_impl(void* out, const void* q, const void* k_new, const 
                              int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                              int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                              float scale, int32_t partition_size, void* workspace, size_t workspace_bytes, pa_dtype dtype,
-                             pa_dtype out_dtype, pa_algo algo, void* stream) {
+                             pa_dtype out_dtype, pa_algo algo, void* stream, bool static_workspace = false) {
   if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return PA_ERR_INVALID_ARG;
   if (algo != PA_ALGO_AUTO && algo != PA_ALGO_VECTOR && algo != PA_ALGO_MFMA) return PA_ERR_INVALID_ARG;
   if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads) return PA_ERR_INVALID_ARG;
@@ -340,6 +340,13 @@ static pa_status decode_impl(void* out, const void* q, const void* k_new, const 
 
   const Plan pl = make_plan(num_seqs, num_kv_heads, max_context_len, partition_size);
   const WorkspaceLayout wl = layout(pl, num_seqs, num_heads, num_kv_heads, head_dim);
+  if (static_workspace) {
+    // the library's fixed per-device array; looked up after every argument
+    // check, so a rejected call touches no device
+    if (wl.total > pa::kStaticScratchBytes) return PA_ERR_WORKSPACE;
+    if (pa::static_scratch(&workspace) != hipSuccess) return PA_ERR_LAUNCH;
+    workspace_bytes = pa::kStaticScratchBytes;
+  }
   if (wl.total > 0) {
     if (!workspace || workspace_bytes < wl.total) return PA_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return PA_ERR_INVALID_ARG;
@@ -415,6 +422,16 @@ pa_status pa_write_decode(void* out, const void* q, const void* k_new, const voi
   return decode_impl(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
                      num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len, scale,
                      partition_size, workspace, workspace_bytes, dtype, out_dtype, PA_ALGO_AUTO, stream);
+}
+
+pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                            int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                            int32_t partition_size, pa_dtype dtype, pa_dtype out_dtype, void* stream) {
+  return decode_impl(out, q, nullptr, nullptr, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len, scale,
+                     partition_size, nullptr, 0, dtype, out_dtype, PA_ALGO_AUTO, stream, true);
 }
 
 pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,

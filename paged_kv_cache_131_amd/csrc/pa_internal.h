@@ -59,6 +59,13 @@ struct DecodeParams {
 // Most finished segments a decode workgroup keeps in LDS before storing them.
 constexpr int kMaxResultSlots = 32;
 
+// Size of the library's own decode workspace for callers that cannot
+// allocate (one array per device, kept until the process ends).
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+// Device address of that array on the current device, looked up once per
+// device (hipGetSymbolAddress) and kept; an error leaves *ptr untouched.
+hipError_t static_scratch(void** ptr);
+
 // Launch the decode kernel for (elem, head_dim, algo, group bucket G),
 // grid = (workers per KV head, num_kv_heads), 64 threads per workgroup, then,
 // when `merge` is set or the call brings new tokens (k_new), the closing

@@ -25,7 +25,33 @@
 #include "pa_device.h"
 #include "pa_internal.h"
 
+// Decode workspace of pa_decode_noalloc: a fixed array per device, so that
+// callers that cannot allocate still get the split path. Host code never
+// passes this name to a kernel (on the host it is only a stand-in for the
+// symbol); it uses the device address static_scratch() looks up.
+static __device__ __align__(256) unsigned char scratch[pa::kStaticScratchBytes];
+
 namespace pa {
+
+hipError_t static_scratch(void** ptr) {
+  constexpr int kDevices = 64;
+  static std::mutex mu;
+  static void* addr[kDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
+
 namespace {
 
 // The length a decode works on: the stored one, cut to what the block

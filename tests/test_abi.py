@@ -83,6 +83,34 @@ def test_decode_argument_checks(lib, over, expected):
     assert lib.pa_decode_ex(*decode_args(**over)) == expected
 
 
+def noalloc_args(**over):
+    a = decode_args(**over)
+    return a[:16] + a[18:20] + [a[21]]   # no workspace, no algo
+
+
+@pytest.mark.parametrize("over,expected", [
+    (dict(q=None), INVALID),
+    (dict(Hq=30), INVALID),
+    (dict(d=96), UNSUPPORTED),
+    (dict(part=48), INVALID),
+    (dict(S=0), OK),
+    # 512-token partitions of 16 sequences of 128K tokens, 64/8 heads: 136 MB
+    # of partial results, above the fixed array; rejected before any device call
+    (dict(S=16, Hq=64, Hkv=8, maxL=131072, maxB=4096, B=32, part=512), WORKSPACE),
+])
+def test_decode_noalloc_argument_checks(lib, over, expected):
+    assert lib.pa_decode_noalloc(*noalloc_args(**over)) == expected
+
+
+def test_noalloc_scratch_limit_covers_the_balanced_split(lib):
+    f = lib.pa_decode_workspace_bytes
+    limit = pb.NOALLOC_SCRATCH_BYTES
+    assert f(256, 32, 8, 128, 8192, -1) <= limit           # Llama-3-8B-shaped batch
+    assert f(16, 64, 8, 128, 131072, -1) <= limit          # long context, balanced split
+    assert f(64, 40, 40, 128, 2048, -1) <= limit           # OPT-13B-shaped batch
+    assert f(16, 64, 8, 128, 131072, 512) > limit          # long context, 512-token partitions
+
+
 def test_decode_workspace_sizes(lib):
     f = lib.pa_decode_workspace_bytes
     assert f(4, 32, 8, 128, 1024, 0) == 0                  # single pass never splits

@@ -1,0 +1,67 @@
+"""pa_decode_noalloc (the decode without a workspace argument, for callers
+that cannot allocate) against pa_decode with a caller workspace: the same
+kernels, so the outputs are bit-identical, and both are within the decode
+tolerance of the oracle. Two calls in a row, the second on a smaller batch,
+share the library's fixed per-device array."""
+
+import ctypes
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_cache_131_amd import binding as pb
+from paged_kv_cache_131_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_case(w, part):
+    cfg = w.cfg
+    et = cfg.etype
+    kc, vc = pb.to_device(w.k_cache, et, DEV), pb.to_device(w.v_cache, et, DEV)
+    pb.pa_write_kv(pb.to_device(w.k_new, et, DEV), pb.to_device(w.v_new, et, DEV), kc, vc,
+                   pb.int32_to_device(w.slot_mapping, DEV))
+    q = pb.to_device(w.q, et, DEV)
+    bt, cl = pb.int32_to_device(w.block_tables, DEV), pb.int32_to_device(w.context_lens, DEV)
+    S, Hq, d = q.shape
+    NB, Hkv, B, _ = kc.shape
+    need = pb.pa_decode_workspace_bytes(S, Hq, Hkv, d, w.max_context_len, part)
+    assert 0 < need <= pb.NOALLOC_SCRATCH_BYTES
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    ref_out = torch.empty(q.shape, dtype=torch.float32, device=DEV)
+    pb.pa_decode(ref_out, q, kc, vc, bt, cl, cfg.scale, w.max_context_len, partition_size=part, workspace=ws)
+    got = torch.full(q.shape, float("nan"), dtype=torch.float32, device=DEV)
+    lib = pb.load_library()
+    st = lib.pa_decode_noalloc(got.data_ptr(), q.data_ptr(), kc.data_ptr(), vc.data_ptr(), bt.data_ptr(),
+                               cl.data_ptr(), S, Hq, Hkv, d, B, NB, bt.shape[1], w.max_context_len,
+                               ctypes.c_float(cfg.scale), part, pb.DTYPE_CODE[kc.dtype], pb.PA_F32,
+                               torch.cuda.current_stream().cuda_stream)
+    assert st == 0, pb.STATUS.get(st, st)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref_out), "pa_decode_noalloc differs from pa_decode"
+    kr, vr = oracle.write_kv(w.k_cache, w.v_cache, w.k_new, w.v_new, w.slot_mapping, B)
+    seqs = sorted(set(range(0, S, max(1, S // 12))) | {S - 1})
+    ref = oracle.decode(w.q, kr, vr, w.block_tables, w.context_lens, cfg.scale, B, et, seqs=seqs)
+    err = float(np.abs(got.cpu().numpy()[seqs].astype(np.float64) - ref[seqs]).max())
+    say(f"  noalloc {cfg.name} S={S} part={part}: bit-identical to pa_decode, max |gpu - oracle| = {err:.3e}")
+    assert err <= 2e-3
+
+
+@pytest.mark.parametrize("part", [-1, 256])
+def test_noalloc_matches_workspace_call_twice(part):
+    say(f"noalloc part={part}")
+    big = wl.make_decode_workload(wl.DecodeConfig("noalloc-a", 41, 96, 32, 8, 128, 16, "bf16", 1.0,
+                                                  ("uniform", 16, 3000), 3000))
+    small = wl.make_decode_workload(wl.DecodeConfig("noalloc-b", 42, 10, 16, 2, 64, 32, "f16", 1.0,
+                                                    ("fixed", (1, 33, 700, 64, 2000, 5, 31, 32, 129, 1500)), 2000))
+    run_case(big, part)
+    run_case(small, part)
