@@ -44,8 +44,8 @@ WORKLOAD_TEXT = {
     "beam_search": "beam search, last of 64 decode steps: 32 prompts of 1000 tokens x 4 beams, beams re-selected "
                    "every step (fork / release, copy-on-write of shared last blocks), 32 q / 8 kv heads, head_dim "
                    "128, block 16, bf16",
-    "shared_prefix": "shared prefix: 256 requests mapping one 1024-token prompt prefix plus own suffixes of U[16, 512] "
-                     "tokens, 32 q / 8 kv heads, head_dim 128, block 16, bf16",
+    "shared_prefix": "shared prefix: 256 requests mapping one {prefix}-token prompt prefix plus own suffixes of "
+                     "U[16, 512] tokens, 32 q / 8 kv heads, head_dim 128, block 16, bf16",
     "prefill": "prompt phase: 32 whole prompts, lengths lognormal(median 800, sigma 1) clipped to [16, 8192], causal "
                "attention over their K/V in the paged pool, 32 q / 8 kv heads, head_dim 128, block 16, bf16, "
                "shuffled pool",
@@ -251,22 +251,43 @@ def unique_kv_bytes(c, tables, lens) -> int:
     return sum(reads.values()) * c.num_kv_heads * c.head_dim * 2 * es
 
 
-def decode_case(w, pb, dev, gen_s: float) -> Case:
-    """Device copies of a generated decode workload."""
+def decode_case(w, pb, dev, gen_s: float, torch=None, reps: int = 10) -> Case:
+    """Device copies of a generated decode workload. A workload with
+    copy-on-write pairs (a shared prefix ending inside a block) gets its
+    copies -- timed here on their own -- and the writes into the copies
+    before the timed decode steps, as the steps that made them would have."""
     c = Case()
     cfg = w.cfg
     c.gen_s = gen_s
     et = cfg.etype
     c.w, c.cfg = w, cfg
+    c.extra = {}
     c.kc, c.vc = pb.to_device(w.k_cache, et, dev), pb.to_device(w.v_cache, et, dev)
+    if w.copy_pairs is not None:
+        pairs = pb.int32_to_device(w.copy_pairs, dev)
+        for _ in range(3):   # idempotent until the writes below
+            pb.pa_copy_blocks(c.kc, c.vc, pairs)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            pb.pa_copy_blocks(c.kc, c.vc, pairs)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        P = w.copy_pairs.shape[0]
+        nbytes = 2 * P * cfg.num_kv_heads * cfg.block_size * cfg.head_dim * 2 * 2 + 8 * P
+        c.extra["copy_blocks"] = {"pairs": P, "avg_ms": round(ms, 5), "bytes": nbytes,
+                                  "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+        pb.pa_write_kv(pb.to_device(w.pre_k, et, dev), pb.to_device(w.pre_v, et, dev), c.kc, c.vc,
+                       pb.int32_to_device(w.pre_slots, dev))
+        torch.cuda.synchronize()
     c.q = pb.to_device(w.q, et, dev)
     c.k_new, c.v_new = pb.to_device(w.k_new, et, dev), pb.to_device(w.v_new, et, dev)
     c.slots = pb.int32_to_device(w.slot_mapping, dev)
     c.bt, c.cl = pb.int32_to_device(w.block_tables, dev), pb.int32_to_device(w.context_lens, dev)
-    c.copy_pairs = np.zeros((0, 2), np.int32)  # no shared blocks in this workload
+    c.copy_pairs = np.zeros((0, 2), np.int32)  # the timed step has no copies
     c.context_lens, c.max_len = w.context_lens, w.max_context_len
     c.unique_kv = unique_kv_bytes(cfg, w.block_tables, w.context_lens)
-    c.extra = {}
     return c
 
 
@@ -575,6 +596,9 @@ def main() -> int:
     ap.add_argument("--contiguous", action="store_true",
                     help="hand out the pool's blocks in order instead of the seeded shuffled order")
     ap.add_argument("--two-calls", action="store_true", help="time pa_write_kv + pa_decode instead of the fused call")
+    ap.add_argument("--prefix-len", type=int, default=1024,
+                    help="shared_prefix: tokens of the shared prefix (not a multiple of 16: copy-on-write of its "
+                         "last block)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold", type=int, default=20, metavar="N",
                     help="also time N single steps, each after evicting the caches (0: skip)")
@@ -611,7 +635,7 @@ def main() -> int:
         import dataclasses
         t0 = time.perf_counter()
         if args.workload == "shared_prefix":
-            w0 = wl.make_shared_prefix_workload()
+            w0 = wl.make_shared_prefix_workload(prefix_len=args.prefix_len)
         else:
             cfg0 = wl.CONFIGS[args.workload]
             if args.block_size:
@@ -634,7 +658,7 @@ def main() -> int:
     elif args.workload == "beam_search":
         c = loop_case(wl.BeamSearchWorkload(), 64, pb, dev, torch, max(args.steps, 10))
     else:
-        c = decode_case(w0, pb, dev, gen_s)
+        c = decode_case(w0, pb, dev, gen_s, torch, max(args.steps, 10))
     cfg, et = c.cfg, c.cfg.etype
     part = cfg.partition_size if args.partition is None else args.partition
     kc, vc, q, k_new, v_new, slots, bt, cl = c.kc, c.vc, c.q, c.k_new, c.v_new, c.slots, c.bt, c.cl
@@ -704,7 +728,7 @@ def main() -> int:
         "dtype": et,
         "data": "synthetic",
         "config": {
-            "workload": WORKLOAD_TEXT[args.workload],
+            "workload": WORKLOAD_TEXT[args.workload].format(prefix=args.prefix_len),
             "num_seqs": len(c.context_lens),
             "context_tokens": int(c.context_lens.astype(np.int64).sum()),
             "max_context_len": max_len,

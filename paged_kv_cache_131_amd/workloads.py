@@ -178,6 +178,14 @@ class DecodeWorkload:
     num_blocks: int
     poison_block: int
     used_blocks: np.ndarray = field(default=None)
+    # Copy-on-write replay (a shared prefix that ends inside a block): the
+    # pools then hold the state before the copies. Apply copy_pairs, then
+    # store pre_k/pre_v at pre_slots (the tokens that landed in the copies),
+    # then the new token.
+    copy_pairs: np.ndarray = field(default=None)
+    pre_slots: np.ndarray = field(default=None)
+    pre_k: np.ndarray = field(default=None)
+    pre_v: np.ndarray = field(default=None)
 
     @property
     def etype(self):
@@ -484,7 +492,14 @@ def make_shared_prefix_workload(prefix_len: int = 1024, cfg: DecodeConfig = SHAR
     shared system prompt): the prefix is prefilled once and its blocks are
     mapped into every request (forks, reference counts raised); each request
     then holds its own suffix of a drawn length, whose last token is the new
-    one. A block-aligned prefix needs no copy."""
+    one. The prefix stays reserved (its own reference is kept), so its last
+    block is copy-on-write for every request ("PagedAttention 论文精读笔记"
+    §6.3). A block-aligned prefix needs no copy. A prefix that ends inside a
+    block makes each request copy that block at its first suffix token: the
+    pools are then returned as they were before those copies (targets
+    poisoned, the shared block valid up to the prefix's end), with the copy
+    pairs and the suffix tokens that landed in the copies (new token
+    excluded) to replay."""
     seqs = np.random.SeedSequence(1000 + cfg.index).spawn(6)
     rng_len, rng_pool = np.random.default_rng(seqs[0]), np.random.default_rng(seqs[1])
     suffix = draw_lengths(cfg, rng_len)
@@ -503,26 +518,42 @@ def make_shared_prefix_workload(prefix_len: int = 1024, cfg: DecodeConfig = SHAR
     poison_block = int(bm.free[-1])
     tables = np.full((cfg.num_seqs, max_blocks), poison_block, dtype=np.int32)
     slots = np.empty(cfg.num_seqs, dtype=np.int32)
-    copies = 0
+    r = prefix_len % B
+    pairs, pre_slots = [], []
     for s in range(cfg.num_seqs):
         seq = bm.fork(root)
-        for _ in range(int(suffix[s])):
+        n_suf = int(suffix[s])
+        for i in range(n_suf):
             slot, copy = bm.append_token(seq)
-            copies += copy is not None
+            if copy is not None:
+                pairs.append(copy)
+            if r and i < B - r and i < n_suf - 1:   # landed in the copy, before the new token
+                pre_slots.append(slot)
         tables[s, :len(seq.block_table)] = seq.block_table
         slots[s] = slot
-    if copies and prefix_len % B == 0:
+    if pairs and r == 0:
         raise AssertionError("a block-aligned prefix must not be copied")
-    used = np.array(sorted(set(tables[tables != poison_block].tolist())), dtype=np.int64)
+    if r and len(pairs) != cfg.num_seqs:
+        raise AssertionError("every request copies the reserved prefix's partial last block")
+    copy_pairs = np.array(pairs, dtype=np.int32).reshape(-1, 2) if r else None
+    pre = np.array(pre_slots, dtype=np.int32) if r else None
+    # the reserved prefix's blocks are held too (its partial last block is
+    # the copies' source, mapped by no request any more)
+    used = np.array(sorted(set(tables[tables != poison_block].tolist()) | set(root.block_table)), dtype=np.int64)
     if not values:
-        return DecodeWorkload(cfg, None, None, None, tables, lens, None, None, slots, num_blocks, poison_block, used)
+        return DecodeWorkload(cfg, None, None, None, tables, lens, None, None, slots, num_blocks, poison_block, used,
+                              copy_pairs, pre)
     Hkv, d = cfg.num_kv_heads, cfg.head_dim
     q = random_stored(seqs[2], (cfg.num_seqs, cfg.num_heads, d), cfg.etype, cfg.value_scale)
     k_cache = random_stored(seqs[3], (num_blocks, Hkv, B, d), cfg.etype, cfg.value_scale)
     v_cache = random_stored(seqs[4], (num_blocks, Hkv, d, B), cfg.etype, cfg.value_scale)
-    kn_ss, vn_ss = seqs[5].spawn(2)
+    kn_ss, vn_ss, pk_ss, pv_ss = seqs[5].spawn(4)
     k_new = random_stored(kn_ss, (cfg.num_seqs, Hkv, d), cfg.etype, cfg.value_scale)
     v_new = random_stored(vn_ss, (cfg.num_seqs, Hkv, d), cfg.etype, cfg.value_scale)
+    pre_k = pre_v = None
+    if r:
+        pre_k = random_stored(pk_ss, (len(pre), Hkv, d), cfg.etype, cfg.value_scale)
+        pre_v = random_stored(pv_ss, (len(pre), Hkv, d), cfg.etype, cfg.value_scale)
     if poison:
         pv = poison_value(cfg.etype)
         held = np.zeros(num_blocks, dtype=bool)
@@ -534,7 +565,15 @@ def make_shared_prefix_workload(prefix_len: int = 1024, cfg: DecodeConfig = SHAR
             off = (int(lens[s]) - 1) % B          # the new token's slot and the rest
             k_cache[last, :, off:, :] = pv
             set_v_tokens(v_cache, last, off, pv)
-    return DecodeWorkload(cfg, q, k_cache, v_cache, tables, lens, k_new, v_new, slots, num_blocks, poison_block, used)
+        if r:
+            # before the copies: targets unwritten, the shared block valid up to the prefix's end
+            k_cache[copy_pairs[:, 1]] = pv
+            v_cache[copy_pairs[:, 1]] = pv
+            src = int(copy_pairs[0, 0])
+            k_cache[src, :, r:, :] = pv
+            set_v_tokens(v_cache, src, r, pv)
+    return DecodeWorkload(cfg, q, k_cache, v_cache, tables, lens, k_new, v_new, slots, num_blocks, poison_block, used,
+                          copy_pairs, pre, pre_k, pre_v)
 
 
 # --------------------------------------------------------------------------

@@ -205,3 +205,80 @@ def test_swap_group_out_and_in():
         assert ps.bm.refcount[new_of[b]] == n
     with pytest.raises(PoolExhausted):
         ps.bm.swap_out(ps.seqs[:8], SwapSpace(1))
+
+
+def test_figure9_beam_sharing_through_the_block_manager(golden_dir):
+    """The pages' Figure 9 beam pattern (k = 4), driven through BlockManager:
+    tables, reference counts, recycled blocks and copy-on-write pairs as the
+    fixture derives them from the pages' rules."""
+    import json
+    import os
+
+    g = json.load(open(os.path.join(golden_dir, "figure9_beam.json")))
+    bm = BlockManager(len(g["free_order"]), g["block_size"], free_order=g["free_order"])
+    root = bm.new_sequence()
+    for _ in range(g["prompt_tokens"]):
+        assert bm.append_token(root)[1] is None
+    seqs = {"c0": bm.fork(root), "c3": bm.fork(root)}
+    bm.free_sequence(root)
+    assert bm.append_token(seqs["c3"])[1] is None
+    for _ in range(8):
+        assert bm.append_token(seqs["c0"])[1] is None
+    seqs["c1"], seqs["c2"] = bm.fork(seqs["c0"]), bm.fork(seqs["c0"])
+    for name in ("c0", "c1", "c2"):
+        assert bm.append_token(seqs[name])[1] is None
+    assert {k: seqs[k].block_table for k in g["figure9_tables"]} == g["figure9_tables"]
+    assert {str(b): bm.refcount[b] for b in range(bm.num_blocks)} == g["figure9_refcounts"]
+    used = {b for s in seqs.values() for b in s.block_table}
+    assert len(used) == g["blocks_used_shared"]
+    assert sum(len(s.block_table) for s in seqs.values()) == g["blocks_used_without_sharing"]
+    assert bm.num_free == 0
+    for name in g["drop"]:
+        bm.free_sequence(seqs.pop(name))
+    assert list(bm.free) == g["recycled_in_order"]
+    assert {str(b): bm.refcount[b] for b in range(bm.num_blocks)} == g["refcounts_after_drop"]
+    seqs["n1"], seqs["n2"] = bm.fork(seqs["c1"]), bm.fork(seqs["c2"])
+    for step in g["appends"]:
+        slot, copy = bm.append_token(seqs[step["seq"]])
+        assert slot == step["slot"], step
+        assert (list(copy) if copy else None) == step["copy"], step
+    assert {k: seqs[k].block_table for k in g["final_tables"]} == g["final_tables"]
+    assert {str(b): bm.refcount[b] for b in range(bm.num_blocks)} == g["final_refcounts"]
+
+
+def test_shared_prefix_ending_inside_a_block():
+    """A 1000-token prefix (62 blocks + 8 tokens at B = 16): the prefix stays
+    reserved, so every request copies its partial last block at its first
+    suffix token (one pair per request, one source), and its next 8 tokens
+    land in that copy; a block-aligned prefix issues no copy."""
+    w = wl.make_shared_prefix_workload(prefix_len=1000, values=False)
+    S, B = w.cfg.num_seqs, 16
+    assert w.copy_pairs.shape == (S, 2)
+    src = int(w.copy_pairs[0, 0])
+    assert (w.copy_pairs[:, 0] == src).all() and len(set(w.copy_pairs[:, 1].tolist())) == S
+    assert (w.block_tables[:, 1000 // B] == w.copy_pairs[:, 1]).all()     # each request maps its own copy
+    assert (w.block_tables[:, :1000 // B] == w.block_tables[0, :1000 // B]).all()
+    assert len(w.pre_slots) == S * (B - 1000 % B)
+    assert set((w.pre_slots // B).tolist()) == set(w.copy_pairs[:, 1].tolist())
+    assert (w.pre_slots % B >= 1000 % B).all()
+    aligned = wl.make_shared_prefix_workload(prefix_len=1024, values=False)
+    assert aligned.copy_pairs is None
+
+
+def test_shared_prefix_replay_reads_no_poison():
+    """Replaying the mid-block prefix's copies and writes on the oracle's
+    pools gives every sampled context finite K/V: the copies bring the
+    prefix's tokens, the writes fill the rest, nothing poisoned is read."""
+    import oracle
+    from oracle.paged_attention import gather_sequence
+
+    w = wl.make_shared_prefix_workload(prefix_len=1000)
+    k, v = oracle.copy_blocks(w.k_cache, w.v_cache, w.copy_pairs)
+    k, v = oracle.write_kv(k, v, w.pre_k, w.pre_v, w.pre_slots, 16, inplace=True)
+    k, v = oracle.write_kv(k, v, w.k_new, w.v_new, w.slot_mapping, 16, inplace=True)
+    src = int(w.copy_pairs[0, 0])
+    for s in (0, 77, 255):
+        keys, values = gather_sequence(k, v, w.block_tables[s], int(w.context_lens[s]), 3, 16, "bf16")
+        assert np.isfinite(keys).all() and np.isfinite(values).all()
+        dst = int(w.copy_pairs[s, 1])
+        np.testing.assert_array_equal(k[dst, :, :1000 % 16], w.k_cache[src, :, :1000 % 16])
