@@ -64,12 +64,28 @@ typedef enum pa_status {
 typedef enum pa_algo { PA_ALGO_AUTO = 0, PA_ALGO_VECTOR = 1, PA_ALGO_MFMA = 2 } pa_algo;
 
 /* partition_size values for pa_decode besides a positive multiple of 32:
- *  PA_PARTITION_AUTO: the context of every (sequence, KV head) is cut so that
- *                     every worker wave gets the same number of 32-token
- *                     chunks (split points fall anywhere in the batch);
- *  PA_PARTITION_NONE: one wave per (sequence, KV head), no split. */
+ *  PA_PARTITION_AUTO:   the context of every (sequence, KV head) is cut so
+ *                       that every worker wave gets the same number of
+ *                       32-token chunks (split points fall anywhere in the
+ *                       batch);
+ *  PA_PARTITION_NONE:   one wave per (sequence, KV head), no split;
+ *  PA_PARTITION_SHARED: as AUTO, and adjacent sequences that map the same
+ *                       physical blocks at the same logical positions from
+ *                       position 0 on (forks of one prompt: parallel
+ *                       samples, beams, requests on a shared prefix,
+ *                       [notes-zh] §6.1-§6.3) form families of up to
+ *                       2 * (16 / g) sequences (g = num_heads /
+ *                       num_kv_heads) whose common prefix, in whole 32-token
+ *                       chunks and at least 64 tokens, is read once and
+ *                       attended for all members at once. Only the block ids
+ *                       decide (the kernels see nothing else, [notes-zh]
+ *                       §6.4); the result is the same attention. It adds two
+ *                       planning launches and needs a larger workspace.
+ *                       16-bit elements, the MFMA engine and at most 1024
+ *                       sequences; otherwise the call runs as AUTO. */
 #define PA_PARTITION_AUTO (-1)
 #define PA_PARTITION_NONE 0
+#define PA_PARTITION_SHARED (-2)
 
 /*
  * pa_write_kv -- store new K/V rows into their slots ("fused reshape and
@@ -108,9 +124,11 @@ pa_status pa_write_kv(const void* k_new, const void* v_new, void* k_cache, void*
  *                  are clamped into range (the result is then unspecified,
  *                  but no memory outside the pools is read).
  *   context_lens : [num_seqs] int32. L is clamped to
- *                  max_blocks_per_seq*block_size; L <= 0 writes zeros.
- *   max_context_len : host-side upper bound of context_lens (sizes the work).
- *   partition_size  : PA_PARTITION_AUTO, PA_PARTITION_NONE, or a positive
+ *                  min(max_blocks_per_seq*block_size, max_context_len) in
+ *                  every split mode; L <= 0 writes zeros.
+ *   max_context_len : host-side upper bound of context_lens (sizes the work;
+ *                  a longer context is cut to it).
+ *   partition_size  : PA_PARTITION_AUTO, PA_PARTITION_SHARED, PA_PARTITION_NONE, or a positive
  *                  multiple of 32: fixed partitions of that many tokens per
  *                  (sequence, KV head), merged by their max and sum of
  *                  exponentials ([review-en] "How does this work?": compute
@@ -178,9 +196,9 @@ pa_status pa_decode_ex(void* out, const void* q, const void* k_cache, const void
  * The block of position L-1 must not be shared with another sequence of the
  * call (copy-on-write has already made it private, [notes-zh] §6.1). No
  * write is made for a sequence with L <= 0, with L beyond
- * max_blocks_per_seq*block_size (or, with fixed partitions, beyond
- * max_context_len), or whose table entry for position L-1 is not a block of
- * the pool (its output is then unspecified, as with any invalid entry).
+ * max_blocks_per_seq*block_size or max_context_len, or whose table entry for
+ * position L-1 is not a block of the pool (its output is then unspecified,
+ * as with any invalid entry).
  * k_new/v_new: device, 16-byte aligned, both given. Workspace as for
  * pa_decode.
  */

@@ -36,10 +36,27 @@ struct Plan {
   size_t slots;     // partial-result slots (0 = never split)
 };
 
+// Shared mode takes at most kSharedMaxSeqs sequences and keeps chunk
+// counts in int; otherwise the call runs the balanced split.
+bool shared_ok(int num_seqs, int max_context_len) {
+  const long long max_chunks = ((long long)max_context_len + pa::kChunk - 1) / pa::kChunk;
+  return num_seqs <= pa::kSharedMaxSeqs && (long long)num_seqs * max_chunks < (1LL << 30);
+}
+
 Plan make_plan(int num_seqs, int num_kv_heads, int max_context_len, int partition_size) {
   Plan pl{pa::kModeFixed, 1, 1, 0, 0};
   const long long max_chunks = ((long long)max_context_len + pa::kChunk - 1) / pa::kChunk;
-  if (partition_size == PA_PARTITION_AUTO && num_seqs <= pa::kMaxBalancedSeqs) {
+  if (partition_size == PA_PARTITION_SHARED && shared_ok(num_seqs, max_context_len)) {
+    pl.mode = pa::kModeShared;
+    const long long wmax = (pa::kSharedMaxWorkersTotal + num_kv_heads - 1) / num_kv_heads;
+    const long long cap = (long long)num_seqs * max_chunks;
+    pl.max_workers = (int)(wmax < cap ? wmax : cap);
+    if (pl.max_workers < 1) pl.max_workers = 1;
+    pl.slots = (size_t)pl.max_workers + 2 * (size_t)num_seqs;  // ordinary pieces: worker + item
+    return pl;
+  }
+  if ((partition_size == PA_PARTITION_AUTO || partition_size == PA_PARTITION_SHARED) &&
+      num_seqs <= pa::kMaxBalancedSeqs) {
     pl.mode = pa::kModeBalanced;
     const long long wmax = (pa::kMaxWorkersTotal + num_kv_heads - 1) / num_kv_heads;
     const long long cap = (long long)num_seqs * max_chunks;
@@ -65,20 +82,53 @@ Plan make_plan(int num_seqs, int num_kv_heads, int max_context_len, int partitio
 }
 
 struct WorkspaceLayout {
-  size_t meta, ml, acc, total;
+  size_t meta, items, wrec, links, ml, acc, total;
+  int fam_base, fam_max;  // shared mode: first family slot, sub-slots per family slot
 };
 
+// Workspace: split records, then (shared mode) the plan's items, worker
+// records and prefix links, then (m, l) and the partial outputs of every
+// slot. Shared mode
+// adds a family region after the ordinary slots: family slot (worker +
+// family index) holds fam_max sub-slots, one per member.
 WorkspaceLayout layout(const Plan& pl, int num_seqs, int num_heads, int num_kv_heads, int head_dim) {
-  WorkspaceLayout w{0, 0, 0, 0};
+  WorkspaceLayout w{0, 0, 0, 0, 0, 0, 0, 0, 0};
   if (pl.slots == 0) return w;
-  const size_t meta = round_up((size_t)num_seqs * 2 * sizeof(int32_t));
-  const size_t ml = round_up(pl.slots * (size_t)num_heads * 2 * sizeof(float));
-  const size_t acc = round_up(pl.slots * (size_t)num_heads * head_dim * sizeof(float));
+  const bool shared = pl.mode == pa::kModeShared;
+  size_t slots = pl.slots;
+  if (shared) {
+    w.fam_base = (int)pl.slots;
+    w.fam_max = pa::shared_family_max(num_heads / num_kv_heads);
+    slots += ((size_t)pl.max_workers + (size_t)num_seqs / 2 + 1) * (size_t)w.fam_max;
+  }
+  const size_t meta = round_up((size_t)num_seqs * (shared ? 4 : 2) * sizeof(int32_t));
+  const size_t items = shared ? round_up((size_t)num_seqs * 2 * pa::kItemInts * sizeof(int32_t)) : 0;
+  const size_t wrec = shared ? round_up((size_t)pl.max_workers * pa::kWorkerInts * sizeof(int32_t)) : 0;
+  const size_t links = shared ? round_up((size_t)num_seqs * sizeof(int32_t)) : 0;
+  const size_t ml = round_up(slots * (size_t)num_heads * 2 * sizeof(float));
+  const size_t acc = round_up(slots * (size_t)num_heads * head_dim * sizeof(float));
   w.meta = 0;
-  w.ml = meta;
-  w.acc = meta + ml;
-  w.total = meta + ml + acc;
+  w.items = meta;
+  w.wrec = meta + items;
+  w.links = w.wrec + wrec;
+  w.ml = w.links + links;
+  w.acc = w.ml + ml;
+  w.total = w.acc + acc;
   return w;
+}
+
+// Bytes a call with these sizes needs: shared mode also covers the
+// balanced split it falls back to for fp32 elements or the vector engine.
+size_t workspace_need(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int max_context_len,
+                      int partition_size) {
+  const Plan pl = make_plan(num_seqs, num_kv_heads, max_context_len, partition_size);
+  size_t need = layout(pl, num_seqs, num_heads, num_kv_heads, head_dim).total;
+  if (pl.mode == pa::kModeShared) {
+    const Plan bal = make_plan(num_seqs, num_kv_heads, max_context_len, PA_PARTITION_AUTO);
+    const size_t b = layout(bal, num_seqs, num_heads, num_kv_heads, head_dim).total;
+    if (b > need) need = b;
+  }
+  return need;
 }
 
 bool decode_shape_ok(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int max_context_len,
@@ -86,7 +136,7 @@ bool decode_shape_ok(int num_seqs, int num_heads, int num_kv_heads, int head_dim
   if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads) return false;
   if (head_dim != 64 && head_dim != 128) return false;
   if (max_context_len < 1) return false;
-  if (partition_size < PA_PARTITION_AUTO) return false;
+  if (partition_size < PA_PARTITION_SHARED) return false;
   if (partition_size > 0 && partition_size % pa::kChunk) return false;
   return true;
 }
@@ -97,7 +147,7 @@ constexpr int kMfmaWavesPerCu = 4;
 std::mutex g_mutex;
 int g_cus[kMaxDevices];
 int g_lds_per_cu[kMaxDevices];
-int g_waves[kMaxDevices][3][2][3][9];  // [device][elem][head_dim 64/128][algo][G]
+int g_waves[kMaxDevices][3][2][4][9];  // [device][elem][head_dim 64/128][algo][G]
 
 // Balanced-split workers for one launch (all KV heads). The MFMA engine runs
 // one wave per SIMD: measured on MI355X, more resident waves of it split the
@@ -121,7 +171,7 @@ int workers_target(int elem, int head_dim, int algo, int G, size_t* lds_per_work
   if (waves == 0) {
     waves = pa::decode_waves_per_cu(elem, head_dim, algo, G);
     if (waves < 1) waves = 8;
-    if (algo == pa::kAlgoMfma && waves > kMfmaWavesPerCu) waves = kMfmaWavesPerCu;
+    if ((algo == pa::kAlgoMfma || algo == pa::kAlgoMfmaShared) && waves > kMfmaWavesPerCu) waves = kMfmaWavesPerCu;
   }
   *lds_per_workgroup = (size_t)g_lds_per_cu[dev] / (size_t)waves;
   return g_cus[dev] * waves;
@@ -188,8 +238,7 @@ int32_t pa_abi_version(void) { return kAbiVersion; }
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                                  int32_t max_context_len, int32_t partition_size) {
   if (!decode_shape_ok(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, partition_size)) return 0;
-  const Plan pl = make_plan(num_seqs, num_kv_heads, max_context_len, partition_size);
-  return layout(pl, num_seqs, num_heads, num_kv_heads, head_dim).total;
+  return workspace_need(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, partition_size);
 }
 
 pa_status pa_write_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
@@ -309,7 +358,7 @@ static pa_status decode_impl(void* out, const void* q, const void* k_new, const 
   if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads) return PA_ERR_INVALID_ARG;
   if (num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
   if (max_context_len < 1 || num_blocks < 1 || max_blocks_per_seq < 1) return PA_ERR_INVALID_ARG;
-  if (partition_size < PA_PARTITION_AUTO || (partition_size > 0 && partition_size % pa::kChunk))
+  if (partition_size < PA_PARTITION_SHARED || (partition_size > 0 && partition_size % pa::kChunk))
     return PA_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
   const int log2b = log2_exact(block_size);
@@ -338,7 +387,11 @@ static pa_status decode_impl(void* out, const void* q, const void* k_new, const 
   }
   const int G = kernel_algo == pa::kAlgoMfma ? 0 : (group <= 1 ? 1 : group <= 2 ? 2 : group <= 4 ? 4 : 8);
 
-  const Plan pl = make_plan(num_seqs, num_kv_heads, max_context_len, partition_size);
+  Plan pl = make_plan(num_seqs, num_kv_heads, max_context_len, partition_size);
+  if (pl.mode == pa::kModeShared) {
+    if (kernel_algo == pa::kAlgoMfma) kernel_algo = pa::kAlgoMfmaShared;
+    else pl = make_plan(num_seqs, num_kv_heads, max_context_len, PA_PARTITION_AUTO);  // vector engine: balanced
+  }
   const WorkspaceLayout wl = layout(pl, num_seqs, num_heads, num_kv_heads, head_dim);
   if (static_workspace) {
     // the library's fixed per-device array; looked up after every argument
@@ -365,6 +418,14 @@ static pa_status decode_impl(void* out, const void* q, const void* k_new, const 
   p.ws_meta = wl.total ? reinterpret_cast<int32_t*>(ws + wl.meta) : nullptr;
   p.ws_ml = wl.total ? reinterpret_cast<float*>(ws + wl.ml) : nullptr;
   p.ws_acc = wl.total ? reinterpret_cast<float*>(ws + wl.acc) : nullptr;
+  const bool shared = pl.mode == pa::kModeShared;
+  p.items = shared ? reinterpret_cast<int32_t*>(ws + wl.items) : nullptr;
+  p.wrec = shared ? reinterpret_cast<int32_t*>(ws + wl.wrec) : nullptr;
+  p.links = shared ? reinterpret_cast<int32_t*>(ws + wl.links) : nullptr;
+  p.fam_base = wl.fam_base;
+  p.fam_max = wl.fam_max;
+  p.meta_stride = shared ? 4 : 2;
+  p.max_len = max_context_len;
   p.num_seqs = num_seqs;
   p.num_heads = num_heads;
   p.num_kv_heads = num_kv_heads;
@@ -383,16 +444,20 @@ static pa_status decode_impl(void* out, const void* q, const void* k_new, const 
   long long workers;
   size_t lds_per_workgroup = 0;
   const int target = workers_target(elem, head_dim, kernel_algo, G, &lds_per_workgroup);
-  if (pl.mode == pa::kModeBalanced || pl.mode == pa::kModeFixedStream) {
+  if (pl.mode == pa::kModeBalanced || pl.mode == pa::kModeFixedStream || shared) {
     // rounded down: every worker of the grid must be resident at once, or
     // the ones left over start only when others finish
     workers = target / num_kv_heads;
-    const long long cap = pl.mode == pa::kModeBalanced ? pl.max_workers : (long long)num_seqs * pl.max_parts;
+    const long long cap = pl.mode == pa::kModeFixedStream ? (long long)num_seqs * pl.max_parts : pl.max_workers;
     if (workers > cap) workers = cap;
     if (workers < 1) workers = 1;
   } else {
     workers = (long long)num_seqs * pl.max_parts;
     if (workers > INT_MAX) return PA_ERR_UNSUPPORTED;
+  }
+  if (shared) {
+    const hipError_t e = pa::launch_plan(p, (unsigned)workers, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return PA_ERR_LAUNCH;
   }
   const hipError_t e = pa::launch_decode(p, elem, head_dim, kernel_algo, G, (unsigned)workers, pl.slots > 0,
                                          lds_per_workgroup, static_cast<hipStream_t>(stream));

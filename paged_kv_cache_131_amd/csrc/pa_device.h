@@ -32,6 +32,22 @@ __device__ __forceinline__ u32x4 load16_stream(const void* ptr) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Max and sum of x over lanes l, l^16, l^32, l^48 (the four lanes holding
+// one MFMA column), by lane-swap instructions (no LDS round trip).
+__device__ __forceinline__ float max_over_column(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float sum_over_column(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // V tiles are stored as sub-tiles [block_size/Bs][head_dim][Bs]: Bs = 32 for
 // a block_size that is a multiple of 32 above 32, else Bs = block_size (a
 // plain [head_dim][block_size] tile). The element of channel c and in-block
@@ -144,6 +160,28 @@ __device__ __forceinline__ void store_out(void* out, size_t idx, float v, int ou
     static_cast<_Float16*>(out)[idx] = static_cast<_Float16>(v);
   } else {
     static_cast<__bf16*>(out)[idx] = static_cast<__bf16>(v);
+  }
+}
+
+// Four consecutive outputs (idx a multiple of 4) converted one by one as
+// store_out does; `vec`: `out` is aligned for one 16-byte (fp32) or 8-byte
+// (16-bit) store of the four.
+__device__ __forceinline__ void store_out4(void* out, size_t idx, f32x4 v, int out_dtype, bool vec) {
+  if (!vec) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) store_out(out, idx + e, v[e], out_dtype);
+  } else if (out_dtype == kF32) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(out) + idx) = v;
+  } else {
+    uint16_t h[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      h[e] = out_dtype == kF16 ? __builtin_bit_cast(uint16_t, static_cast<_Float16>(v[e]))
+                               : __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[e]));
+    uint2 w;
+    w.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+    w.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + idx) = w;
   }
 }
 

@@ -23,8 +23,23 @@ enum Elem : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 // Balanced: chunk ranges per persistent worker. Fixed: one workgroup per
 // partition. FixedStream: fixed partitions taken in ranges by persistent
 // workers.
-enum Mode : int { kModeBalanced = 0, kModeFixed = 1, kModeFixedStream = 2 };
-enum Algo : int { kAlgoVector = 1, kAlgoMfma = 2 };
+enum Mode : int { kModeBalanced = 0, kModeFixed = 1, kModeFixedStream = 2, kModeShared = 3 };
+
+// Shared mode (balanced split over work items, where adjacent sequences
+// that map the same blocks from position 0 on form families whose common
+// prefix is attended once for all members).
+constexpr int kSharedMaxSeqs = 1024;      // sequences a shared-mode call takes (the plan's LDS)
+constexpr int kSharedColumnGroups = 2;    // 16-column MFMA groups of a family segment
+constexpr int kSharedMinChunks = 2;       // a shorter common prefix does not form a family
+constexpr int kSharedMaxWorkersTotal = 2048;  // workers summed over KV heads (sizes the workspace)
+constexpr int kItemInts = 4;              // ints per work item record
+constexpr int kWorkerInts = 12;           // ints per worker record: range, first item, its record
+// Most members of a family: column groups times the members one 16-column
+// group holds (a member takes g columns, one per query head).
+inline int shared_family_max(int group) { return kSharedColumnGroups * (16 / group); }
+// kAlgoMfmaShared: the MFMA engine with kSharedColumnGroups column groups
+// (shared mode only).
+enum Algo : int { kAlgoVector = 1, kAlgoMfma = 2, kAlgoMfmaShared = 3 };
 
 struct DecodeParams {
   void* out;
@@ -54,6 +69,14 @@ struct DecodeParams {
   int32_t merge;        // set by launch_decode: some sequence is split and needs merging
   int32_t lens_pad;     // set by launch_decode: ints of dynamic LDS holding the lengths
   int32_t res_slots;    // set by launch_decode: finished segments the LDS result buffer holds
+  int32_t max_len;      // host bound of the context lengths: longer ones are cut to it
+  // shared mode: the plan written by plan_kernel, and where family partials go
+  int32_t* items;       // [2 * num_seqs][kItemInts] work items
+  int32_t* wrec;        // [workers][kWorkerInts] per-worker range and first item
+  int32_t* links;       // [num_seqs] common prefix (blocks) with the previous sequence
+  int32_t fam_base;     // first partial-result slot of the family region
+  int32_t fam_max;      // most members of a family (sub-slots per family slot)
+  int32_t meta_stride;  // ints per sequence in ws_meta: 2, or 4 in shared mode
 };
 
 // Most finished segments a decode workgroup keeps in LDS before storing them.
@@ -75,6 +98,11 @@ hipError_t static_scratch(void** ptr);
 // (the CU's LDS over the resident workgroups per CU the worker count assumes).
 hipError_t launch_decode(const DecodeParams& p, int elem, int head_dim, int algo, int G,
                          unsigned workers, bool merge, size_t lds_per_workgroup, hipStream_t stream);
+// Shared mode: the planning launches ahead of launch_decode: one compares
+// every sequence's block-id list with its predecessor's (a wave per
+// sequence), the next (one workgroup) forms the families and lays out the
+// work items and every worker's range.
+hipError_t launch_plan(const DecodeParams& p, unsigned workers, hipStream_t stream);
 // Resident waves per CU of that kernel (0 if unknown).
 int decode_waves_per_cu(int elem, int head_dim, int algo, int G);
 

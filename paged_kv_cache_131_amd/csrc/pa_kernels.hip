@@ -20,6 +20,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <climits>
 #include <mutex>
 
 #include "pa_device.h"
@@ -55,13 +56,10 @@ hipError_t static_scratch(void** ptr) {
 namespace {
 
 // The length a decode works on: the stored one, cut to what the block
-// table can address and, with fixed partitions, to max_parts partitions (a
-// context longer than the host's bound is cut there rather than left
-// without a merging piece).
+// table can address and to the host's bound max_context_len (in every split
+// mode: the partitions and workspaces are sized from that bound).
 __device__ __forceinline__ int capped_len(const DecodeParams& p, int L_raw) {
-  int L = min(L_raw, p.max_blocks_per_seq << p.log2_block);
-  if (p.mode != kModeBalanced) L = (int)min((long long)L, (long long)p.max_parts * p.part_chunks * kChunk);
-  return L;
+  return min(min(L_raw, p.max_blocks_per_seq << p.log2_block), p.max_len);
 }
 
 // Stored length of sequence s (wave-uniform), read with a scalar load so
@@ -105,22 +103,59 @@ __device__ __forceinline__ u32x4 put_elem(u32x4 w, int e, uint32_t v) {
   return sizeof(U) == 4 ? put_elem32(w, e, v) : put_elem16(w, e, v);
 }
 
-// One sequence's share of a worker's work: tokens [t0, t1) of sequence s,
-// whose last logical block is lbl; tnew is the position of the token the
-// fused write stores (the sequence's last, when this piece holds it and the
-// call brings one), else -1.
+// What the piece holding an item's first chunk records for the merge
+// (bits of Segment::kind): where the sequence's own pieces are, where its
+// family's pieces are, or that it has no family (shared mode).
+enum RecordKind : int { kRecOwn = 1, kRecFamily = 2, kRecNoFamily = 4 };
+
+// One share of a worker's work: tokens [t0, t1) of sequences s .. s +
+// members - 1 (more than one: the common prefix of a family, which maps the
+// same blocks in every member), whose last logical block is lbl; tnew is
+// the position of the token the fused write stores (the sequence's last,
+// when this piece holds it and the call brings one), else -1. slot and
+// first_slot are partial-result slots (of member 0 for a family: member m
+// adds m); direct: the piece is a whole sequence and writes its output.
+// flags (shared mode only; the other modes derive the same from t0 and
+// npieces): members in bits 0-15, RecordKind bits the piece records when it
+// holds the item's first chunk in bits 16-18, direct in bit 19.
 struct Segment {
   int s, t0, t1, lbl, npieces, slot, first_slot;
   int tnew;
   int valid;
+  int flags;
 };
+
+__device__ __forceinline__ int segment_flags(int members, int kind, int direct) {
+  return members | (kind << 16) | (direct << 19);
+}
 
 __device__ __forceinline__ Segment invalid_segment() {
   Segment g;
   g.s = g.t0 = g.t1 = g.lbl = g.npieces = g.slot = g.first_slot = 0;
   g.tnew = -1;
   g.valid = 0;
+  g.flags = segment_flags(1, 0, 0);
   return g;
+}
+
+// The family kernel (SHARED true) runs the shared mode only, the others
+// never do.
+template <bool SHARED>
+__device__ __forceinline__ int seg_members(const Segment& g) {
+  return SHARED ? (g.flags & 0xffff) : 1;
+}
+// Output of a whole sequence, written directly (no merge).
+template <bool SHARED>
+__device__ __forceinline__ int seg_direct(const Segment& g) {
+  return SHARED ? (g.flags >> 19) & 1 : g.npieces == 1;
+}
+// Split record the piece writes: the piece holding a sequence's first token
+// in the balanced split (single pieces too, so the merge never reads a stale
+// record); the plan's choice in shared mode; none with fixed partitions.
+template <bool SHARED>
+__device__ __forceinline__ int seg_kind(const DecodeParams& p, const Segment& g) {
+  if (SHARED) return (g.flags >> 16) & 7;
+  return p.mode == kModeBalanced && g.t0 == 0 ? kRecOwn : 0;
 }
 
 __device__ __forceinline__ Segment uniform(Segment g) {
@@ -133,6 +168,7 @@ __device__ __forceinline__ Segment uniform(Segment g) {
   g.first_slot = __builtin_amdgcn_readfirstlane(g.first_slot);
   g.tnew = __builtin_amdgcn_readfirstlane(g.tnew);
   g.valid = __builtin_amdgcn_readfirstlane(g.valid);
+  g.flags = __builtin_amdgcn_readfirstlane(g.flags);
   return g;
 }
 
@@ -151,66 +187,115 @@ __device__ __forceinline__ int num_chunks(int L) { return L > 0 ? (L + kChunk - 
 // result of lane l (tokens 8*(l/16)+0..7 of its head slot) is exactly the P
 // operand lane l must supply, and V's token-minor tile makes each lane's
 // eight tokens at one dd a single 16-byte load.
-// Head slots: c < g carry head c with P rounded to 16 bits ("hi"), g <= c <
-// 2g carry head c-g with the rounding residual ("lo"), the rest are zero; the
-// two PV results are added at the end, so P enters the product with ~16
-// significant bits instead of 8.
+// One column group (NCG = 1): a sequence takes 2g consecutive head slots:
+// c < g carry head c with P rounded to 16 bits ("hi"), g <= c < 2g carry
+// head c-g with the rounding residual ("lo"); the two PV results are added at
+// the end, so P enters the product with ~16 significant bits instead of 8.
+// Slots no sequence takes are zero.
+// NCG 16-slot column groups (family kernel): every slot carries a distinct
+// (member, head) pair, 16/g members per group, all against the same K and V
+// registers, so the blocks a family shares are read once for all of them;
+// P enters PV as two products into the same accumulator, the rounded part
+// and its residual.
 // ---------------------------------------------------------------------------
-template <int E, int D, int SUB>
+template <int E, int D, int SUB, int NCG>
 struct MfmaEngine {
   using Tr = ElemT<E>;
   using op8 = typename Tr::op8;
   using scalar = typename Tr::scalar;
   using raw = typename Tr::raw;
   static constexpr int kSub = SUB;   // 32-token sub-chunks per step
+  static constexpr int kGroups = NCG;
+  static constexpr bool kDistinct = NCG > 1;  // distinct (member, head) slots, P's parts in two products
   static constexpr int MQ = D / 32;  // QK k-steps
   static constexpr int NT = D / 16;  // PV column tiles
   static constexpr int kPad = 4;
-  struct Smem {
+  static constexpr int kMaxGroup = kDistinct ? 16 : 8;  // query heads per KV head the slots hold
+  struct alignas(16) Smem {
     float o[16][D + kPad];
     float ml[16][2];
   };
 
-  op8 qop[MQ];
-  f32x4 o[NT];
-  float m_run;
-  float l_run;
+  op8 qop[NCG][MQ];
+  f32x4 o[NCG][NT];
+  float m_run[NCG];
+  float l_run[NCG];
   uint32_t vn[NT];  // the segment's new token's V at this lane's output columns 16j + col
+  int ncg;          // column groups the current segment uses
 
-  // q of one sequence as the QK B operand (columns = head slots), and the
-  // new token's V values this lane's B operands carry (fused write)
+  // q of every column group as the QK B operand (columns = head slots), and
+  // the new token's V values this lane's B operands carry (fused write)
   struct Q {
-    u32x4 w[MQ];
+    u32x4 w[NCG][MQ];
     uint32_t vn[NT];
   };
 
-  __device__ void load_q(Q& q, const DecodeParams& p, int s, int kvh, int lane) const {
+  // Head of the segment's member `member` that this lane's column carries
+  // in column group cg, or -1 (a slot no member takes).
+  __device__ static int column_head(int g, int members, int cg, int col, int& member) {
+    if (!kDistinct) {
+      member = 0;
+      return col < g ? col : (col < 2 * g ? col - g : -1);
+    }
+    const int per = 16 / g, mi = col / g;
+    member = cg * per + mi;
+    if (mi >= per || member >= members) return -1;
+    return col - mi * g;
+  }
+
+  // Part of P this lane's column carries: 0 rounded, 1 residual, 2 none
+  // (one column group; the family kernel uses both parts in every column).
+  __device__ static int column_part(int g, int col) { return col < g ? 0 : (col < 2 * g ? 1 : 2); }
+
+  __device__ __forceinline__ static void load_q_group(u32x4* w, const DecodeParams& p, int s, int members, int cg, int kvh,
+                                      int lane) {
     const int col = lane & 15, grp = lane >> 4, g = p.group;
-    const int hs = col < g ? col : (col < 2 * g ? col - g : -1);
-    const raw* qb = static_cast<const raw*>(p.q) + ((size_t)s * p.num_heads + (size_t)kvh * g) * D;
+    int member;
+    const int hs = column_head(g, members, cg, col, member);
+    const raw* qb = static_cast<const raw*>(p.q) + ((size_t)(s + (hs >= 0 ? member : 0)) * p.num_heads +
+                                                    (size_t)kvh * g) * D;
 #pragma unroll
     for (int m = 0; m < MQ; ++m) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (hs >= 0) w = load16(qb + (size_t)hs * D + 32 * m + 8 * grp);
-      q.w[m] = w;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (hs >= 0) x = load16(qb + (size_t)hs * D + 32 * m + 8 * grp);
+      w[m] = x;
     }
+  }
+
+  __device__ __forceinline__ void load_q(Q& q, const DecodeParams& p, const Segment& seg, int kvh, int lane) const {
+    const int col = lane & 15;
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) load_q_group(q.w[cg], p, seg.s, seg_members<kDistinct>(seg), cg, kvh, lane);
     // read unconditionally (from q when the call brings no new token: an
     // in-bounds row, never used) so every segment issues the same loads
-    const raw* vb = static_cast<const raw*>(p.v_new ? p.v_new : p.q) + ((size_t)s * p.num_kv_heads + kvh) * D + col;
+    const raw* vb = static_cast<const raw*>(p.v_new ? p.v_new : p.q) + ((size_t)seg.s * p.num_kv_heads + kvh) * D + col;
 #pragma unroll
     for (int j = 0; j < NT; ++j) q.vn[j] = vb[16 * j];
   }
 
-  __device__ void reset(const Q& q) {
-#pragma unroll
-    for (int m = 0; m < MQ; ++m) qop[m] = __builtin_bit_cast(op8, q.w[m]);
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      vn[j] = q.vn[j];
+  // Start a segment with its q (loaded during the previous segment's last
+  // chunk, every column group for every segment, so the code path is the
+  // same whether a segment is a family's or not).
+  __device__ __forceinline__ void reset(const Q& q, const DecodeParams& p, const Segment& seg, int kvh, int lane, Smem& sm) {
+    if (NCG == 1) {
+      ncg = 1;
+    } else {
+      const int per = 16 / p.group;
+      ncg = min((seg_members<kDistinct>(seg) + per - 1) / per, NCG);
     }
-    m_run = kNegInf;
-    l_run = 0.f;
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg)
+#pragma unroll
+      for (int m = 0; m < MQ; ++m) qop[cg][m] = __builtin_bit_cast(op8, q.w[cg][m]);
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j) o[cg][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m_run[cg] = kNegInf;
+      l_run[cg] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) vn[j] = q.vn[j];
   }
 
   // registers of one step: K rows (A operands) and V columns (B operands)
@@ -260,56 +345,44 @@ struct MfmaEngine {
     }
   }
 
-  // Compute the step at `cs` from `f`; as soon as a register set is
-  // consumed it is refilled with the next step (K after QK, V after PV), so
-  // one step's loads are always in flight behind the math.
-  __device__ void step(Frag& f, const DecodeParams& p, Smem&, int kvh, int lane, int cs, const Segment& cur,
-                       int cs_next, const ChunkIds* ids_next, const Segment& nxt) {
-    const int col = lane & 15, grp = lane >> 4, g = p.group;
-    const int t1 = cur.t1;
-    const bool has_new = cur.tnew >= cs && cur.tnew < cs + SUB * kChunk;
-    // scores: in sub-chunk u the lane holds tokens cs+32u+8*grp+0..7 of head slot `col`
-    f32x4 sc[SUB][2];
+  // QK of column group cg: in sub-chunk u the lane holds tokens
+  // cs+32u+8*grp+0..7 of head slot `col`, scaled to base-2 units and masked
+  // past the segment's end.
+  __device__ __forceinline__ void scores(const Frag& f, const DecodeParams& p, const op8 (&qg)[MQ], int grp, int cs, int t1,
+                         bool partial, float (&sv)[SUB][8]) const {
 #pragma unroll
     for (int u = 0; u < SUB; ++u) {
-      sc[u][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-      sc[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int m = 0; m < MQ; ++m) {
-        sc[u][0] = mfma_16x16x32(__builtin_bit_cast(op8, f.ka[u][0][m]), qop[m], sc[u][0]);
-        sc[u][1] = mfma_16x16x32(__builtin_bit_cast(op8, f.ka[u][1][m]), qop[m], sc[u][1]);
+        s0 = mfma_16x16x32(__builtin_bit_cast(op8, f.ka[u][0][m]), qg[m], s0);
+        s1 = mfma_16x16x32(__builtin_bit_cast(op8, f.ka[u][1][m]), qg[m], s1);
       }
-    }
-    // unconditional refill (at the end of the stream the last step re-reads
-    // itself from L2) keeps the count of loads in flight the same on every
-    // path, so the PV wait below never has to drain the next step's K loads
-    load_k(f, p, kvh, lane, cs_next, ids_next, nxt);
-    float sv[SUB][8];
-#pragma unroll
-    for (int u = 0; u < SUB; ++u)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sv[u][i] = sc[u][0][i] * p.scale_log2;
-        sv[u][4 + i] = sc[u][1][i] * p.scale_log2;
+        sv[u][i] = s0[i] * p.scale_log2;
+        sv[u][4 + i] = s1[i] * p.scale_log2;
       }
-    const bool partial = cs + SUB * kChunk > t1;
+    }
     if (partial) {
 #pragma unroll
       for (int u = 0; u < SUB; ++u)
 #pragma unroll
         for (int e = 0; e < 8; ++e) sv[u][e] = (cs + kChunk * u + 8 * grp + e < t1) ? sv[u][e] : kNegInf;
     }
+  }
 
-    // online softmax (base 2), per head slot
+  // Online softmax (base 2) of column group cg's scores and its PV products
+  // with the chunk's V (P as a rounded part or its residual, by head slot).
+  __device__ __forceinline__ void softmax_pv(const Frag& f, int cg, int grp, int part, float (&sv)[SUB][8]) {
     float cmax = kNegInf;
 #pragma unroll
     for (int u = 0; u < SUB; ++u)
 #pragma unroll
       for (int e = 0; e < 8; ++e) cmax = fmaxf(cmax, sv[u][e]);
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-    const float m_new = fmaxf(m_run, cmax);
-    const float alpha = fast_exp2(m_run - m_new);
+    cmax = max_over_column(cmax);
+    const float m_new = fmaxf(m_run[cg], cmax);
+    const float alpha = fast_exp2(m_run[cg] - m_new);
     float pe[SUB][8];
     float psum = 0.f;
 #pragma unroll
@@ -319,65 +392,126 @@ struct MfmaEngine {
         pe[u][e] = fast_exp2(sv[u][e] - m_new);
         psum += pe[u][e];
       }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+    l_run[cg] = l_run[cg] * alpha + psum;
+    m_run[cg] = m_new;
     if (__any(alpha != 1.f)) {
       // output rows of this lane are head slots 4*grp+i; their factor lives in lane 4*grp+i
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float ai = __shfl(alpha, 4 * grp + i);
 #pragma unroll
-        for (int j = 0; j < NT; ++j) o[j][i] *= ai;
+        for (int j = 0; j < NT; ++j) o[cg][j][i] *= ai;
       }
     }
-
-    // P operands: hi part, lo residual or zero depending on the head slot
-    const int part = col < g ? 0 : (col < 2 * g ? 1 : 2);
 #pragma unroll
     for (int u = 0; u < SUB; ++u) {
-      op8 pa;
+      if constexpr (kDistinct) {
+        op8 phi, plo;
+        Tr::split(pe[u], phi, plo);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const scalar hi = static_cast<scalar>(pe[u][e]);
-        const scalar lo = static_cast<scalar>(pe[u][e] - static_cast<float>(hi));
-        pa[e] = part == 0 ? hi : (part == 1 ? lo : static_cast<scalar>(0.f));
+        for (int j = 0; j < NT; ++j) {
+          o[cg][j] = mfma_16x16x32(phi, __builtin_bit_cast(op8, f.vr[u][j]), o[cg][j]);
+          o[cg][j] = mfma_16x16x32(plo, __builtin_bit_cast(op8, f.vr[u][j]), o[cg][j]);
+        }
+      } else {
+        op8 pa;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const scalar hi = static_cast<scalar>(pe[u][e]);
+          const scalar lo = static_cast<scalar>(pe[u][e] - static_cast<float>(hi));
+          pa[e] = part == 0 ? hi : (part == 1 ? lo : static_cast<scalar>(0.f));
+        }
+#pragma unroll
+        for (int j = 0; j < NT; ++j) o[cg][j] = mfma_16x16x32(pa, __builtin_bit_cast(op8, f.vr[u][j]), o[cg][j]);
       }
+    }
+  }
+
+  // Compute the step at `cs` from `f`; as soon as a register set is
+  // consumed it is refilled with the next step (K after the last QK, V after
+  // the last PV), so one step's loads are always in flight behind the math.
+  // Column groups run one after the other: group cg's QK, softmax and PV
+  // (the K refill waits for the last group's QK).
+  __device__ __forceinline__ void step(Frag& f, const DecodeParams& p, Smem& sm, int kvh, int lane, int cs, const Segment& cur,
+                       int cs_next, const ChunkIds* ids_next, const Segment& nxt) {
+    const int col = lane & 15, grp = lane >> 4, g = p.group;
+    const int t1 = cur.t1;
+    const int nact = NCG == 1 ? 1 : ncg;
+    const bool has_new = cur.tnew >= cs && cur.tnew < cs + SUB * kChunk;
+    const bool partial = cs + SUB * kChunk > t1;
+    const int part = kDistinct ? 0 : column_part(g, col);
+    float sv[SUB][8];
+    scores(f, p, qop[0], grp, cs, t1, partial, sv);
+    if (NCG == 1) {
+      // unconditional refill (at the end of the stream the last step re-reads
+      // itself from L2) keeps the count of loads in flight the same on every
+      // path, so the PV wait below never has to drain the next step's K loads
+      load_k(f, p, kvh, lane, cs_next, ids_next, nxt);
+    }
+    // V of tokens past the segment's end is selected out (never multiplied),
+    // the new token's V replaces what its slot held before this launch
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) {
       if (partial) {
         const int nvalid = t1 - (cs + kChunk * u + 8 * grp);
 #pragma unroll
         for (int j = 0; j < NT; ++j) f.vr[u][j] = Tr::keep_first(f.vr[u][j], nvalid);
       }
       if (has_new) {
-        // the new token's V replaces what its slot held before this launch
         const int e = cur.tnew - (cs + kChunk * u + 8 * grp);
         const int en = e >= 0 && e < 8 ? e : -1;
 #pragma unroll
         for (int j = 0; j < NT; ++j) f.vr[u][j] = put_elem<raw>(f.vr[u][j], en, vn[j]);
       }
-#pragma unroll
-      for (int j = 0; j < NT; ++j) o[j] = mfma_16x16x32(pa, __builtin_bit_cast(op8, f.vr[u][j]), o[j]);
     }
+    softmax_pv(f, 0, grp, part, sv);
+    if constexpr (NCG > 1) {
+#pragma unroll
+      for (int cg = 1; cg < NCG; ++cg) {
+        if (cg < nact) {
+          scores(f, p, qop[cg], grp, cs, t1, partial, sv);
+          softmax_pv(f, cg, grp, part, sv);
+        }
+      }
+    }
+    if (NCG > 1) load_k(f, p, kvh, lane, cs_next, ids_next, nxt);
     load_v(f, p, kvh, lane, cs_next, ids_next, nxt);
   }
 
-  __device__ void finish(Smem& sm, int lane) {
+  // Column group cg's results into sm: o[head slot][dd], (m, l) per slot.
+  __device__ __forceinline__ void finish(Smem& sm, int lane, int cg) {
     const int col = lane & 15, grp = lane >> 4;
-    float l_tot = l_run + __shfl_xor(l_run, 16);
-    l_tot += __shfl_xor(l_tot, 32);
+    const float l_tot = sum_over_column(l_run[cg]);
 #pragma unroll
     for (int j = 0; j < NT; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sm.o[4 * grp + i][16 * j + col] = o[j][i];
+      for (int i = 0; i < 4; ++i) sm.o[4 * grp + i][16 * j + col] = o[cg][j][i];
     if (grp == 0) {
-      sm.ml[col][0] = m_run;
+      sm.ml[col][0] = m_run[cg];
       sm.ml[col][1] = l_tot;
     }
     __syncthreads();
   }
 
-  __device__ static float o_val(const Smem& sm, int h, int dd, int g) { return sm.o[h][dd] + sm.o[h + g][dd]; }
-  __device__ static float m_val(const Smem& sm, int h) { return sm.ml[h][0]; }
-  __device__ static float l_val(const Smem& sm, int h) { return sm.ml[h][1]; }
+  // members whose results group cg holds, and the first head slot of member mi
+  __device__ int members_in_group(const DecodeParams& p, const Segment& g, int cg) const {
+    if (!kDistinct) return 1;
+    const int per = 16 / p.group;
+    return max(0, min(per, seg_members<kDistinct>(g) - cg * per));
+  }
+  __device__ static int member_row(const DecodeParams& p, int mi) { return kDistinct ? mi * p.group : 0; }
+  __device__ static int member_of(const DecodeParams& p, int cg, int mi) {
+    return kDistinct ? cg * (16 / p.group) + mi : 0;
+  }
+
+  // outputs dd..dd+3 of head h (dd a multiple of 4)
+  __device__ static f32x4 o_val4(const Smem& sm, int row, int h, int dd, int g) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.o[row + h][dd]);
+    if (kDistinct) return a;
+    return a + *reinterpret_cast<const f32x4*>(&sm.o[row + h + g][dd]);
+  }
+  __device__ static float m_val(const Smem& sm, int row, int h) { return sm.ml[row + h][0]; }
+  __device__ static float l_val(const Smem& sm, int row, int h) { return sm.ml[row + h][1]; }
 };
 
 // ---------------------------------------------------------------------------
@@ -400,7 +534,9 @@ struct VecEngine {
   static constexpr int DPS = 64 / LPD;          // dd rows per V load step
   static constexpr int VSTEPS = D / DPS;        // V load steps per chunk
   static constexpr int kSub = 1;
-  struct Smem {
+  static constexpr int kGroups = 1;
+  static constexpr int kMaxGroup = G;
+  struct alignas(16) Smem {
     float sc[G][kChunk];
     float pl[G][kChunk];
     float o[G][D];
@@ -418,7 +554,8 @@ struct VecEngine {
     uint32_t vn[VSTEPS];
   };
 
-  __device__ void load_q(Q& q, const DecodeParams& p, int s, int kvh, int lane) const {
+  __device__ void load_q(Q& q, const DecodeParams& p, const Segment& seg, int kvh, int lane) const {
+    const int s = seg.s;
     const int piece = lane % LPR, g = p.group;
     const raw* qb = static_cast<const raw*>(p.q) + ((size_t)s * p.num_heads + (size_t)kvh * g) * D;
 #pragma unroll
@@ -435,7 +572,7 @@ struct VecEngine {
     for (int st = 0; st < VSTEPS; ++st) q.vn[st] = vb[st * DPS];
   }
 
-  __device__ void reset(const Q& q) {
+  __device__ void reset(const Q& q, const DecodeParams&, const Segment&, int, int, Smem&) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       Tr::widen(q.w[h], qv[h]);
@@ -557,7 +694,7 @@ struct VecEngine {
     __syncthreads();  // sc/pl are rewritten by the next chunk
   }
 
-  __device__ void finish(Smem& sm, int lane) {
+  __device__ void finish(Smem& sm, int lane, int) {
     const int tg = lane % LPD, ddl = lane / LPD;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -579,9 +716,14 @@ struct VecEngine {
     __syncthreads();
   }
 
-  __device__ static float o_val(const Smem& sm, int h, int dd, int) { return sm.o[h][dd]; }
-  __device__ static float m_val(const Smem& sm, int h) { return sm.ml[h][0]; }
-  __device__ static float l_val(const Smem& sm, int h) { return sm.ml[h][1]; }
+  __device__ int members_in_group(const DecodeParams&, const Segment&, int) const { return 1; }
+  __device__ static int member_row(const DecodeParams&, int) { return 0; }
+  __device__ static int member_of(const DecodeParams&, int, int) { return 0; }
+  __device__ static f32x4 o_val4(const Smem& sm, int, int h, int dd, int) {
+    return *reinterpret_cast<const f32x4*>(&sm.o[h][dd]);
+  }
+  __device__ static float m_val(const Smem& sm, int, int h) { return sm.ml[h][0]; }
+  __device__ static float l_val(const Smem& sm, int, int h) { return sm.ml[h][1]; }
 };
 
 // ---------------------------------------------------------------------------
@@ -598,25 +740,71 @@ __device__ __forceinline__ long long owner_of(long long c, long long W, long lon
   return ((c + 1) * W - 1) / T;
 }
 
+// Work item i of a shared-mode plan: {sequence | members << 16, family
+// index (members > 1) or first token, end token, first chunk in the
+// laid-out order}, read with scalar loads (the plan is read-only for the
+// launch); a worker's first item comes with its worker record.
+struct Item {
+  int seq, members, fam, t0, t1;
+  long long c;
+};
+
+__device__ __forceinline__ Item make_item(int r0, int r1, int r2, int r3) {
+  Item it;
+  it.seq = r0 & 0xffff;
+  it.members = r0 >> 16;
+  it.fam = it.members > 1 ? r1 : -1;
+  it.t0 = it.members > 1 ? 0 : r1;
+  it.t1 = r2;
+  it.c = r3;
+  return it;
+}
+
+__device__ __forceinline__ Item item_at(const DecodeParams& p, int i) {
+  const const_i32* q = (const const_i32*)p.items + (size_t)i * kItemInts;
+  return make_item(q[0], q[1], q[2], q[3]);
+}
+
 // Yields a worker's segments in order. Balanced mode: the chunks of all
 // sequences (per KV head) are laid end to end and worker w owns chunks
-// [start, end); fixed mode: a single partition.
-struct SegmentSource {
+// [start, end); shared mode: the same over the plan's work items; fixed
+// mode: a single partition.
+// Fields of the shared mode's walk (the family kernel's only); none for the
+// other kernels.
+template <bool SHARED>
+struct ItemWalk {
+  int num_items;  // items of the plan
+  int first;      // the worker's first item, whose record is `first_item`
+  Item first_item;
+};
+template <>
+struct ItemWalk<false> {};
+
+template <bool SHARED>
+struct SegmentSource : ItemWalk<SHARED> {
   int mode;
-  int s;          // next sequence to look at
-  long long c;    // first chunk of sequence s in the laid-out order
+  int s;          // next sequence (shared mode: next item) to look at
+  long long c;    // first chunk of sequence (item) s in the laid-out order
   int k;          // fixed-partition stream: next partition of sequence s
   long long start, end, W, T;
   int w;
   Segment fixed;  // one-partition-per-workgroup mode's only segment
 
   __device__ Segment next(const DecodeParams& p) {
-    if (mode == kModeFixed) {
-      const Segment g = fixed;
-      fixed.valid = 0;
-      return g;
+    if constexpr (SHARED) {
+      return next_item(p);
+    } else {
+      if (mode == kModeFixed) {
+        const Segment g = fixed;
+        fixed.valid = 0;
+        return g;
+      }
+      if (mode == kModeFixedStream) return next_partition(p);
+      return next_sequence(p);
     }
-    if (mode == kModeFixedStream) return next_partition(p);
+  }
+
+  __device__ Segment next_sequence(const DecodeParams& p) {
     while (s < p.num_seqs && c < end) {
       const int L_raw = lds_len(s);
       const int L = capped_len(p, L_raw);
@@ -629,6 +817,7 @@ struct SegmentSource {
       const long long c1 = end < c + n ? end : c + n;
       Segment g;
       g.s = s;
+      g.flags = segment_flags(1, 0, 0);
       g.t0 = (int)(c0 - c) * kChunk;
       g.t1 = min((int)(c1 - c) * kChunk, L);
       g.lbl = (g.t1 - 1) >> p.log2_block;
@@ -638,6 +827,52 @@ struct SegmentSource {
       g.npieces = last - first + 1;
       g.slot = w + s;
       g.first_slot = first + s;
+      g.valid = 1;
+      c += n;
+      ++s;
+      return uniform(g);
+    }
+    return invalid_segment();
+  }
+
+  // Shared mode: items laid end to end like the sequences of the balanced
+  // split. A family's common prefix (members > 1) always leaves partial
+  // results, in the family region: piece slot (w + family) * fam_max +
+  // member. A member's own rest (first token > 0) merges with them; a
+  // sequence outside every family is treated as in the balanced split.
+  __device__ Segment next_item(const DecodeParams& p) {
+    while (s < this->num_items && c < end) {
+      const Item it = s == this->first ? this->first_item : item_at(p, s);
+      const int n = num_chunks(it.t1 - it.t0);
+      c = it.c;
+      if (n == 0) {
+        ++s;
+        continue;
+      }
+      const long long c0 = start > c ? start : c;
+      const long long c1 = end < c + n ? end : c + n;
+      Segment g;
+      g.s = it.seq;
+      g.t0 = it.t0 + (int)(c0 - c) * kChunk;
+      g.t1 = min(it.t0 + (int)(c1 - c) * kChunk, it.t1);
+      g.lbl = (g.t1 - 1) >> p.log2_block;
+      const int first = (int)owner_of(c, W, T);
+      const int last = (int)owner_of(c + n - 1, W, T);
+      g.npieces = last - first + 1;
+      const bool head = c0 == c;
+      if (it.members > 1) {
+        g.tnew = -1;  // a family's common prefix ends before every member's last token
+        g.slot = p.fam_base + (w + it.fam) * p.fam_max;
+        g.first_slot = p.fam_base + (first + it.fam) * p.fam_max;
+        g.flags = segment_flags(it.members, head ? kRecFamily : 0, 0);
+      } else {
+        const int L_raw = len_uniform(p, it.seq);
+        g.tnew = new_token_pos(p, g.t1, it.t1, L_raw);
+        g.slot = w + s;
+        g.first_slot = first + s;
+        g.flags = segment_flags(1, head ? (it.t0 == 0 ? (kRecOwn | kRecNoFamily) : kRecOwn) : 0,
+                                it.t0 == 0 && g.npieces == 1);
+      }
       g.valid = 1;
       c += n;
       ++s;
@@ -660,6 +895,7 @@ struct SegmentSource {
         if (c + (long long)k * pc >= end) break;
         Segment g;
         g.s = s;
+        g.flags = segment_flags(1, 0, 0);
         g.t0 = k * pc * kChunk;
         g.t1 = (int)min((long long)g.t0 + (long long)pc * kChunk, (long long)L);
         g.lbl = (g.t1 - 1) >> p.log2_block;
@@ -716,9 +952,9 @@ __device__ __forceinline__ ChunkIds ids_at(const DecodeParams& p, Pos x, const S
 // step of 512-token partitions spent a fifth of its time there.
 // Slot k: values [g][D] (normalised outputs of a whole sequence, or the
 // unnormalised partial of a piece), (m, l) of each head, and a record
-// {sequence, pieces, partial-result slot, first slot, 1 if the split record
-// is written}.
-constexpr int kResRec = 5;
+// {sequence, pieces, partial-result slot, first slot, RecordKind bits of the
+// split record to write, 1 if the values are the sequence's output}.
+constexpr int kResRec = 6;
 
 template <bool NT>
 __device__ __forceinline__ void store16(f32x4* dst, f32x4 v) {
@@ -751,72 +987,131 @@ __device__ __forceinline__ ResultBuf result_buffer(const DecodeParams& p, int D)
 // stream's load, so the load waits behind them are shorter: 512-token
 // partitions at the long-context shape 939 -> 913 us); at the stream's end
 // ordinary stores.
-template <int D, bool NT>
+template <int D, int MAXG, bool NT, bool SHARED>
 __device__ void flush_results(const DecodeParams& p, ResultBuf& rb, int kvh, int lane) {
+  constexpr int kStride = SHARED ? 4 : 2;  // ints per sequence in ws_meta
+  constexpr int kV4 = (MAXG * D / 4 + 63) / 64;  // 16-byte pieces per lane and result
   const int gq = p.group, Hq = p.num_heads, n4 = gq * D / 4;
   const size_t head0 = (size_t)kvh * gq;
-  const bool out_vec = p.out_dtype == kF32 && (reinterpret_cast<uintptr_t>(p.out) & 15) == 0;
+  const bool out_vec = (reinterpret_cast<uintptr_t>(p.out) & (p.out_dtype == kF32 ? 15 : 7)) == 0;
   for (int k = 0; k < rb.n; ++k) {
     const int* r = rb.rec + kResRec * k;
     const int s = __builtin_amdgcn_readfirstlane(r[0]), np = __builtin_amdgcn_readfirstlane(r[1]);
     const int slot = __builtin_amdgcn_readfirstlane(r[2]);
     const float* v = rb.vals + (size_t)k * gq * D;
-    if (r[4] && lane == 0) {
-      p.ws_meta[2 * s] = r[3];
-      p.ws_meta[2 * s + 1] = np;
+    const int kind = r[4];
+    if (kind && lane == 0) {
+      // split record of sequence s: {own first slot, own pieces}, or in
+      // shared mode {family first slot, family pieces, own first, own pieces}
+      int* meta = p.ws_meta + (size_t)s * kStride;
+      if (kind & kRecOwn) {
+        meta[kStride - 2] = r[3];
+        meta[kStride - 1] = np;
+      }
+      if (SHARED && (kind & kRecFamily)) {
+        meta[0] = r[3];
+        meta[1] = np;
+      }
+      if (SHARED && (kind & kRecNoFamily)) {
+        meta[0] = 0;
+        meta[1] = 0;
+      }
     }
-    if (np == 1) {
+    // the result's LDS reads all issued before its first store
+    f32x4 t[kV4];
+#pragma unroll
+    for (int u = 0; u < kV4; ++u) {
+      const int i = lane + 64 * u;
+      if (i < n4) t[u] = reinterpret_cast<const f32x4*>(v)[i];
+    }
+    if (r[5]) {
       const size_t base = ((size_t)s * Hq + head0) * D;
-      if (out_vec) {
-        for (int i = lane; i < n4; i += 64)
-          store16<NT>(reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + base) + i, reinterpret_cast<const f32x4*>(v)[i]);
-      } else {
-        for (int idx = lane; idx < gq * D; idx += 64) store_out(p.out, base + idx, v[idx], p.out_dtype);
+#pragma unroll
+      for (int u = 0; u < kV4; ++u) {
+        const int i = lane + 64 * u;
+        if (i >= n4) continue;
+        if (NT && p.out_dtype == kF32 && out_vec)
+          store16<NT>(reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + base) + i, t[u]);
+        else
+          store_out4(p.out, base + 4 * (size_t)i, t[u], p.out_dtype, out_vec);
       }
     } else {
       const size_t row0 = (size_t)slot * Hq + head0;
-      for (int i = lane; i < n4; i += 64)
-        store16<NT>(reinterpret_cast<f32x4*>(p.ws_acc + row0 * D) + i, reinterpret_cast<const f32x4*>(v)[i]);
+#pragma unroll
+      for (int u = 0; u < kV4; ++u) {
+        const int i = lane + 64 * u;
+        if (i < n4) store16<NT>(reinterpret_cast<f32x4*>(p.ws_acc + row0 * D) + i, t[u]);
+      }
       for (int i = lane; i < 2 * gq; i += 64) p.ws_ml[row0 * 2 + i] = rb.ml[(size_t)k * gq * 2 + i];
     }
   }
   rb.n = 0;
 }
 
+// Buffers the result of one sequence of a finished segment: member m
+// (0 unless the segment is a family's common prefix), whose head slots start
+// at row `row` of the engine's staging area.
 template <class Eng, int D>
-__device__ void segment_epilogue(const DecodeParams& p, const typename Eng::Smem& sm, const Segment& g, int kvh,
-                                 int lane, ResultBuf& rb) {
-  if (rb.n == p.res_slots) flush_results<D, true>(p, rb, kvh, lane);
+__device__ void segment_epilogue(const DecodeParams& p, const typename Eng::Smem& sm, const Segment& g, int m,
+                                 int row, int kvh, int lane, ResultBuf& rb) {
+  constexpr bool kShared = Eng::kGroups > 1;
+  if (rb.n == p.res_slots) flush_results<D, Eng::kMaxGroup, true, kShared>(p, rb, kvh, lane);
   const int gq = p.group;
   const int k = rb.n;
   float* v = rb.vals + (size_t)k * gq * D;
-  if (g.npieces == 1) {
-    for (int idx = lane; idx < gq * D; idx += 64) {
-      const int h = idx / D, dd = idx % D;
-      v[idx] = Eng::o_val(sm, h, dd, gq) / Eng::l_val(sm, h);
+  const int direct = seg_direct<kShared>(g);
+  // 16 bytes per lane and access, every read issued before the first write
+  // (one LDS round trip per result, not one per element)
+  constexpr int kV4 = (Eng::kMaxGroup * D / 4 + 63) / 64;
+  const int n4 = gq * D / 4;
+  f32x4 t[kV4];
+#pragma unroll
+  for (int u = 0; u < kV4; ++u) {
+    const int i = lane + 64 * u;
+    if (i < n4) {
+      const int h = 4 * i / D, dd = 4 * i % D;
+      t[u] = Eng::o_val4(sm, row, h, dd, gq);
+      if (direct) t[u] = t[u] / Eng::l_val(sm, row, h);
     }
-  } else {
-    for (int idx = lane; idx < gq * D; idx += 64) {
-      const int h = idx / D, dd = idx % D;
-      v[idx] = Eng::o_val(sm, h, dd, gq);
-    }
+  }
+#pragma unroll
+  for (int u = 0; u < kV4; ++u) {
+    const int i = lane + 64 * u;
+    if (i < n4) reinterpret_cast<f32x4*>(v)[i] = t[u];
+  }
+  if (!direct) {
     for (int h = lane; h < gq; h += 64) {
-      rb.ml[((size_t)k * gq + h) * 2] = Eng::m_val(sm, h);
-      rb.ml[((size_t)k * gq + h) * 2 + 1] = Eng::l_val(sm, h);
+      rb.ml[((size_t)k * gq + h) * 2] = Eng::m_val(sm, row, h);
+      rb.ml[((size_t)k * gq + h) * 2 + 1] = Eng::l_val(sm, row, h);
     }
   }
   if (lane == 0) {
     int* r = rb.rec + kResRec * k;
-    r[0] = g.s;
+    r[0] = g.s + m;
     r[1] = g.npieces;
-    r[2] = g.slot;
-    r[3] = g.first_slot;
-    // the piece holding a sequence's first token records where its pieces
-    // are (single pieces too, so the merge kernel never reads a stale record)
-    r[4] = p.mode == kModeBalanced && g.t0 == 0 && kvh == 0;
+    r[2] = g.slot + m;
+    r[3] = g.first_slot + m;
+    r[4] = kvh == 0 ? seg_kind<kShared>(p, g) : 0;
+    r[5] = direct;
   }
   rb.n = k + 1;
   __syncthreads();
+}
+
+// Every result of a finished segment: column group by column group, each
+// member the group holds.
+template <class Eng, int D>
+__device__ void finish_segment(const DecodeParams& p, Eng& eng, typename Eng::Smem& sm, const Segment& g, int kvh,
+                               int lane, ResultBuf& rb) {
+#pragma unroll
+  for (int cg = 0; cg < Eng::kGroups; ++cg) {
+    const int nm = eng.members_in_group(p, g, cg);
+    if (nm > 0) {
+      eng.finish(sm, lane, cg);
+      for (int mi = 0; mi < nm; ++mi)
+        segment_epilogue<Eng, D>(p, sm, g, Eng::member_of(p, cg, mi), Eng::member_row(p, mi), kvh, lane, rb);
+    }
+  }
 }
 
 // Runs all of a worker's segments as one stream of 32-token chunks: the
@@ -825,7 +1120,8 @@ __device__ void segment_epilogue(const DecodeParams& p, const typename Eng::Smem
 // same time; block ids are read two chunks ahead. A segment's epilogue
 // therefore overlaps the next segment's first loads.
 template <class Eng, int D>
-__device__ void run_stream(const DecodeParams& p, typename Eng::Smem& sm, SegmentSource& src, int kvh, int lane) {
+__device__ void run_stream(const DecodeParams& p, typename Eng::Smem& sm, SegmentSource<(Eng::kGroups > 1)>& src,
+                           int kvh, int lane) {
   static_assert(Eng::kSub == 1, "the chunk stream assumes one 32-token chunk per step");
   Segment A = src.next(p);
   if (!A.valid) return;
@@ -835,7 +1131,7 @@ __device__ void run_stream(const DecodeParams& p, typename Eng::Smem& sm, Segmen
   const ChunkIds ids0 = ids_at(p, p0, A, A, A);
   Eng eng;
   typename Eng::Q q, qn;
-  eng.load_q(q, p, A.s, kvh, lane);
+  eng.load_q(q, p, A, kvh, lane);
   ResultBuf rb = result_buffer(p, D);
   Segment B = src.next(p);
   Segment C = B.valid ? src.next(p) : invalid_segment();
@@ -845,31 +1141,30 @@ __device__ void run_stream(const DecodeParams& p, typename Eng::Smem& sm, Segmen
   typename Eng::Frag f;
   eng.load_k(f, p, kvh, lane, p0.cs, &ids0, A);
   eng.load_v(f, p, kvh, lane, p0.cs, &ids0, A);
-  eng.reset(q);  // after the first K/V loads are issued: only the first QK needs q
+  eng.reset(q, p, A, kvh, lane, sm);  // after the first K/V loads are issued: only the first QK needs q
   for (;;) {
     const ChunkIds ids2 = ids_at(p, p2, A, B, C);
     const bool leaving = p1.rel != 0;                       // p0 is the current segment's last chunk
     const bool at_end = !leaving && p1.cs == p0.cs;         // and there is no next segment
     const Segment n1 = seg_at(p1.rel, A, B, C);
-    if (leaving) eng.load_q(qn, p, n1.s, kvh, lane);
+    if (leaving) eng.load_q(qn, p, n1, kvh, lane);
     eng.step(f, p, sm, kvh, lane, p0.cs, A, p1.cs, &ids1, n1);
     if (leaving || at_end) {
-      eng.finish(sm, lane);
-      segment_epilogue<Eng, D>(p, sm, A, kvh, lane, rb);
+      finish_segment<Eng, D>(p, eng, sm, A, kvh, lane, rb);
       if (at_end) break;
       A = B;
       B = C;
       C = B.valid ? src.next(p) : invalid_segment();
       p1.rel -= 1;
       p2.rel -= 1;
-      eng.reset(qn);
+      eng.reset(qn, p, A, kvh, lane, sm);
     }
     p0 = p1;
     p1 = p2;
     p2 = advance(p2, A, B, C);
     ids1 = ids2;
   }
-  flush_results<D, false>(p, rb, kvh, lane);
+  flush_results<D, Eng::kMaxGroup, false, (Eng::kGroups > 1)>(p, rb, kvh, lane);
 }
 
 // Workgroups are handed to the 8 XCDs (each with its own L2) in turn by
@@ -890,10 +1185,33 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
   const int kvh = blockIdx.y;
   const int W = gridDim.x;
   const int w = worker_index(blockIdx.x, W, p.mode);
-  SegmentSource src;
+  SegmentSource<(Eng::kGroups > 1)> src;
   src.mode = p.mode;
   src.w = w;
 
+  if constexpr (Eng::kGroups > 1) {
+    // the family kernel runs the shared mode only; the plan launch wrote
+    // this worker's chunk range and first item
+    const int S = p.num_seqs;
+    for (int s = w; s < S; s += W)
+      if (capped_len(p, len_uniform(p, s)) <= 0) write_zero_rows<Eng, D>(p, s, kvh, lane);
+    const const_i32* wr = (const const_i32*)p.wrec + (size_t)w * kWorkerInts;
+    const int start = wr[0], end = wr[1], first = wr[2], T = wr[3];
+    if (p.mode != kModeShared || start >= end) return;
+    src.s = first;
+    src.c = start;
+    src.k = 0;
+    src.start = start;
+    src.end = end;
+    src.W = min(W, T);
+    src.T = T;
+    src.num_items = wr[4];
+    src.first = first;
+    src.first_item = make_item(wr[8], wr[9], wr[10], wr[11]);
+    src.fixed = invalid_segment();
+    run_stream<Eng, D>(p, sm, src, kvh, lane);
+    return;
+  } else {
   if (p.mode == kModeFixed) {
     const int s = w / p.max_parts, part = w % p.max_parts;
     const int P = p.part_chunks * kChunk;
@@ -907,6 +1225,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
     if (t0 >= L) return;
     Segment g;
     g.s = s;
+    g.flags = segment_flags(1, 0, 0);
     g.t0 = t0;
     g.t1 = min(t0 + P, L);
     g.lbl = (g.t1 - 1) >> p.log2_block;
@@ -986,6 +1305,245 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
   src.T = T;
   src.fixed = invalid_segment();
   run_stream<Eng, D>(p, sm, src, kvh, lane);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Shared-mode plan (a link launch, then one workgroup, ahead of the decode
+// launch).
+//
+// Sequences that map the same physical blocks at the same logical positions
+// from position 0 on (forks of one prompt: parallel samples, beams, requests
+// on a shared prefix; the kernels see only their block-id lists) hold the
+// same K/V there. Adjacent sequences with at least kSharedMinChunks chunks of
+// such a common prefix form families of up to fam_max members. Work items,
+// laid end to end in 32-token chunks as the balanced split lays out
+// sequences: a family's common prefix (tokens [0, Sf), Sf a multiple of 32
+// and below every member's last token), then each member's rest [Sf, L); a
+// sequence outside every family is one item [0, L). Worker w of W gets
+// chunks [w T / W', (w + 1) T / W'), W' = min(W, T), as in the balanced split.
+// ---------------------------------------------------------------------------
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / 64;
+
+// Inclusive sums of two ints per thread over the workgroup, in one pass.
+__device__ int2 plan_scan2(int2 x, int2* tot) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int a = __shfl_up(x.x, d), b = __shfl_up(x.y, d);
+    if (lane >= d) {
+      x.x += a;
+      x.y += b;
+    }
+  }
+  if (lane == 63) tot[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    int2 v = lane < kPlanWaves ? tot[lane] : int2{0, 0};
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int a = __shfl_up(v.x, d), b = __shfl_up(v.y, d);
+      if (lane >= d) {
+        v.x += a;
+        v.y += b;
+      }
+    }
+    if (lane < kPlanWaves) tot[lane] = v;
+  }
+  __syncthreads();
+  if (wave > 0) {
+    x.x += tot[wave - 1].x;
+    x.y += tot[wave - 1].y;
+  }
+  __syncthreads();
+  return x;
+}
+
+// Inclusive scan (sum, or max with `use_max`) of one int per thread over the
+// workgroup: lane shuffles within a wave, the waves' totals through LDS.
+__device__ int plan_scan(int x, int* tot, bool use_max) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x = use_max ? max(x, y) : x + y;
+  }
+  if (lane == 63) tot[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    int v = lane < kPlanWaves ? tot[lane] : (use_max ? INT_MIN : 0);
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(v, d);
+      if (lane >= d) v = use_max ? max(v, y) : v + y;
+    }
+    if (lane < kPlanWaves) tot[lane] = v;
+  }
+  __syncthreads();
+  if (wave > 0) x = use_max ? max(x, tot[wave - 1]) : x + tot[wave - 1];
+  __syncthreads();
+  return x;
+}
+
+// Common prefix, in blocks, of sequence s's block-id list with sequence
+// s - 1's (0 for s = 0), written to p.links[s]: one wave per sequence,
+// kLinkSpan loads of 64 entries per lane and row in flight per round.
+constexpr int kLinkWaves = 4;
+constexpr int kLinkSpan = 4;
+
+__global__ __launch_bounds__(64 * kLinkWaves) void link_kernel(DecodeParams p) {
+  const int lane = threadIdx.x & 63;
+  const int s = blockIdx.x * kLinkWaves + (threadIdx.x >> 6);
+  if (s >= p.num_seqs) return;  // whole waves
+  int c = 0;
+  if (s > 0) {
+    const int lg = p.log2_block, B = p.block_size, mb = p.max_blocks_per_seq;
+    const int la = max(capped_len(p, p.context_lens[s]), 0);
+    const int lb = max(capped_len(p, p.context_lens[s - 1]), 0);
+    // both lengths are within their tables, so entries below n exist in both rows
+    const int n = min((la + B - 1) >> lg, (lb + B - 1) >> lg);
+    const int32_t* a = p.block_tables + (size_t)s * mb;
+    const int32_t* b = a - mb;
+    c = n;
+    for (int k0 = 0; k0 < n; k0 += 64 * kLinkSpan) {
+      int va[kLinkSpan], vb[kLinkSpan];
+#pragma unroll
+      for (int h = 0; h < kLinkSpan; ++h) {
+        const int k = min(k0 + 64 * h + lane, n - 1);
+        va[h] = a[k];
+        vb[h] = b[k];
+      }
+      int found = -1;
+#pragma unroll
+      for (int h = 0; h < kLinkSpan; ++h) {
+        const int k = k0 + 64 * h + lane;
+        const unsigned long long m = __ballot(k < n && va[h] != vb[h]);
+        if (found < 0 && m) found = k0 + 64 * h + __builtin_ctzll(m);
+      }
+      if (found >= 0) {
+        c = found;
+        break;
+      }
+    }
+  }
+  if (lane == 0) p.links[s] = c;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p, int W) {
+  __shared__ int s_fam[kSharedMaxSeqs];     // per family leader: shared tokens (0: no family)
+  __shared__ int s_cb[kSharedMaxSeqs];      // per leader: least common prefix (blocks) of its members
+  __shared__ int s_ml[kSharedMaxSeqs];      // per leader: least last-token position of its group
+  __shared__ int s_gn[kSharedMaxSeqs];      // per leader: sequences in its group
+  __shared__ int s_item[2 * kSharedMaxSeqs];  // first chunk of every item
+  __shared__ int s_rec[2 * kSharedMaxSeqs][kItemInts];
+  __shared__ int s_tot[kPlanWaves];
+  __shared__ int2 s_tot2[kPlanWaves];
+  __shared__ int s_misc[4];
+  const int S = p.num_seqs, t = threadIdx.x;
+  const int B = p.block_size, F = p.fam_max;
+  // one sequence per thread (S <= kPlanThreads); loads of valid rows for
+  // every thread, results used where they apply
+  const int s = t;
+  const bool has = s < S;
+  const int sc = min(s, S - 1);
+  const int L_raw = p.context_lens[sc];
+  const int cpre = p.links[sc];
+  const int L = has ? max(capped_len(p, L_raw), 0) : 0;
+  // families: runs of linked sequences cut into groups of F from the run's start
+  const bool link = has && s > 0 && cpre * B >= kSharedMinChunks * kChunk;
+  const int run = plan_scan(has && !link ? s : 0, s_tot, true);
+  const int leader = run + F * ((s - run) / F);
+  if (has && leader == s) {
+    s_cb[s] = INT_MAX;
+    s_ml[s] = L - 1;
+    s_gn[s] = 1;
+  }
+  __syncthreads();
+  if (has && leader != s) {
+    atomicMin(&s_cb[leader], cpre);
+    atomicMin(&s_ml[leader], L - 1);
+    atomicAdd(&s_gn[leader], 1);
+  }
+  __syncthreads();
+  // the shared tokens: the members' least common prefix, below every
+  // member's last token, in whole chunks; a group of one, or one sharing
+  // fewer than kSharedMinChunks chunks, disbands (every member alone)
+  int members = 0;
+  if (has && leader == s) {
+    const int gsize = s_gn[s];
+    int sf = 0;
+    if (gsize > 1) sf = (int)(min((long long)s_cb[s] * B, (long long)s_ml[s]) / kChunk * kChunk);
+    members = gsize;
+    if (gsize < 2 || sf < kSharedMinChunks * kChunk) {
+      members = 1;
+      sf = 0;
+    }
+    s_fam[s] = sf;
+  }
+  __syncthreads();
+  const int my_sf = has ? s_fam[leader] : 0;
+  const bool fam_leader = has && leader == s && members > 1;
+  // items of this sequence (a family leader: the common prefix, then its
+  // rest), their index, the family index, their chunks
+  const int nitems = has ? (fam_leader ? 2 : 1) : 0;
+  const int pre_chunks = fam_leader ? my_sf / kChunk : 0;
+  const int own_chunks = num_chunks(L - my_sf);
+  const int chunks = pre_chunks + own_chunks;
+  // one pass: items (< 2^15) in the low half and families in the high half
+  // of the first sum, chunks in the second
+  const int2 sums = plan_scan2(int2{nitems | ((fam_leader ? 1 : 0) << 16), chunks}, s_tot2);
+  const int item0 = (sums.x & 0xffff) - nitems;
+  const int fam = (sums.x >> 16) - 1;
+  const int c0 = sums.y - chunks;
+  if (t == kPlanThreads - 1) {
+    s_misc[1] = item0 + nitems;  // items
+    s_misc[2] = c0 + chunks;     // chunks per KV head
+  }
+  if (fam_leader) {
+    s_rec[item0][0] = s | (members << 16);
+    s_rec[item0][1] = fam;
+    s_rec[item0][2] = my_sf;
+    s_rec[item0][3] = c0;
+    s_item[item0] = c0;
+  }
+  if (has) {
+    const int it = item0 + nitems - 1;
+    s_rec[it][0] = s | (1 << 16);
+    s_rec[it][1] = my_sf;
+    s_rec[it][2] = L;
+    s_rec[it][3] = c0 + pre_chunks;
+    s_item[it] = c0 + pre_chunks;
+  }
+  __syncthreads();
+  const int NI = s_misc[1], T = s_misc[2];
+  for (int i = t; i < NI * kItemInts; i += kPlanThreads) p.items[i] = s_rec[i / kItemInts][i % kItemInts];
+  const int Wn = min(W, T);
+  for (int w = t; w < W; w += kPlanThreads) {
+    int32_t* r = p.wrec + (size_t)w * kWorkerInts;
+    int start = 0, end = 0, first = 0;
+    if (w < Wn) {
+      start = (int)((long long)w * T / Wn);
+      end = (int)((long long)(w + 1) * T / Wn);
+      // the last item whose first chunk is at or before `start` (items
+      // without chunks share their successor's first chunk)
+      int lo = 0, hi = NI;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_item[mid] <= start) lo = mid;
+        else hi = mid;
+      }
+      first = lo;
+    }
+    r[0] = start;
+    r[1] = end;
+    r[2] = first;
+    r[3] = T;
+    r[4] = NI;
+    r[5] = r[6] = r[7] = 0;
+#pragma unroll
+    for (int j = 0; j < kItemInts; ++j) r[8 + j] = NI > 0 ? s_rec[first][j] : 0;
+  }
 }
 
 // Combine the partial results of every split (sequence, KV head): the
@@ -999,6 +1557,18 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
 // many: four waves per (sequence, query head), reading 16 bytes per lane.
 constexpr int kMergeTile = 256;
 
+// Where the k-th piece of a sequence's partial results lies: its family's
+// pieces first (shared mode: slots fam_first + k * fam_stride), then its own
+// (slots own_first + k - fam_n).
+template <bool SHARED>
+struct PieceMap {
+  int fam_first, fam_n, fam_stride, own_first;
+  __device__ int slot(int k) const {
+    if (!SHARED) return own_first + k;
+    return k < fam_n ? fam_first + k * fam_stride : own_first + (k - fam_n);
+  }
+};
+
 template <int W>
 struct MergeSmem {
   float wgt[kMaxGroup][kMergeTile];
@@ -1006,16 +1576,17 @@ struct MergeSmem {
   float part[W][kMaxGroup][128];
 };
 
-template <int D, int W>
-__device__ void merge_long(const DecodeParams& p, int s, int head0, int nh, int tid, int first_slot, int npieces) {
+template <int D, int W, bool SHARED>
+__device__ void merge_long(const DecodeParams& p, int s, int head0, int nh, int tid, const PieceMap<SHARED>& pm,
+                           int npieces) {
   const int Hq = p.num_heads;
   for (int idx = tid; idx < nh * D; idx += 64 * W) {
     const int head = head0 + idx / D, dd = idx % D;
     float M = kNegInf;
-    for (int k = 0; k < npieces; ++k) M = fmaxf(M, p.ws_ml[((size_t)(first_slot + k) * Hq + head) * 2]);
+    for (int k = 0; k < npieces; ++k) M = fmaxf(M, p.ws_ml[((size_t)pm.slot(k) * Hq + head) * 2]);
     float num = 0.f, den = 0.f;
     for (int k = 0; k < npieces; ++k) {
-      const size_t r = (size_t)(first_slot + k) * Hq + head;
+      const size_t r = (size_t)pm.slot(k) * Hq + head;
       const float wgt = fast_exp2(p.ws_ml[r * 2] - M);
       den = fmaf(wgt, p.ws_ml[r * 2 + 1], den);
       num = fmaf(wgt, p.ws_acc[r * D + dd], num);
@@ -1030,9 +1601,9 @@ __device__ void merge_long(const DecodeParams& p, int s, int head0, int nh, int 
 // kIn * W * 64/(D/4)) are in flight before the weights are formed. Piece k
 // of wave v's instruction t is (t W + v) 64/(D/4) + lane / (D/4). The lane
 // groups of a wave are then added by lane swaps and the W waves in wave order.
-template <int D, int W>
-__device__ void merge_one_head(const DecodeParams& p, MergeSmem<W>& sm, int s, int head, int tid, int first_slot,
-                               int npieces) {
+template <int D, int W, bool SHARED>
+__device__ void merge_one_head(const DecodeParams& p, MergeSmem<W>& sm, int s, int head, int tid,
+                               const PieceMap<SHARED>& pm, int npieces) {
   constexpr int LPP = D / 4;     // lanes per piece
   constexpr int PPW = 64 / LPP;  // pieces per wave instruction
   constexpr int kIn = 16;
@@ -1040,15 +1611,15 @@ __device__ void merge_one_head(const DecodeParams& p, MergeSmem<W>& sm, int s, i
   const int wave = tid >> 6, lane = tid & 63;
   const int po = lane / LPP, d4 = (lane % LPP) * 4;
   const size_t step = (size_t)Hq * D;
-  const float* base = p.ws_acc + ((size_t)first_slot * Hq + head) * D + d4;
+  const float* base = p.ws_acc + (size_t)head * D + d4;
   f32x4 x[kIn];
 #pragma unroll
   for (int t = 0; t < kIn; ++t) {
     const int k = (t * W + wave) * PPW + po;
-    x[t] = k < npieces ? *reinterpret_cast<const f32x4*>(base + (size_t)k * step) : f32x4{0.f, 0.f, 0.f, 0.f};
+    x[t] = k < npieces ? *reinterpret_cast<const f32x4*>(base + (size_t)pm.slot(k) * step) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   for (int i = tid; i < npieces; i += 64 * W) {
-    const size_t r = ((size_t)(first_slot + i) * Hq + head) * 2;
+    const size_t r = ((size_t)pm.slot(i) * Hq + head) * 2;
     sm.wgt[0][i] = p.ws_ml[r];
     sm.ls[0][i] = p.ws_ml[r + 1];
   }
@@ -1078,7 +1649,7 @@ __device__ void merge_one_head(const DecodeParams& p, MergeSmem<W>& sm, int s, i
   }
 #pragma unroll 4
   for (int k = (kIn * W + wave) * PPW + po; k < npieces; k += W * PPW)
-    acc += sm.wgt[0][k] * *reinterpret_cast<const f32x4*>(base + (size_t)k * step);
+    acc += sm.wgt[0][k] * *reinterpret_cast<const f32x4*>(base + (size_t)pm.slot(k) * step);
 #pragma unroll
   for (int off = LPP; off < 64; off <<= 1) {
     acc.x += __shfl_xor(acc.x, off);
@@ -1104,15 +1675,15 @@ __device__ void merge_one_head(const DecodeParams& p, MergeSmem<W>& sm, int s, i
 // The one-wave form (few pieces per sequence): lane l holds output elements
 // l, l + 64, ... of every head; each lane's first kPre pieces are requested
 // together with the (m, l) pairs.
-template <int D>
+template <int D, bool SHARED>
 __device__ void merge_heads_one_wave(const DecodeParams& p, MergeSmem<1>& sm, int s, int head0, int nh, int tid,
-                                     int first_slot, int npieces) {
+                                     const PieceMap<SHARED>& pm, int npieces) {
   constexpr int kPre = 4;
   const int Hq = p.num_heads;
   const int lane = tid;
   constexpr int PER = D / 64;
   const size_t step = (size_t)Hq * D;
-  const float* acc0 = p.ws_acc + ((size_t)first_slot * Hq + head0) * D + lane;
+  const float* acc0 = p.ws_acc + (size_t)head0 * D + lane;
   float pre[kPre][kMaxGroup][PER];
 #pragma unroll
   for (int j = 0; j < kPre; ++j)
@@ -1120,11 +1691,11 @@ __device__ void merge_heads_one_wave(const DecodeParams& p, MergeSmem<1>& sm, in
     for (int h = 0; h < kMaxGroup; ++h)
 #pragma unroll
       for (int i = 0; i < PER; ++i)
-        pre[j][h][i] = (h < nh && j < npieces) ? acc0[(size_t)h * D + j * step + 64 * i] : 0.f;
+        pre[j][h][i] = (h < nh && j < npieces) ? acc0[(size_t)h * D + (size_t)pm.slot(j) * step + 64 * i] : 0.f;
   // (m, l) of every (head, piece): m into wgt, l kept in the same slot's pair
   for (int i = tid; i < nh * npieces; i += 64) {
     const int h = i / npieces, k = i % npieces;
-    const size_t r = ((size_t)(first_slot + k) * Hq + head0 + h) * 2;
+    const size_t r = ((size_t)pm.slot(k) * Hq + head0 + h) * 2;
     sm.wgt[h][k] = p.ws_ml[r];
     sm.ls[h][k] = p.ws_ml[r + 1];
   }
@@ -1163,12 +1734,13 @@ __device__ void merge_heads_one_wave(const DecodeParams& p, MergeSmem<1>& sm, in
   }
 #pragma unroll 2
   for (int k = kPre; k < npieces; ++k) {
+    const size_t off = (size_t)pm.slot(k) * step;
 #pragma unroll
     for (int h = 0; h < kMaxGroup; ++h) {
       if (h < nh) {
         const float w = sm.wgt[h][k];
 #pragma unroll
-        for (int i = 0; i < PER; ++i) acc[h][i] = fmaf(w, acc0[(size_t)h * D + k * step + 64 * i], acc[h][i]);
+        for (int i = 0; i < PER; ++i) acc[h][i] = fmaf(w, acc0[(size_t)h * D + off + 64 * i], acc[h][i]);
       }
     }
   }
@@ -1183,30 +1755,34 @@ __device__ void merge_heads_one_wave(const DecodeParams& p, MergeSmem<1>& sm, in
 // Combines the pieces of query heads head0 .. head0+nh-1 of sequence s when
 // it was split; called by the whole workgroup. L_raw and the split record
 // (meta_first, meta_n; balanced mode) were loaded by the caller.
-template <int D, int W>
+template <int D, int W, bool SHARED>
 __device__ void merge_sequence(const DecodeParams& p, MergeSmem<W>& sm, int s, int head0, int nh, int tid, int L_raw,
-                               int meta_first, int meta_n) {
+                               const int* meta) {
   static_assert(D <= 128, "partial-sum tile");
   const int L = capped_len(p, L_raw);
   if (L <= 0) return;
-  int first_slot, npieces;
-  if (p.mode != kModeBalanced) {
+  PieceMap<SHARED> pm{0, 0, 1, 0};
+  int npieces;
+  if (SHARED) {
+    pm = PieceMap<SHARED>{meta[0], meta[1], p.fam_max, meta[2]};
+    npieces = meta[1] + meta[3];
+  } else if (p.mode == kModeFixed || p.mode == kModeFixedStream) {
     const int P = p.part_chunks * kChunk;
     npieces = (L + P - 1) / P;
-    first_slot = s * p.max_parts;
+    pm.own_first = s * p.max_parts;
   } else {
-    first_slot = meta_first;
-    npieces = meta_n;
+    pm.own_first = meta[0];
+    npieces = meta[1];
   }
   if (npieces <= 1) return;
   if (npieces > kMergeTile) {
-    merge_long<D, W>(p, s, head0, nh, tid, first_slot, npieces);
+    merge_long<D, W, SHARED>(p, s, head0, nh, tid, pm, npieces);
   } else if constexpr (W > 1) {
     // the W-wave launch gives each workgroup one query head
-    if (nh == 1) merge_one_head<D, W>(p, sm, s, head0, tid, first_slot, npieces);
-    else merge_long<D, W>(p, s, head0, nh, tid, first_slot, npieces);
+    if (nh == 1) merge_one_head<D, W, SHARED>(p, sm, s, head0, tid, pm, npieces);
+    else merge_long<D, W, SHARED>(p, s, head0, nh, tid, pm, npieces);
   } else {
-    merge_heads_one_wave<D>(p, sm, s, head0, nh, tid, first_slot, npieces);
+    merge_heads_one_wave<D, SHARED>(p, sm, s, head0, nh, tid, pm, npieces);
   }
 }
 
@@ -1228,7 +1804,7 @@ __device__ __forceinline__ int new_token_slot(const DecodeParams& p, int s, int 
 // every read of the cache by the attention kernel, which took the new token
 // from k_new/v_new; its values are read first and stored last, so its round
 // trips overlap the merge's.
-template <int D, typename U, int W>
+template <int D, typename U, int W, bool SHARED>
 __global__ __launch_bounds__(64 * W) void merge_kernel(DecodeParams p) {
   __shared__ MergeSmem<W> sm;
   const int s = blockIdx.x, kvh = blockIdx.y, tid = threadIdx.x;
@@ -1236,10 +1812,15 @@ __global__ __launch_bounds__(64 * W) void merge_kernel(DecodeParams p) {
   const int nh = p.group / gridDim.z, head0 = kvh * p.group + (int)blockIdx.z * nh;
   // every load that depends on nothing else is issued first
   const int L = p.context_lens[s];
-  int meta_first = 0, meta_n = 0;
-  if (p.merge && p.mode == kModeBalanced) {
-    meta_first = p.ws_meta[2 * s];
-    meta_n = p.ws_meta[2 * s + 1];
+  // split record: {own first slot, own pieces}, or in shared mode {family
+  // first slot, family pieces, own first slot, own pieces}
+  int meta[4] = {0, 0, 0, 0};
+  if (SHARED) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) meta[i] = p.ws_meta[(size_t)s * 4 + i];
+  } else if (p.merge && p.mode == kModeBalanced) {
+    meta[0] = p.ws_meta[2 * s];
+    meta[1] = p.ws_meta[2 * s + 1];
   }
   // the new token's elements e = tid, tid + 64W, ..., read unconditionally
   // (from q without one: an in-bounds row, never stored) and widened, so
@@ -1259,7 +1840,7 @@ __global__ __launch_bounds__(64 * W) void merge_kernel(DecodeParams p) {
   }
   // the slot's block-table entry is requested before the merge's loads
   const int slot = (p.k_new && blockIdx.z == 0) ? new_token_slot(p, s, L) : -1;
-  if (p.merge) merge_sequence<D, W>(p, sm, s, head0, nh, tid, L, meta_first, meta_n);
+  if (p.merge) merge_sequence<D, W, SHARED>(p, sm, s, head0, nh, tid, L, meta);
   if (slot >= 0) {
     const int B = p.block_size, phys = slot / B, off = slot % B, Bs = v_subtile(B);
     U* kd = const_cast<U*>(static_cast<const U*>(p.k_cache)) + (((size_t)phys * Hkv + kvh) * B + off) * D;
@@ -1345,14 +1926,18 @@ const void* vec_kernel_d(int D, int G) {
   return D == 64 ? vec_kernel<E, 64>(G) : (D == 128 ? vec_kernel<E, 128>(G) : nullptr);
 }
 
+template <int NCG>
+const void* mfma_kernel(int elem, int head_dim) {
+  if (elem == kBF16) return head_dim == 64 ? kernel_of<MfmaEngine<kBF16, 64, kMfmaSub, NCG>, 64>()
+                                           : (head_dim == 128 ? kernel_of<MfmaEngine<kBF16, 128, kMfmaSub, NCG>, 128>() : nullptr);
+  if (elem == kF16) return head_dim == 64 ? kernel_of<MfmaEngine<kF16, 64, kMfmaSub, NCG>, 64>()
+                                          : (head_dim == 128 ? kernel_of<MfmaEngine<kF16, 128, kMfmaSub, NCG>, 128>() : nullptr);
+  return nullptr;
+}
+
 const void* decode_fn(int elem, int head_dim, int algo, int G) {
-  if (algo == kAlgoMfma) {
-    if (elem == kBF16) return head_dim == 64 ? kernel_of<MfmaEngine<kBF16, 64, kMfmaSub>, 64>()
-                                             : (head_dim == 128 ? kernel_of<MfmaEngine<kBF16, 128, kMfmaSub>, 128>() : nullptr);
-    if (elem == kF16) return head_dim == 64 ? kernel_of<MfmaEngine<kF16, 64, kMfmaSub>, 64>()
-                                            : (head_dim == 128 ? kernel_of<MfmaEngine<kF16, 128, kMfmaSub>, 128>() : nullptr);
-    return nullptr;
-  }
+  if (algo == kAlgoMfma) return mfma_kernel<1>(elem, head_dim);
+  if (algo == kAlgoMfmaShared) return mfma_kernel<kSharedColumnGroups>(elem, head_dim);
   if (elem == kF32) return vec_kernel_d<kF32>(head_dim, G);
   if (elem == kF16) return vec_kernel_d<kF16>(head_dim, G);
   if (elem == kBF16) return vec_kernel_d<kBF16>(head_dim, G);
@@ -1364,7 +1949,13 @@ const void* decode_fn(int elem, int head_dim, int algo, int G) {
 size_t decode_static_lds(int elem, int head_dim, int algo, int G) {
   if (algo == kAlgoMfma) {
     if (elem == kF32) return 0;
-    return head_dim == 64 ? sizeof(MfmaEngine<kBF16, 64, kMfmaSub>::Smem) : sizeof(MfmaEngine<kBF16, 128, kMfmaSub>::Smem);
+    return head_dim == 64 ? sizeof(MfmaEngine<kBF16, 64, kMfmaSub, 1>::Smem)
+                          : sizeof(MfmaEngine<kBF16, 128, kMfmaSub, 1>::Smem);
+  }
+  if (algo == kAlgoMfmaShared) {
+    if (elem == kF32) return 0;
+    return head_dim == 64 ? sizeof(MfmaEngine<kBF16, 64, kMfmaSub, kSharedColumnGroups>::Smem)
+                          : sizeof(MfmaEngine<kBF16, 128, kMfmaSub, kSharedColumnGroups>::Smem);
   }
   const int D = head_dim;
   switch (G) {
@@ -1373,6 +1964,24 @@ size_t decode_static_lds(int elem, int head_dim, int algo, int G) {
     case 4: return D == 64 ? sizeof(VecEngine<kF32, 64, 4>::Smem) : sizeof(VecEngine<kF32, 128, 4>::Smem);
     default: return D == 64 ? sizeof(VecEngine<kF32, 64, 8>::Smem) : sizeof(VecEngine<kF32, 128, 8>::Smem);
   }
+}
+
+template <int D, typename U, int W>
+const void* merge_fn_w(bool shared) {
+  return shared ? reinterpret_cast<const void*>(&merge_kernel<D, U, W, true>)
+                : reinterpret_cast<const void*>(&merge_kernel<D, U, W, false>);
+}
+
+// The closing launch's kernel: element width, head_dim, one or four waves,
+// and whether split records come from the shared mode (only 16-bit
+// elements run it).
+const void* merge_fn(int elem, int head_dim, bool wide, bool shared) {
+  if (elem == kF32) {
+    if (wide) return head_dim == 64 ? merge_fn_w<64, uint32_t, 4>(false) : merge_fn_w<128, uint32_t, 4>(false);
+    return head_dim == 64 ? merge_fn_w<64, uint32_t, 1>(false) : merge_fn_w<128, uint32_t, 1>(false);
+  }
+  if (wide) return head_dim == 64 ? merge_fn_w<64, uint16_t, 4>(shared) : merge_fn_w<128, uint16_t, 4>(shared);
+  return head_dim == 64 ? merge_fn_w<64, uint16_t, 1>(shared) : merge_fn_w<128, uint16_t, 1>(shared);
 }
 
 hipError_t launch_decode(const DecodeParams& p, int elem, int head_dim, int algo, int G, unsigned workers,
@@ -1384,7 +1993,7 @@ hipError_t launch_decode(const DecodeParams& p, int elem, int head_dim, int algo
   // dynamic LDS: the lengths (balanced split and partition stream), then as
   // many result slots as the workgroup's share of the CU's LDS leaves room
   // for (at least one; one segment per workgroup needs no more)
-  args.lens_pad = p.mode == kModeFixed ? 0 : (p.num_seqs + 3) / 4 * 4;
+  args.lens_pad = (p.mode == kModeFixed || p.mode == kModeShared) ? 0 : (p.num_seqs + 3) / 4 * 4;
   const size_t lens_bytes = (size_t)args.lens_pad * sizeof(int32_t);
   const size_t slot_bytes = ((size_t)p.group * head_dim + 2 * (size_t)p.group + kResRec) * sizeof(float);
   const size_t fixed = decode_static_lds(elem, head_dim, algo, G) + lens_bytes;
@@ -1400,26 +2009,25 @@ hipError_t launch_decode(const DecodeParams& p, int elem, int head_dim, int algo
   // few pieces per sequence: one wave per (sequence, KV head); many (fixed
   // partitions, or a balanced split of few sequences over many workers):
   // four waves per (sequence, query head)
-  const bool wide = merge && (p.mode == kModeBalanced ? (long long)workers > 4LL * p.num_seqs : p.max_parts > 4);
-  const void* mf;
-  if (wide) {
-    if (elem == kF32)
-      mf = head_dim == 64 ? reinterpret_cast<const void*>(&merge_kernel<64, uint32_t, 4>)
-                          : reinterpret_cast<const void*>(&merge_kernel<128, uint32_t, 4>);
-    else
-      mf = head_dim == 64 ? reinterpret_cast<const void*>(&merge_kernel<64, uint16_t, 4>)
-                          : reinterpret_cast<const void*>(&merge_kernel<128, uint16_t, 4>);
-  } else {
-    if (elem == kF32)
-      mf = head_dim == 64 ? reinterpret_cast<const void*>(&merge_kernel<64, uint32_t, 1>)
-                          : reinterpret_cast<const void*>(&merge_kernel<128, uint32_t, 1>);
-    else
-      mf = head_dim == 64 ? reinterpret_cast<const void*>(&merge_kernel<64, uint16_t, 1>)
-                          : reinterpret_cast<const void*>(&merge_kernel<128, uint16_t, 1>);
-  }
+  const bool few_seqs = p.mode == kModeBalanced || p.mode == kModeShared;
+  const bool wide = merge && (few_seqs ? (long long)workers > 4LL * p.num_seqs : p.max_parts > 4);
+  const bool shared = p.mode == kModeShared;
+  const void* mf = merge_fn(elem, head_dim, wide, shared);
   const unsigned z = wide ? (unsigned)p.group : 1u;
   return hipLaunchKernel(mf, dim3((unsigned)p.num_seqs, (unsigned)p.num_kv_heads, z), dim3(wide ? 256 : 64, 1, 1),
                          kargs, 0, stream);
+}
+
+hipError_t launch_plan(const DecodeParams& p, unsigned workers, hipStream_t stream) {
+  DecodeParams args = p;
+  int W = (int)workers;
+  void* largs[] = {&args};
+  const unsigned groups = (unsigned)((p.num_seqs + kLinkWaves - 1) / kLinkWaves);
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&link_kernel), dim3(groups), dim3(64 * kLinkWaves),
+                                 largs, 0, stream);
+  if (e != hipSuccess) return e;
+  void* kargs[] = {&args, &W};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&plan_kernel), dim3(1), dim3(kPlanThreads), kargs, 0, stream);
 }
 
 int decode_waves_per_cu(int elem, int head_dim, int algo, int G) {

@@ -21,6 +21,7 @@ holding the raw bfloat16 bits.
 
 from __future__ import annotations
 
+import dataclasses
 import math
 import os
 from concurrent.futures import ThreadPoolExecutor
@@ -574,6 +575,81 @@ def make_shared_prefix_workload(prefix_len: int = 1024, cfg: DecodeConfig = SHAR
             set_v_tokens(v_cache, src, r, pv)
     return DecodeWorkload(cfg, q, k_cache, v_cache, tables, lens, k_new, v_new, slots, num_blocks, poison_block, used,
                           copy_pairs, pre, pre_k, pre_v)
+
+
+def make_forked_workload(cfg: DecodeConfig, groups, poison: bool = True) -> DecodeWorkload:
+    """One decode step of sequences forked from shared prompts: `groups` is a
+    list of (prompt_len, [own_len, ...]); the forks of a group are adjacent
+    in the batch, map the prompt's full blocks by the same ids and hold their
+    own tokens (at least one each, the new token among them) in blocks of
+    their own. A prompt that ends inside a block gives every fork its own
+    copy of that block (as copy-on-write leaves it), holding the prompt's
+    tokens there. Ids come from a seeded permutation of the pool (10% spare,
+    plus a poisoned padding block); values as in make_decode_workload."""
+    seqs = np.random.SeedSequence(1000 + cfg.index).spawn(6)
+    rng_pool = np.random.default_rng(seqs[1])
+    B = cfg.block_size
+    lens, layout = [], []
+    need = 0
+    for prompt_len, owns in groups:
+        full = prompt_len // B
+        need += full
+        for own in owns:
+            if own < 1:
+                raise ValueError("every fork holds at least its new token")
+            L = prompt_len + own
+            need += -(-L // B) - full
+            lens.append(L)
+    num_blocks = math.ceil(1.1 * need) + 1
+    perm = rng_pool.permutation(num_blocks).astype(np.int32)
+    lens = np.array(lens, dtype=np.int32)
+    S = len(lens)
+    max_blocks = max(-(-cfg.max_len // B), int(-(-lens.max() // B)))
+    poison_block = int(perm[need])
+    tables = np.full((S, max_blocks), poison_block, dtype=np.int32)
+    pos, s, copies = 0, 0, []
+    for prompt_len, owns in groups:
+        full = prompt_len // B
+        shared = perm[pos:pos + full]
+        pos += full
+        src = None
+        for own in owns:
+            L = int(lens[s])
+            n = -(-L // B)
+            tables[s, :full] = shared
+            tables[s, full:n] = perm[pos:pos + n - full]
+            pos += n - full
+            if prompt_len % B:
+                if src is None:
+                    src = int(tables[s, full])
+                else:
+                    copies.append((src, int(tables[s, full])))
+            s += 1
+    used = perm[:need]
+    last_pos = lens.astype(np.int64) - 1
+    slots = (tables[np.arange(S), last_pos // B].astype(np.int64) * B + last_pos % B).astype(np.int32)
+    Hkv, d = cfg.num_kv_heads, cfg.head_dim
+    q = random_stored(seqs[2], (S, cfg.num_heads, d), cfg.etype, cfg.value_scale)
+    k_cache = random_stored(seqs[3], (num_blocks, Hkv, B, d), cfg.etype, cfg.value_scale)
+    v_cache = random_stored(seqs[4], (num_blocks, Hkv, d, B), cfg.etype, cfg.value_scale)
+    kn_ss, vn_ss = seqs[5].spawn(2)
+    k_new = random_stored(kn_ss, (S, Hkv, d), cfg.etype, cfg.value_scale)
+    v_new = random_stored(vn_ss, (S, Hkv, d), cfg.etype, cfg.value_scale)
+    # the prompt's tokens in every fork's copy of its partial last block
+    for a, b in copies:
+        k_cache[b] = k_cache[a]
+        v_cache[b] = v_cache[a]
+    if poison:
+        pv = poison_value(cfg.etype)
+        k_cache[perm[need:]] = pv
+        v_cache[perm[need:]] = pv
+        for s in range(S):
+            last = tables[s, int(last_pos[s]) // B]
+            off = int(last_pos[s]) % B          # the new token's slot and the rest
+            k_cache[last, :, off:, :] = pv
+            set_v_tokens(v_cache, last, off, pv)
+    cfg = dataclasses.replace(cfg, num_seqs=S)
+    return DecodeWorkload(cfg, q, k_cache, v_cache, tables, lens, k_new, v_new, slots, num_blocks, poison_block, used)
 
 
 # --------------------------------------------------------------------------

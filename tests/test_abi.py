@@ -123,6 +123,23 @@ def test_decode_workspace_sizes(lib):
     assert f(4, 32, 8, 128, 1024, 40) == 0
 
 
+def test_decode_workspace_sizes_shared_mode(lib):
+    f = lib.pa_decode_workspace_bytes
+    S, Hq, Hkv, d, L = 256, 32, 8, 128, 1280
+    workers = 2048 // Hkv                                  # worker waves per KV head
+    fam_max = 2 * (16 // (Hq // Hkv))                      # members per family
+    slots = workers + 2 * S + (workers + S // 2 + 1) * fam_max
+    need = (S * 4 * 4                                      # split records, four ints
+            + S * 2 * 4 * 4                                # work items
+            + workers * 12 * 4                             # worker records
+            + S * 4                                        # prefix links
+            + slots * Hq * 2 * 4 + slots * Hq * d * 4)     # (m, l) and partial outputs
+    assert f(S, Hq, Hkv, d, L, -2) == need
+    assert f(S, Hq, Hkv, d, L, -2) >= f(S, Hq, Hkv, d, L, -1)
+    # past 1024 sequences the call runs the balanced split and sizes for it
+    assert f(1025, Hq, Hkv, d, L, -2) == f(1025, Hq, Hkv, d, L, -1)
+
+
 def test_write_decode_argument_checks(lib):
     args = decode_args()
     # out, q, k_new, v_new, k, v, then the decode tail without `algo`

@@ -167,3 +167,186 @@ def test_prefill_tile_map_covers_each_tile_once(g):
         for s, k in tiles:
             nq = min(qt, int(n[s]) - k * qt)
             assert 1 <= nq <= qt and nq * g <= 16
+
+
+# ---------------------------------------------------------------------------
+# Shared mode: the plan launch (families, work items, worker ranges) and the
+# workers' walk over the items, modelled as the kernels do them.
+# ---------------------------------------------------------------------------
+
+MIN_CHUNKS = 2  # a shorter common prefix does not form a family
+
+
+def family_max(group):
+    return 2 * (16 // group)
+
+
+def shared_plan(lengths, tables, B, F, W):
+    """Items [seq, members, fam or t0, t1, first chunk] and worker ranges, as
+    the plan kernel lays them out."""
+    S = len(lengths)
+    nblk = [-(-L // B) for L in lengths]
+    c = [0] * S
+    for s in range(1, S):
+        n = min(nblk[s], nblk[s - 1])
+        k = 0
+        while k < n and tables[s][k] == tables[s - 1][k]:
+            k += 1
+        c[s] = k
+    link = [s > 0 and c[s] * B >= MIN_CHUNKS * CHUNK for s in range(S)]
+    run = [0] * S
+    for s in range(S):
+        run[s] = s if not link[s] else run[s - 1]
+    leader = [run[s] + F * ((s - run[s]) // F) for s in range(S)]
+    fam_sf, fam_members = {}, {}
+    for s in range(S):
+        if leader[s] != s:
+            continue
+        g = 1
+        cb, ml = 1 << 40, lengths[s] - 1
+        while g < F and s + g < S and leader[s + g] == s:
+            cb, ml = min(cb, c[s + g]), min(ml, lengths[s + g] - 1)
+            g += 1
+        sf = (min(cb * B, ml) // CHUNK) * CHUNK if g > 1 else 0
+        if g < 2 or sf < MIN_CHUNKS * CHUNK:
+            g, sf = 1, 0
+        fam_members[s] = g
+        for j in range(g):
+            fam_sf[s + j] = sf
+    items, chunk = [], 0
+    fam = 0
+    for s in range(S):
+        sf = fam_sf[s]
+        if leader[s] == s and fam_members[s] > 1:
+            items.append((s, fam_members[s], fam, sf, chunk))   # t1 = sf
+            chunk += sf // CHUNK
+            fam += 1
+        n = -(-(lengths[s] - sf) // CHUNK) if lengths[s] > sf else 0
+        items.append((s, 1, sf, lengths[s], chunk))
+        chunk += n
+    return items, chunk, fam_sf
+
+
+def shared_walk(lengths, tables, B, group, W):
+    S = len(lengths)
+    F = family_max(group)
+    items, T, fam_sf = shared_plan(lengths, tables, B, F, W)
+    starts = [it[4] for it in items]
+    pieces = {s: [] for s in range(S)}
+    meta = {}
+    if T == 0:
+        return pieces, meta, fam_sf, F, 0
+    Wn = min(W, T)
+    owner = lambda c: ((c + 1) * Wn - 1) // T  # noqa: E731
+    wmax = -(-2048 // 8)  # workspace bound used with 8 KV heads below
+    fam_base = wmax + 2 * S
+    for w in range(Wn):
+        start, end = w * T // Wn, (w + 1) * T // Wn
+        i = int(np.searchsorted(starts, start, side="right") - 1)
+        while i < len(items) and items[i][4] < end:
+            seq, members, f_or_t0, t1, c = items[i]
+            t0 = 0 if members > 1 else f_or_t0
+            n = -(-(t1 - t0) // CHUNK) if t1 > t0 else 0
+            if n == 0:
+                i += 1
+                continue
+            c0, c1 = max(start, c), min(end, c + n)
+            first, last = owner(c), owner(c + n - 1)
+            a, b = t0 + (c0 - c) * CHUNK, min(t0 + (c1 - c) * CHUNK, t1)
+            if members > 1:
+                for m in range(members):
+                    slot = fam_base + (w + f_or_t0) * F + m
+                    pieces[seq + m].append(("fam", a, b, slot))
+                    if c0 == c:
+                        meta.setdefault(seq + m, {})["fam"] = (fam_base + (first + f_or_t0) * F + m, last - first + 1)
+            else:
+                pieces[seq].append(("own", a, b, w + i))
+                if c0 == c:
+                    meta.setdefault(seq, {})["own"] = (first + i, last - first + 1)
+                    if t0 == 0:
+                        meta[seq]["fam"] = (0, 0)
+            i += 1
+    return pieces, meta, fam_sf, F, fam_base
+
+
+def forked_tables(rng, S, B):
+    """Sequences forked from a few prompts (adjacent forks share the prompt's
+    blocks, then diverge), with some lone sequences and some empty ones."""
+    lengths, tables, nxt = [], [], [0]
+
+    def fresh(k):
+        out = list(range(nxt[0], nxt[0] + k))
+        nxt[0] += k
+        return out
+
+    s = 0
+    while s < S:
+        forks = int(rng.integers(1, 12))
+        plen = int(rng.integers(0, 400))
+        prompt = fresh(-(-plen // B))
+        for _ in range(min(forks, S - s)):
+            own = int(rng.integers(0, 200))
+            L = plen + own
+            if plen % B and own:
+                base = prompt[:-1] + fresh(1)   # copy-on-write of the partial last block
+            else:
+                base = list(prompt)
+            tbl = base + fresh(-(-L // B) - len(base))
+            lengths.append(L)
+            tables.append(tbl)
+            s += 1
+    return lengths, tables
+
+
+@pytest.mark.parametrize("B,group,W", [(16, 4, 128), (16, 4, 3), (8, 1, 64), (32, 8, 17), (16, 2, 1000),
+                                       (128, 4, 50)])
+def test_shared_plan_covers_each_token_once(B, group, W):
+    rng = np.random.default_rng(B * 7 + group * 3 + W)
+    for trial in range(40):
+        S = int(rng.integers(1, 40))
+        lengths, tables = forked_tables(rng, S, B)
+        pieces, meta, fam_sf, F, fam_base = shared_walk(lengths, tables, B, group, W)
+        slots = set()
+        for s, L in enumerate(lengths):
+            got = sorted(pieces[s], key=lambda x: x[1])
+            covered = [t for (_, a, b, _) in got for t in range(a, b)]
+            assert covered == list(range(L)), (lengths, s)
+            sf = fam_sf[s]
+            assert sf % CHUNK == 0 and (sf == 0 or sf <= L - 1)
+            # a family's common prefix lies in blocks every member maps alike
+            for (kind, a, b, _) in got:
+                if kind == "fam":
+                    leader = s
+                    while leader > 0 and fam_sf.get(leader - 1) == sf and tables[leader - 1][:(b + B - 1) // B] == tables[s][:(b + B - 1) // B]:
+                        leader -= 1
+                    assert tables[leader][:(b + B - 1) // B] == tables[s][:(b + B - 1) // B]
+            for (_, _, _, slot) in got:
+                assert slot not in slots
+                slots.add(slot)
+            if L == 0:
+                continue
+            # the merge record names exactly the pieces that exist
+            fam_first, fam_n = meta[s]["fam"]
+            own_first, own_n = meta[s]["own"]
+            fam_slots = sorted(x[3] for x in got if x[0] == "fam")
+            own_slots = sorted(x[3] for x in got if x[0] == "own")
+            assert fam_slots == [fam_first + k * F for k in range(fam_n)]
+            assert own_slots == [own_first + k for k in range(own_n)]
+            assert all(x < fam_base for x in own_slots)
+            assert all(x < fam_base + (-(-2048 // 8) + len(lengths) // 2 + 1) * F for x in fam_slots)
+
+
+def test_shared_plan_families_of_the_sampling_workload():
+    # 32 prompts of 1016 tokens x 8 samples (B = 16): each prompt's samples
+    # form one family (8 = 2 groups x 4 members at g = 4) over the first 992
+    # tokens (the partial last prompt block is each sample's own copy)
+    from paged_kv_cache_131_amd import workloads as wl
+
+    ps = wl.ParallelSamplingWorkload(prompt_len=1016, values=False)
+    st = ps.step()
+    lengths = st.context_lens.tolist()
+    tables = [list(st.block_tables[s, :-(-L // 16)]) for s, L in enumerate(lengths)]
+    items, T, fam_sf = shared_plan(lengths, tables, 16, family_max(4), 128)
+    fams = [it for it in items if it[1] > 1]
+    assert len(fams) == 32 and all(it[1] == 8 and it[3] == 992 for it in fams)
+    assert T == 32 * 31 + sum(-(-(L - 992) // CHUNK) for L in lengths)
