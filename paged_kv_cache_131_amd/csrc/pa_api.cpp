@@ -40,7 +40,9 @@ struct Plan {
 // counts in int; otherwise the call runs the balanced split.
 bool shared_ok(int num_seqs, int max_context_len) {
   const long long max_chunks = ((long long)max_context_len + pa::kChunk - 1) / pa::kChunk;
-  return num_seqs <= pa::kSharedMaxSeqs && (long long)num_seqs * max_chunks < (1LL << 30);
+  // chunk counts and the plan's costs (at most 2 * kCostChunk per chunk
+  // plus the item ends) in int
+  return num_seqs <= pa::kSharedMaxSeqs && (long long)num_seqs * max_chunks < (1LL << 26);
 }
 
 Plan make_plan(int num_seqs, int num_kv_heads, int max_context_len, int partition_size) {

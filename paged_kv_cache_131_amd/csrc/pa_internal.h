@@ -32,8 +32,17 @@ constexpr int kSharedMaxSeqs = 1024;      // sequences a shared-mode call takes 
 constexpr int kSharedColumnGroups = 2;    // 16-column MFMA groups of a family segment
 constexpr int kSharedMinChunks = 2;       // a shorter common prefix does not form a family
 constexpr int kSharedMaxWorkersTotal = 2048;  // workers summed over KV heads (sizes the workspace)
-constexpr int kItemInts = 4;              // ints per work item record
-constexpr int kWorkerInts = 12;           // ints per worker record: range, first item, its record
+constexpr int kItemInts = 8;              // ints per work item record
+constexpr int kWorkerInts = 16;           // ints per worker record: range, first item, its record
+// Estimated cost of the shared-mode work, in sixteenths of a one-group
+// 32-token chunk (per-worker clock logs of the parallel-sampling step: a
+// chunk 2.3 us, a two-group family chunk 2.5 us, a member's epilogue about
+// 0.4 us, the end of an item and the start of the next about 0.6 us). The
+// plan splits the total cost evenly over the workers.
+constexpr int kCostChunk = 16;        // a chunk, one column group
+constexpr int kCostGroupChunk = 1;    // more per chunk and column group of a family's prefix
+constexpr int kCostMemberEnd = 3;     // a finished family prefix, per member
+constexpr int kCostItemEnd = 4;       // a finished item
 // Most members of a family: column groups times the members one 16-column
 // group holds (a member takes g columns, one per query head).
 inline int shared_family_max(int group) { return kSharedColumnGroups * (16 / group); }

@@ -210,7 +210,7 @@ struct MfmaEngine {
   static constexpr int MQ = D / 32;  // QK k-steps
   static constexpr int NT = D / 16;  // PV column tiles
   static constexpr int kPad = 4;
-  static constexpr int kMaxGroup = kDistinct ? 16 : 8;  // query heads per KV head the slots hold
+  static constexpr int kMaxGroup = pa::kMaxGroup;  // a sequence's heads per KV head (one result)
   struct alignas(16) Smem {
     float o[16][D + kPad];
     float ml[16][2];
@@ -742,27 +742,29 @@ __device__ __forceinline__ long long owner_of(long long c, long long W, long lon
 
 // Work item i of a shared-mode plan: {sequence | members << 16, family
 // index (members > 1) or first token, end token, first chunk in the
-// laid-out order}, read with scalar loads (the plan is read-only for the
-// launch); a worker's first item comes with its worker record.
+// laid-out order, the worker holding that chunk, the workers it spans, 0,
+// 0}, read with scalar loads (the plan is read-only for the launch); a
+// worker's first item comes with its worker record.
 struct Item {
-  int seq, members, fam, t0, t1;
+  int seq, members, fam, t0, t1, owner, npieces;
   long long c;
 };
 
-__device__ __forceinline__ Item make_item(int r0, int r1, int r2, int r3) {
+__device__ __forceinline__ Item make_item(const const_i32* r) {
   Item it;
-  it.seq = r0 & 0xffff;
-  it.members = r0 >> 16;
-  it.fam = it.members > 1 ? r1 : -1;
-  it.t0 = it.members > 1 ? 0 : r1;
-  it.t1 = r2;
-  it.c = r3;
+  it.seq = r[0] & 0xffff;
+  it.members = r[0] >> 16;
+  it.fam = it.members > 1 ? r[1] : -1;
+  it.t0 = it.members > 1 ? 0 : r[1];
+  it.t1 = r[2];
+  it.c = r[3];
+  it.owner = r[4];
+  it.npieces = r[5];
   return it;
 }
 
 __device__ __forceinline__ Item item_at(const DecodeParams& p, int i) {
-  const const_i32* q = (const const_i32*)p.items + (size_t)i * kItemInts;
-  return make_item(q[0], q[1], q[2], q[3]);
+  return make_item((const const_i32*)p.items + (size_t)i * kItemInts);
 }
 
 // Yields a worker's segments in order. Balanced mode: the chunks of all
@@ -856,9 +858,8 @@ struct SegmentSource : ItemWalk<SHARED> {
       g.t0 = it.t0 + (int)(c0 - c) * kChunk;
       g.t1 = min(it.t0 + (int)(c1 - c) * kChunk, it.t1);
       g.lbl = (g.t1 - 1) >> p.log2_block;
-      const int first = (int)owner_of(c, W, T);
-      const int last = (int)owner_of(c + n - 1, W, T);
-      g.npieces = last - first + 1;
+      const int first = it.owner;
+      g.npieces = it.npieces;
       const bool head = c0 == c;
       if (it.members > 1) {
         g.tnew = -1;  // a family's common prefix ends before every member's last token
@@ -1026,14 +1027,22 @@ __device__ void flush_results(const DecodeParams& p, ResultBuf& rb, int kvh, int
     }
     if (r[5]) {
       const size_t base = ((size_t)s * Hq + head0) * D;
+      // one loop per output form, the choice made once per result
+      if (p.out_dtype == kF32 && out_vec) {
+        f32x4* o = reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + base);
 #pragma unroll
-      for (int u = 0; u < kV4; ++u) {
-        const int i = lane + 64 * u;
-        if (i >= n4) continue;
-        if (NT && p.out_dtype == kF32 && out_vec)
-          store16<NT>(reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + base) + i, t[u]);
-        else
-          store_out4(p.out, base + 4 * (size_t)i, t[u], p.out_dtype, out_vec);
+        for (int u = 0; u < kV4; ++u)
+          if (lane + 64 * u < n4) store16<NT>(o + lane + 64 * u, t[u]);
+      } else if (out_vec) {
+        const int dt = p.out_dtype;
+#pragma unroll
+        for (int u = 0; u < kV4; ++u)
+          if (lane + 64 * u < n4) store_out4(p.out, base + 4 * (size_t)(lane + 64 * u), t[u], dt, true);
+      } else {
+        const int dt = p.out_dtype;
+#pragma unroll
+        for (int u = 0; u < kV4; ++u)
+          if (lane + 64 * u < n4) store_out4(p.out, base + 4 * (size_t)(lane + 64 * u), t[u], dt, false);
       }
     } else {
       const size_t row0 = (size_t)slot * Hq + head0;
@@ -1207,7 +1216,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
     src.T = T;
     src.num_items = wr[4];
     src.first = first;
-    src.first_item = make_item(wr[8], wr[9], wr[10], wr[11]);
+    src.first_item = make_item(wr + 8);
     src.fixed = invalid_segment();
     run_stream<Eng, D>(p, sm, src, kvh, lane);
     return;
@@ -1320,68 +1329,80 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
 // laid end to end in 32-token chunks as the balanced split lays out
 // sequences: a family's common prefix (tokens [0, Sf), Sf a multiple of 32
 // and below every member's last token), then each member's rest [Sf, L); a
-// sequence outside every family is one item [0, L). Worker w of W gets
-// chunks [w T / W', (w + 1) T / W'), W' = min(W, T), as in the balanced split.
+// sequence outside every family is one item [0, L). The W' = min(W, T)
+// workers get contiguous chunk ranges of about equal estimated cost (a
+// family's chunks, with more column groups, and every item's end cost more
+// than a plain chunk), each at least one chunk.
 // ---------------------------------------------------------------------------
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanWaves = kPlanThreads / 64;
 
-// Inclusive sums of two ints per thread over the workgroup, in one pass.
-__device__ int2 plan_scan2(int2 x, int2* tot) {
+// floor(a / b) for 0 <= a < 2^53 and 0 < b < 2^53: the correctly rounded
+// double quotient is within one of it, and one integer check on either
+// side makes it exact (cheaper than a 64-bit integer division).
+__device__ __forceinline__ long long floor_div(long long a, long long b) {
+  long long q = (long long)((double)a / (double)b);
+  if (q * b > a) --q;
+  else if ((q + 1) * b <= a) ++q;
+  return q;
+}
+
+// Inclusive scan of one int over the wave's 64 lanes with DPP moves: sums
+// (or maxima of non-negative values) within rows of 16 lanes by shifts of
+// 1, 2, 4, 8, then row 0's total into row 1 and row 2's into row 3
+// (row_bcast:15), then row 1's into rows 2 and 3 (row_bcast:31). Lanes
+// shifted in from outside a row, and rows a broadcast skips, add 0.
+template <bool MAX>
+__device__ __forceinline__ int wave_scan(int x) {
+  const auto op = [](int a, int b) { return MAX ? max(a, b) : a + b; };
+  x = op(x, __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false));  // row_shr:1
+  x = op(x, __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false));  // row_shr:2
+  x = op(x, __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false));  // row_shr:4
+  x = op(x, __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false));  // row_shr:8
+  x = op(x, __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  x = op(x, __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return x;
+}
+
+// Inclusive sums of three ints per thread over the workgroup, in one pass:
+// wave scans, the waves' totals through LDS.
+__device__ int3 plan_scan3(int3 x, int3* tot) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int a = __shfl_up(x.x, d), b = __shfl_up(x.y, d);
-    if (lane >= d) {
-      x.x += a;
-      x.y += b;
-    }
-  }
+  x.x = wave_scan<false>(x.x);
+  x.y = wave_scan<false>(x.y);
+  x.z = wave_scan<false>(x.z);
   if (lane == 63) tot[wave] = x;
   __syncthreads();
   if (wave == 0) {
-    int2 v = lane < kPlanWaves ? tot[lane] : int2{0, 0};
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int a = __shfl_up(v.x, d), b = __shfl_up(v.y, d);
-      if (lane >= d) {
-        v.x += a;
-        v.y += b;
-      }
-    }
+    int3 v = lane < kPlanWaves ? tot[lane] : int3{0, 0, 0};
+    v.x = wave_scan<false>(v.x);
+    v.y = wave_scan<false>(v.y);
+    v.z = wave_scan<false>(v.z);
     if (lane < kPlanWaves) tot[lane] = v;
   }
   __syncthreads();
   if (wave > 0) {
     x.x += tot[wave - 1].x;
     x.y += tot[wave - 1].y;
+    x.z += tot[wave - 1].z;
   }
   __syncthreads();
   return x;
 }
 
-// Inclusive scan (sum, or max with `use_max`) of one int per thread over the
-// workgroup: lane shuffles within a wave, the waves' totals through LDS.
-__device__ int plan_scan(int x, int* tot, bool use_max) {
+// Inclusive maximum of one non-negative int per thread over the workgroup.
+__device__ int plan_scan_max(int x, int* tot) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d);
-    if (lane >= d) x = use_max ? max(x, y) : x + y;
-  }
+  x = wave_scan<true>(x);
   if (lane == 63) tot[wave] = x;
   __syncthreads();
   if (wave == 0) {
-    int v = lane < kPlanWaves ? tot[lane] : (use_max ? INT_MIN : 0);
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int y = __shfl_up(v, d);
-      if (lane >= d) v = use_max ? max(v, y) : v + y;
-    }
+    int v = lane < kPlanWaves ? tot[lane] : 0;
+    v = wave_scan<true>(v);
     if (lane < kPlanWaves) tot[lane] = v;
   }
   __syncthreads();
-  if (wave > 0) x = use_max ? max(x, tot[wave - 1]) : x + tot[wave - 1];
+  if (wave > 0) x = max(x, tot[wave - 1]);
   __syncthreads();
   return x;
 }
@@ -1435,10 +1456,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p, int 
   __shared__ int s_cb[kSharedMaxSeqs];      // per leader: least common prefix (blocks) of its members
   __shared__ int s_ml[kSharedMaxSeqs];      // per leader: least last-token position of its group
   __shared__ int s_gn[kSharedMaxSeqs];      // per leader: sequences in its group
-  __shared__ int s_item[2 * kSharedMaxSeqs];  // first chunk of every item
+  __shared__ int s_item[2 * kSharedMaxSeqs + 1];  // first chunk of every item, then the total
+  __shared__ int s_cost[2 * kSharedMaxSeqs + 1];  // cost before every item, then the total
+  __shared__ int s_first[kSharedMaxWorkersTotal];  // every worker's first item
+  __shared__ int s_bound[kSharedMaxWorkersTotal + 1];  // worker w's chunks: [s_bound[w], s_bound[w + 1])
   __shared__ int s_rec[2 * kSharedMaxSeqs][kItemInts];
   __shared__ int s_tot[kPlanWaves];
-  __shared__ int2 s_tot2[kPlanWaves];
+  __shared__ int3 s_tot3[kPlanWaves];
   __shared__ int s_misc[4];
   const int S = p.num_seqs, t = threadIdx.x;
   const int B = p.block_size, F = p.fam_max;
@@ -1452,7 +1476,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p, int 
   const int L = has ? max(capped_len(p, L_raw), 0) : 0;
   // families: runs of linked sequences cut into groups of F from the run's start
   const bool link = has && s > 0 && cpre * B >= kSharedMinChunks * kChunk;
-  const int run = plan_scan(has && !link ? s : 0, s_tot, true);
+  const int run = plan_scan_max(has && !link ? s : 0, s_tot);
   const int leader = run + F * ((s - run) / F);
   if (has && leader == s) {
     s_cb[s] = INT_MAX;
@@ -1485,20 +1509,28 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p, int 
   const int my_sf = has ? s_fam[leader] : 0;
   const bool fam_leader = has && leader == s && members > 1;
   // items of this sequence (a family leader: the common prefix, then its
-  // rest), their index, the family index, their chunks
+  // rest), their index, the family index, their chunks and costs
   const int nitems = has ? (fam_leader ? 2 : 1) : 0;
   const int pre_chunks = fam_leader ? my_sf / kChunk : 0;
   const int own_chunks = num_chunks(L - my_sf);
   const int chunks = pre_chunks + own_chunks;
+  const int per = 16 / p.group;  // members a column group holds
+  const int fam_rate = kCostChunk + kCostGroupChunk * ((members + per - 1) / per);
+  const int fam_cost = fam_leader ? pre_chunks * fam_rate + kCostMemberEnd * members + kCostItemEnd : 0;
+  const int own_cost = own_chunks > 0 ? own_chunks * kCostChunk + kCostItemEnd : 0;
   // one pass: items (< 2^15) in the low half and families in the high half
-  // of the first sum, chunks in the second
-  const int2 sums = plan_scan2(int2{nitems | ((fam_leader ? 1 : 0) << 16), chunks}, s_tot2);
+  // of the first sum, chunks in the second, costs in the third
+  const int3 sums = plan_scan3(int3{nitems | ((fam_leader ? 1 : 0) << 16), chunks, fam_cost + own_cost}, s_tot3);
   const int item0 = (sums.x & 0xffff) - nitems;
   const int fam = (sums.x >> 16) - 1;
   const int c0 = sums.y - chunks;
+  const int k0 = sums.z - fam_cost - own_cost;
   if (t == kPlanThreads - 1) {
     s_misc[1] = item0 + nitems;  // items
     s_misc[2] = c0 + chunks;     // chunks per KV head
+    s_misc[3] = sums.z;          // total cost
+    s_item[item0 + nitems] = c0 + chunks;
+    s_cost[item0 + nitems] = sums.z;
   }
   if (fam_leader) {
     s_rec[item0][0] = s | (members << 16);
@@ -1506,6 +1538,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p, int 
     s_rec[item0][2] = my_sf;
     s_rec[item0][3] = c0;
     s_item[item0] = c0;
+    s_cost[item0] = k0;
   }
   if (has) {
     const int it = item0 + nitems - 1;
@@ -1514,29 +1547,75 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p, int 
     s_rec[it][2] = L;
     s_rec[it][3] = c0 + pre_chunks;
     s_item[it] = c0 + pre_chunks;
+    s_cost[it] = k0 + fam_cost;
   }
   __syncthreads();
-  const int NI = s_misc[1], T = s_misc[2];
-  for (int i = t; i < NI * kItemInts; i += kPlanThreads) p.items[i] = s_rec[i / kItemInts][i % kItemInts];
+  const int NI = s_misc[1], T = s_misc[2], C = s_misc[3];
   const int Wn = min(W, T);
+  // worker boundaries: boundary b (0 < b < Wn) at the chunk x where the cost
+  // reaches X = floor(b C / Wn), found by the item whose cost range
+  // [s_cost[i], s_cost[i + 1]) holds X; then pulled towards the even split
+  // so that every worker keeps at least one chunk: s_bound[b] =
+  // x (T - Wn) / T + b is strictly increasing in b, with s_bound[0] = 0 and
+  // s_bound[Wn] = T
+  if (T > 0) {
+    for (int i = t; i < NI; i += kPlanThreads) {
+      const long long k = s_cost[i], k1 = s_cost[i + 1];
+      if (k1 == k) continue;
+      const int m = s_rec[i][0] >> 16;
+      const int rate = m > 1 ? kCostChunk + kCostGroupChunk * ((m + per - 1) / per) : kCostChunk;
+      const long long n = s_item[i + 1] - s_item[i];
+      // X >= k  <=>  b C >= k Wn;  X < k1  <=>  b C < k1 Wn
+      const int b0 = (int)floor_div(k * Wn + C - 1, C), b1 = (int)floor_div(k1 * Wn + C - 1, C);
+      for (int b = max(b0, 1); b < min(b1, Wn); ++b) {
+        const int off = (int)(floor_div((long long)b * C, Wn) - k) / rate;
+        const long long x = s_item[i] + (off < n ? off : n);
+        s_bound[b] = (int)floor_div(x * (T - Wn), T) + b;
+      }
+    }
+    if (t == 0) {
+      s_bound[0] = 0;
+      s_bound[Wn] = T;
+    }
+  }
+  __syncthreads();
+  // every worker's range and first item; each item's first and last owner
+  // marked by the workers holding its first and its last chunk
+  for (int w = t; w < Wn; w += kPlanThreads) {
+    const int start = s_bound[w], end = s_bound[w + 1];
+    // the last item whose first chunk is at or before `start` (items
+    // without chunks share their successor's first chunk)
+    int lo = 0, hi = NI;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_item[mid] <= start) lo = mid;
+      else hi = mid;
+    }
+    s_first[w] = lo;
+    for (int i = lo; i < NI && s_item[i] < end; ++i) {
+      const int c = s_item[i], c1 = s_item[i + 1];
+      if (c1 == c) continue;
+      if (c >= start) s_rec[i][4] = w;
+      if (c1 <= end) s_rec[i][5] = w;  // last chunk c1 - 1 in [start, end)
+    }
+  }
+  __syncthreads();
+  for (int i = t; i < NI; i += kPlanThreads) {
+    const bool some = s_item[i + 1] > s_item[i];
+    const int o0 = some ? s_rec[i][4] : 0;
+    s_rec[i][4] = o0;
+    s_rec[i][5] = some ? s_rec[i][5] - o0 + 1 : 0;
+    s_rec[i][6] = 0;
+    s_rec[i][7] = 0;
+  }
+  __syncthreads();
+  for (int i = t; i < NI * kItemInts; i += kPlanThreads) p.items[i] = s_rec[i / kItemInts][i % kItemInts];
   for (int w = t; w < W; w += kPlanThreads) {
     int32_t* r = p.wrec + (size_t)w * kWorkerInts;
-    int start = 0, end = 0, first = 0;
-    if (w < Wn) {
-      start = (int)((long long)w * T / Wn);
-      end = (int)((long long)(w + 1) * T / Wn);
-      // the last item whose first chunk is at or before `start` (items
-      // without chunks share their successor's first chunk)
-      int lo = 0, hi = NI;
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (s_item[mid] <= start) lo = mid;
-        else hi = mid;
-      }
-      first = lo;
-    }
-    r[0] = start;
-    r[1] = end;
+    const bool live = w < Wn;
+    const int first = live ? s_first[w] : 0;
+    r[0] = live ? s_bound[w] : 0;
+    r[1] = live ? s_bound[w + 1] : 0;
     r[2] = first;
     r[3] = T;
     r[4] = NI;

@@ -130,8 +130,8 @@ def test_decode_workspace_sizes_shared_mode(lib):
     fam_max = 2 * (16 // (Hq // Hkv))                      # members per family
     slots = workers + 2 * S + (workers + S // 2 + 1) * fam_max
     need = (S * 4 * 4                                      # split records, four ints
-            + S * 2 * 4 * 4                                # work items
-            + workers * 12 * 4                             # worker records
+            + S * 2 * 8 * 4                                # work items, eight ints
+            + workers * 16 * 4                             # worker records, sixteen ints
             + S * 4                                        # prefix links
             + slots * Hq * 2 * 4 + slots * Hq * d * 4)     # (m, l) and partial outputs
     assert f(S, Hq, Hkv, d, L, -2) == need

@@ -227,6 +227,46 @@ def shared_plan(lengths, tables, B, F, W):
     return items, chunk, fam_sf
 
 
+# the plan's cost estimate, in sixteenths of a one-group chunk
+COST_CHUNK, COST_GROUP_CHUNK, COST_MEMBER_END, COST_ITEM_END = 16, 1, 3, 4
+
+
+def item_chunks(it):
+    seq, members, f_or_t0, t1, c = it
+    t0 = 0 if members > 1 else f_or_t0
+    return -(-(t1 - t0) // CHUNK) if t1 > t0 else 0
+
+
+def shared_bounds(items, T, W, group):
+    """Worker boundaries of the plan: boundary b where the estimated cost
+    reaches b C / W', pulled towards the even split so that every worker
+    keeps a chunk."""
+    per = 16 // group
+    cost, start_cost = 0, []
+    rates = []
+    for it in items:
+        n, m = item_chunks(it), it[1]
+        rate = COST_CHUNK + COST_GROUP_CHUNK * (-(-m // per)) if m > 1 else COST_CHUNK
+        start_cost.append(cost)
+        rates.append(rate)
+        if m > 1:
+            cost += n * rate + COST_MEMBER_END * m + COST_ITEM_END
+        elif n > 0:
+            cost += n * rate + COST_ITEM_END
+    C, Wn = cost, min(W, T)
+    starts = [it[4] for it in items] + [T]
+    bounds = []
+    for b in range(Wn + 1):
+        x = T
+        if b < Wn:
+            X = b * C // Wn
+            lo = max(i for i in range(len(items)) if start_cost[i] <= X)
+            n = starts[lo + 1] - starts[lo]
+            x = starts[lo] + min(n, (X - start_cost[lo]) // rates[lo])
+        bounds.append(x * (T - Wn) // T + b)
+    return bounds
+
+
 def shared_walk(lengths, tables, B, group, W):
     S = len(lengths)
     F = family_max(group)
@@ -237,11 +277,13 @@ def shared_walk(lengths, tables, B, group, W):
     if T == 0:
         return pieces, meta, fam_sf, F, 0
     Wn = min(W, T)
-    owner = lambda c: ((c + 1) * Wn - 1) // T  # noqa: E731
+    bounds = shared_bounds(items, T, W, group)
+    assert bounds[0] == 0 and bounds[-1] == T and all(b > a for a, b in zip(bounds, bounds[1:]))
+    owner = lambda c: int(np.searchsorted(bounds, c, side="right") - 1)  # noqa: E731
     wmax = -(-2048 // 8)  # workspace bound used with 8 KV heads below
     fam_base = wmax + 2 * S
     for w in range(Wn):
-        start, end = w * T // Wn, (w + 1) * T // Wn
+        start, end = bounds[w], bounds[w + 1]
         i = int(np.searchsorted(starts, start, side="right") - 1)
         while i < len(items) and items[i][4] < end:
             seq, members, f_or_t0, t1, c = items[i]
@@ -350,3 +392,32 @@ def test_shared_plan_families_of_the_sampling_workload():
     fams = [it for it in items if it[1] > 1]
     assert len(fams) == 32 and all(it[1] == 8 and it[3] == 992 for it in fams)
     assert T == 32 * 31 + sum(-(-(L - 992) // CHUNK) for L in lengths)
+
+
+def test_shared_bounds_weigh_families():
+    # the sampling step's shape (32 prompts of 1016 tokens, 8 forks each
+    # 256 tokens further on, B = 16, g = 4): families over 992 tokens, own
+    # tails of 9 chunks. A worker on a family prefix gets fewer chunks than
+    # one on the forks' own tails, every worker at least one.
+    B, lengths, tables, nxt = 16, [], [], 0
+    for _ in range(32):
+        prompt = list(range(nxt, nxt + 63))
+        nxt += 63
+        for _ in range(8):
+            L = 1016 + 256
+            rest = -(-L // B) - 63
+            tables.append(prompt + list(range(nxt, nxt + rest)))
+            nxt += rest
+            lengths.append(L)
+    items, T, fam_sf = shared_plan(lengths, tables, B, family_max(4), 128)
+    assert T == 32 * 31 + 256 * 9 and set(fam_sf.values()) == {992}
+    bounds = shared_bounds(items, T, 128, 4)
+    fam_chunks = set()
+    for it in items:
+        if it[1] > 1:
+            fam_chunks.update(range(it[4], it[4] + item_chunks(it)))
+    sizes = np.diff(bounds)
+    on_fam = [w for w in range(128) if all(c in fam_chunks for c in range(bounds[w], bounds[w + 1]))]
+    on_own = [w for w in range(128) if not any(c in fam_chunks for c in range(bounds[w], bounds[w + 1]))]
+    assert on_fam and on_own and sizes.min() >= 1
+    assert max(sizes[on_fam]) < min(sizes[on_own])
