@@ -40,8 +40,8 @@ constexpr int kWorkerInts = 16;           // ints per worker record: range, firs
 // 0.4 us, the end of an item and the start of the next about 0.6 us). The
 // plan splits the total cost evenly over the workers.
 constexpr int kCostChunk = 16;        // a chunk, one column group
-constexpr int kCostGroupChunk = 1;    // more per chunk and column group of a family's prefix
-constexpr int kCostMemberEnd = 3;     // a finished family prefix, per member
+constexpr int kCostGroupChunk = 0;    // more per chunk and column group of a family's prefix
+constexpr int kCostMemberEnd = 8;     // a finished family prefix, per member
 constexpr int kCostItemEnd = 4;       // a finished item
 // Most members of a family: column groups times the members one 16-column
 // group holds (a member takes g columns, one per query head).

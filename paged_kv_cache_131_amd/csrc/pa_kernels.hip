@@ -1420,20 +1420,31 @@ __global__ __launch_bounds__(64 * kLinkWaves) void link_kernel(DecodeParams p) {
   int c = 0;
   if (s > 0) {
     const int lg = p.log2_block, B = p.block_size, mb = p.max_blocks_per_seq;
+    const int32_t* a = p.block_tables + (size_t)s * mb;
+    const int32_t* b = a - mb;
+    // the first round's entries are requested with the lengths (clamped to
+    // the rows' last entry: in bounds whatever the lengths), so the compare
+    // waits for one round trip, not two
+    int va[kLinkSpan], vb[kLinkSpan];
+#pragma unroll
+    for (int h = 0; h < kLinkSpan; ++h) {
+      const int k = min(64 * h + lane, mb - 1);
+      va[h] = a[k];
+      vb[h] = b[k];
+    }
     const int la = max(capped_len(p, p.context_lens[s]), 0);
     const int lb = max(capped_len(p, p.context_lens[s - 1]), 0);
     // both lengths are within their tables, so entries below n exist in both rows
     const int n = min((la + B - 1) >> lg, (lb + B - 1) >> lg);
-    const int32_t* a = p.block_tables + (size_t)s * mb;
-    const int32_t* b = a - mb;
     c = n;
     for (int k0 = 0; k0 < n; k0 += 64 * kLinkSpan) {
-      int va[kLinkSpan], vb[kLinkSpan];
+      if (k0 > 0) {
 #pragma unroll
-      for (int h = 0; h < kLinkSpan; ++h) {
-        const int k = min(k0 + 64 * h + lane, n - 1);
-        va[h] = a[k];
-        vb[h] = b[k];
+        for (int h = 0; h < kLinkSpan; ++h) {
+          const int k = min(k0 + 64 * h + lane, n - 1);
+          va[h] = a[k];
+          vb[h] = b[k];
+        }
       }
       int found = -1;
 #pragma unroll
@@ -1571,11 +1582,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p, int 
         const int off = (int)(floor_div((long long)b * C, Wn) - k) / rate;
         const long long x = s_item[i] + (off < n ? off : n);
         s_bound[b] = (int)floor_div(x * (T - Wn), T) + b;
+        s_first[b] = i;  // the item x lies in: the start of the search for b's first item
       }
     }
     if (t == 0) {
       s_bound[0] = 0;
       s_bound[Wn] = T;
+      s_first[0] = 0;
     }
   }
   __syncthreads();
@@ -1584,12 +1597,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p, int 
   for (int w = t; w < Wn; w += kPlanThreads) {
     const int start = s_bound[w], end = s_bound[w + 1];
     // the last item whose first chunk is at or before `start` (items
-    // without chunks share their successor's first chunk)
-    int lo = 0, hi = NI;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_item[mid] <= start) lo = mid;
-      else hi = mid;
+    // without chunks share their successor's first chunk), walked to from
+    // the item the boundary's cost target fell in (the pull towards the
+    // even split moves it by a few chunks)
+    int lo = s_first[w], steps = 0;
+    while (steps < 8 && lo > 0 && s_item[lo] > start) --lo, ++steps;
+    while (steps < 8 && lo + 1 < NI && s_item[lo + 1] <= start) ++lo, ++steps;
+    if (steps == 8) {  // far off (runs of items without chunks): binary search
+      lo = 0;
+      int hi = NI;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_item[mid] <= start) lo = mid;
+        else hi = mid;
+      }
     }
     s_first[w] = lo;
     for (int i = lo; i < NI && s_item[i] < end; ++i) {
@@ -2102,8 +2123,8 @@ hipError_t launch_plan(const DecodeParams& p, unsigned workers, hipStream_t stre
   int W = (int)workers;
   void* largs[] = {&args};
   const unsigned groups = (unsigned)((p.num_seqs + kLinkWaves - 1) / kLinkWaves);
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&link_kernel), dim3(groups), dim3(64 * kLinkWaves),
-                                 largs, 0, stream);
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&link_kernel), dim3(groups),
+                                       dim3(64 * kLinkWaves), largs, 0, stream);
   if (e != hipSuccess) return e;
   void* kargs[] = {&args, &W};
   return hipLaunchKernel(reinterpret_cast<const void*>(&plan_kernel), dim3(1), dim3(kPlanThreads), kargs, 0, stream);

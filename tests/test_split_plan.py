@@ -228,7 +228,7 @@ def shared_plan(lengths, tables, B, F, W):
 
 
 # the plan's cost estimate, in sixteenths of a one-group chunk
-COST_CHUNK, COST_GROUP_CHUNK, COST_MEMBER_END, COST_ITEM_END = 16, 1, 3, 4
+COST_CHUNK, COST_GROUP_CHUNK, COST_MEMBER_END, COST_ITEM_END = 16, 0, 8, 4
 
 
 def item_chunks(it):
