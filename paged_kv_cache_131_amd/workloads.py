@@ -124,7 +124,7 @@ class DecodeConfig:
     lengths: tuple             # ("fixed", values) | ("uniform", lo, hi) | ("lognormal", median, sigma, lo, hi)
     max_len: int               # upper bound of the length law: sizes block tables
     pool_blocks: int = 0       # 0 = ceil(1.1 * blocks needed)
-    partition_size: int = -1   # -1 = balanced split chosen by the library
+    partition_size: int = -1   # -1 = balanced split; -2 = shared split (forks read their common blocks once)
 
     @property
     def group(self) -> int:
@@ -267,7 +267,7 @@ def make_decode_workload(cfg: DecodeConfig, lengths=None, poison: bool = True,
 # --------------------------------------------------------------------------
 
 PARALLEL_SAMPLING = DecodeConfig("parallel_sampling", 4, 256, 32, 8, 128, 16, "bf16", 1.0,
-                                 ("fixed", ()), 1024 + 256)
+                                 ("fixed", ()), 1024 + 256, partition_size=-2)
 
 
 @dataclass
@@ -380,7 +380,8 @@ class ParallelSamplingWorkload:
         return self.num_blocks - self.bm.num_free
 
 
-BEAM_SEARCH = DecodeConfig("beam_search", 5, 128, 32, 8, 128, 16, "bf16", 1.0, ("fixed", ()), 1000 + 64)
+BEAM_SEARCH = DecodeConfig("beam_search", 5, 128, 32, 8, 128, 16, "bf16", 1.0, ("fixed", ()), 1000 + 64,
+                           partition_size=-2)
 
 
 class BeamSearchWorkload:
@@ -484,7 +485,7 @@ class BeamSearchWorkload:
 
 
 SHARED_PREFIX = DecodeConfig("shared_prefix", 6, 256, 32, 8, 128, 16, "bf16", 1.0, ("uniform", 16, 512),
-                             1024 + 512)
+                             1024 + 512, partition_size=-2)
 
 
 def make_shared_prefix_workload(prefix_len: int = 1024, cfg: DecodeConfig = SHARED_PREFIX, poison: bool = True,
