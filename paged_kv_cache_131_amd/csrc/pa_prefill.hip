@@ -397,16 +397,16 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(PrefillPara
     T.m_run[gi] = kNegInf;
     T.l_run[gi] = 0.f;
   }
-  // the q loads complete here, so the ring's waits count ring loads only; the
-  // builtin form tells the compiler they are done
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-
+  // chunk 0's ring loads fly together with the q loads; both complete here,
+  // so the ring's later waits count ring loads only (the builtin form tells
+  // the compiler that q is done)
   const int nch = T.nch;
   {
     const ChunkIds ids0 = load_chunk_ids(T.tbl, 0, T.lbl, p.log2_block);
     T.template issue<0>(0, ids0);
   }
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   ChunkIds ids_next = load_chunk_ids(T.tbl, min(2, nch - 1) * kChunk, T.lbl, p.log2_block);
   if (nch > 1) {
     const ChunkIds ids1 = load_chunk_ids(T.tbl, kChunk, T.lbl, p.log2_block);
@@ -418,20 +418,62 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(PrefillPara
     if (!T.template step<2>(ci + 2, ids_next)) break;
   }
 
-  // rows of this lane: columns r = 4*grp + i, i.e. query r / g, head r % g
+  // Rows of this lane: columns r = 4*grp + i, i.e. query r / g, head r % g;
+  // a row is normalised with one reciprocal. A query's g heads are g*D
+  // contiguous outputs, so each wave stages its rows, group by group, in its
+  // own half of a ring stage (free once every wave is past the last chunk's
+  // reads) and stores them 16 bytes per lane; element dd of row r sits at
+  // r*D + (dd ^ ((r & 3) << 4)), which spreads the four rows one write
+  // instruction touches over the banks. An output not 16-byte aligned takes
+  // the per-element stores.
+  __syncthreads();
+  const bool vec_out = (reinterpret_cast<uintptr_t>(p.out) & 15) == 0;
+  const int es = p.out_dtype == kF32 ? 4 : 2;
+  char* stg = reinterpret_cast<char*>(wave < 2 ? stage_buf<0, D>() : stage_buf<1, D>()) + (wave & 1) * (16 * D * 4);
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {
     const float l_tot = sum_over_column(T.l_run[gi]);
+    float inv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * grp + i;
-      const float lr = __shfl(l_tot, r);
-      const int qr = r / g;
-      const int jq = gi * qt + qr;
-      if (qr < qt && jq < nq_w) {
-        const size_t base = ((size_t)(q0 + j0 + wave * qw + jq) * Hq + T.kvh * g + (r - qr * g)) * D + col;
+    for (int i = 0; i < 4; ++i) inv[i] = 1.f / __shfl(l_tot, 4 * grp + i);
+    if (vec_out) {
 #pragma unroll
-        for (int j = 0; j < NT; ++j) store_out(p.out, base + 16 * j, T.o[gi][j][i] / lr, p.out_dtype);
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * grp + i;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          const int e = r * D + ((16 * j + col) ^ ((r & 3) << 4));
+          const float v = T.o[gi][j][i] * inv[i];
+          if (es == 4) reinterpret_cast<float*>(stg)[e] = v;
+          else
+            reinterpret_cast<uint16_t*>(stg)[e] =
+                p.out_dtype == kF16 ? __builtin_bit_cast(uint16_t, static_cast<_Float16>(v))
+                                    : __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
+        }
+      }
+      // this wave's own writes, then its reads, in order
+      const int upr = D * es / 16;  // 16-byte units per row
+      for (int u = lane; u < qt * g * upr; u += 64) {
+        const int r = u / upr, c = u - r * upr;
+        const int qr = r / g, jq = gi * qt + qr;
+        if (jq < nq_w) {
+          const int e0 = (c * 16 / es) ^ ((r & 3) << 4);  // the unit's first element, as staged
+          const u32x4 val = *reinterpret_cast<const u32x4*>(stg + (size_t)(r * D + e0) * es);
+          const size_t base = ((size_t)(q0 + j0 + wave * qw + jq) * Hq + T.kvh * g + (r - qr * g)) * D;
+          *reinterpret_cast<u32x4*>(static_cast<char*>(p.out) + (base + (size_t)c * 16 / es) * es) = val;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * grp + i;
+        const int qr = r / g;
+        const int jq = gi * qt + qr;
+        if (qr < qt && jq < nq_w) {
+          const size_t base = ((size_t)(q0 + j0 + wave * qw + jq) * Hq + T.kvh * g + (r - qr * g)) * D + col;
+#pragma unroll
+          for (int j = 0; j < NT; ++j) store_out(p.out, base + 16 * j, T.o[gi][j][i] * inv[i], p.out_dtype);
+        }
       }
     }
   }
