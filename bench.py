@@ -169,8 +169,9 @@ def cpu_baseline(w, budget_s: float) -> dict:
 
 
 def traffic_for(kernel: str, workload: str):
-    """HBM bytes per step of the timed launches from the committed counter
-    summary, if it was taken on the current kernel sources."""
+    """HBM bytes per step of the timed launches ("a+b+...": the sum over
+    those kernels) from the committed counter summary, if it was taken on the
+    current kernel sources and holds every one of them."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
@@ -179,11 +180,26 @@ def traffic_for(kernel: str, workload: str):
     entry = rec.get(workload, {})
     if entry.get("kernel_hash") != kernel_hash(workload):
         return None
-    return entry.get(kernel)
+    per = entry.get("kernels", {})
+    names = kernel.split("+")
+    if not all(k in per for k in names):
+        return None
+    return sum(per[k]["traffic_bytes"] for k in names)
 
 
-FUSED_KERNELS = ("decode_kernel", "merge_kernel")
-TWO_CALL_KERNELS = ("write_kv_kernel", "decode_kernel", "merge_kernel")
+# Kernels of the decode step's launches, in launch order: the planning
+# launches of the shared split, the decode kernel, the closing merge launch.
+DECODE_KERNELS = ("write_kv_kernel", "link_kernel", "plan_kernel", "decode_kernel", "merge_kernel")
+
+
+def step_kernels(launches: int, fused: bool) -> str:
+    """The timed step's kernels from the number of launches the decode call
+    makes (pa_decode_launches): 1 decode only, 2 with the closing merge, 4
+    with the shared split's two planning launches before them."""
+    names = {1: ["decode_kernel"], 2: ["decode_kernel", "merge_kernel"],
+             3: ["link_kernel", "plan_kernel", "decode_kernel"],
+             4: ["link_kernel", "plan_kernel", "decode_kernel", "merge_kernel"]}[launches]
+    return "+".join(names if fused else ["write_kv_kernel"] + names)
 
 
 def summarize_counters(fetch_csv: str, write_csv: str, workload: str, calibration_mib: int) -> dict:
@@ -202,8 +218,8 @@ def summarize_counters(fetch_csv: str, write_csv: str, workload: str, calibratio
                 if name.startswith("__amd_rocclr_copyBuffer"):
                     calib = max(calib, v)
                     continue
-                for k in TWO_CALL_KERNELS + ("prefill_kernel",):
-                    if f"::{k}<" in name:
+                for k in DECODE_KERNELS + ("prefill_kernel",):
+                    if f"::{k}<" in name or f"::{k}(" in name:
                         vals[k].append(v)
         return {k: float(np.mean(v)) for k, v in vals.items()}, calib
 
@@ -218,11 +234,6 @@ def summarize_counters(fetch_csv: str, write_csv: str, workload: str, calibratio
              "calibration": f"one {calibration_mib} MiB device-to-device torch copy (__amd_rocclr_copyBuffer) in "
                             f"the same run: FETCH_SIZE {fcal:.1f} KiB, WRITE_SIZE {wcal:.1f} KiB",
              "kernels": kernels}
-    for key, ks in (("+".join(FUSED_KERNELS), FUSED_KERNELS), ("+".join(TWO_CALL_KERNELS), TWO_CALL_KERNELS)):
-        if all(k in kernels for k in ks):
-            entry[key] = sum(kernels[k]["traffic_bytes"] for k in ks)
-    if "prefill_kernel" in kernels:
-        entry["prefill_kernel"] = kernels["prefill_kernel"]["traffic_bytes"]
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
@@ -708,11 +719,15 @@ def main() -> int:
     step_bytes = db["total"] + wb
     ms_per_step = elapsed * 1e3 / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    # per step on the GPU: the fused call's launches (decode_kernel, then
-    # merge_kernel: merges split sequences and stores the new tokens)
+    # per step on the GPU: the call's launches (the decode kernel; the
+    # shared split's planning launches before it; the closing launch that
+    # merges split sequences and stores the new tokens, unless the decode
+    # kernel does both itself)
     launch_bytes = step_bytes if fused else db["total"] + wb
     achieved = launch_bytes / (call_ms * 1e-3) / 1e9
-    kernel = "decode_kernel+merge_kernel" if fused else "write_kv_kernel+decode_kernel+merge_kernel"
+    launches = pb.pa_decode_launches(len(c.context_lens), cfg.num_heads, cfg.num_kv_heads, cfg.head_dim, max_len,
+                                     part, q.dtype, args.algo, fused)
+    kernel = step_kernels(launches, fused)
     traffic = traffic_for(kernel, args.workload)
     result = {
         "metric": "paged decode attention: achieved HBM GB/s (% of peak) + sequences/s at 1 GPU",

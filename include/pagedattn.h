@@ -87,6 +87,10 @@ typedef enum pa_algo { PA_ALGO_AUTO = 0, PA_ALGO_VECTOR = 1, PA_ALGO_MFMA = 2 } 
 #define PA_PARTITION_NONE 0
 #define PA_PARTITION_SHARED (-2)
 
+/* Bytes at the start of every decode workspace that hold its arrival
+ * counters (zero between calls; see pa_decode). */
+#define PA_WORKSPACE_COUNTER_BYTES ((size_t)32768)
+
 /*
  * pa_write_kv -- store new K/V rows into their slots ("fused reshape and
  * block write", [review-kr] §3-2(5); new KV goes into its physical block,
@@ -134,10 +138,18 @@ pa_status pa_write_kv(const void* k_new, const void* v_new, void* k_cache, void*
  *                  exponentials ([review-en] "How does this work?": compute
  *                  per block, then combine the partial results).
  *   workspace    : device scratch of at least pa_decode_workspace_bytes(...)
- *                  bytes (may be NULL when that is 0); no initial contents
- *                  are required. Split sequences leave their partial results
- *                  there and a second kernel on `stream` combines them, so
- *                  calls that overlap in time must not share a workspace.
+ *                  bytes (may be NULL when that is 0). Its first
+ *                  PA_WORKSPACE_COUNTER_BYTES hold arrival counters: they
+ *                  must be zero before the workspace's first use (e.g. a
+ *                  zero fill of the new allocation), and every call leaves
+ *                  them zero; the rest needs no initial contents. Split
+ *                  sequences leave their partial results there. Under
+ *                  PA_PARTITION_AUTO (and calls that run as AUTO) the decode
+ *                  kernel combines them itself: the worker whose piece is
+ *                  counted last merges the sequence (the counters decide who
+ *                  merges, never the arithmetic). Otherwise a second kernel
+ *                  on `stream` combines them. Calls that overlap in time
+ *                  must not share a workspace.
  *   Requirements: head_dim in {64, 128}; block_size in {8, 16, 32, 64, 128};
  *   num_heads % num_kv_heads == 0 and num_heads/num_kv_heads <= 8;
  *   PA_ALGO_MFMA needs dtype F16 or BF16.
@@ -163,9 +175,11 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
  * pa_decode_workspace_bytes exceeds that size return PA_ERR_WORKSPACE before
  * touching the device (e.g. 512-token partitions of 16 sequences of 128K
  * tokens with 64 query heads need 136 MB; their balanced split needs 35 MB).
- * The array needs no initial contents. Every call on one device shares it,
- * so calls that may overlap in time on one device (several streams, several
- * host threads) race: serialise them. No memory is allocated by this call.
+ * The array is zero when the library is loaded (its counter region, as a
+ * workspace's, is left zero by every call). Every call on one device shares
+ * it, so calls that may overlap in time on one device (several streams,
+ * several host threads) race: serialise them. No memory is allocated by this
+ * call.
  */
 #define PA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -191,8 +205,10 @@ pa_status pa_decode_ex(void* out, const void* q, const void* k_cache, const void
  * followed by pa_decode with the same arguments: output and cache contents
  * are bit-identical to that pair of calls ([notes-zh] §5.3: the new token's
  * KV goes into the last logical block, then attention reads the blocks).
- * The attention kernel takes position L-1 from k_new/v_new; the launch
- * after it (which also merges split sequences) stores them into the cache.
+ * The attention kernel takes position L-1 from k_new/v_new and never uses
+ * what the slot holds, so the store may overlap it: under
+ * PA_PARTITION_AUTO the decode kernel stores the new tokens itself, in the
+ * other modes the launch after it (which also merges split sequences) does.
  * The block of position L-1 must not be shared with another sequence of the
  * call (copy-on-write has already made it private, [notes-zh] §6.1). No
  * write is made for a sequence with L <= 0, with L beyond
@@ -242,6 +258,18 @@ pa_status pa_prefill(void* out, const void* q, const int32_t* q_start, int32_t t
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_context_len,
                                  int32_t partition_size);
+
+/* Kernel launches a pa_decode (fused = 0) or pa_write_decode (fused = 1)
+ * call with these sizes makes on its stream, on the current device: the
+ * decode kernel; under PA_PARTITION_SHARED (16-bit, MFMA) two planning
+ * launches before it; and a closing launch after it that merges split
+ * sequences and stores the new tokens, except where the balanced split
+ * (PA_PARTITION_AUTO) merges inside the decode kernel. 0 for num_seqs == 0
+ * or arguments pa_decode would reject. Host function (it reads the
+ * device's compute-unit count, as the call does). */
+int32_t pa_decode_launches(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t max_context_len, int32_t partition_size, pa_dtype dtype, pa_algo algo,
+                           int32_t fused);
 
 /*
  * pa_copy_blocks -- batched whole-block copy for copy-on-write ([notes-zh]

@@ -20,6 +20,7 @@ DTYPE_CODE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_B
 ALGO_CODE = {"auto": 0, "vector": 1, "mfma": 2}
 PA_PARTITION_AUTO = -1
 PA_PARTITION_NONE = 0
+WORKSPACE_COUNTER_BYTES = 32768  # PA_WORKSPACE_COUNTER_BYTES: zero between calls
 STATUS = {0: "PA_OK", -1: "PA_ERR_INVALID_ARG", -2: "PA_ERR_UNSUPPORTED", -3: "PA_ERR_WORKSPACE",
           -4: "PA_ERR_LAUNCH"}
 
@@ -36,6 +37,7 @@ SIGNATURES = {
     "pa_write_decode": (_i32, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                                _i32, _p, _sz, _i32, _i32, _p]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_launches": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_copy_blocks": (_i32, [_p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p]),
     "pa_prefill": (_i32, [_p, _p, _p, _i32, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                           _i32, _p]),
@@ -128,6 +130,15 @@ def pa_decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_c
                                                         max_context_len, partition_size))
 
 
+def pa_decode_launches(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
+                       partition_size=PA_PARTITION_AUTO, dtype=torch.bfloat16, algo="auto", fused=False) -> int:
+    """Kernel launches pa_decode (fused=False) or pa_write_decode (fused=True) makes for these sizes on the
+    current device (0 for no sequences or rejected arguments)."""
+    return int(load_library().pa_decode_launches(num_seqs, num_heads, num_kv_heads, head_dim, int(max_context_len),
+                                                 int(partition_size), DTYPE_CODE[dtype], ALGO_CODE[algo],
+                                                 int(bool(fused))))
+
+
 _workspaces = {}
 
 
@@ -135,15 +146,16 @@ def workspace_for(device, nbytes: int, stream_handle: int) -> torch.Tensor:
     """A workspace of at least nbytes on `device` for calls on the stream
     `stream_handle`, reused by later calls on that stream (they run in order,
     so they never use it at the same time). Calls on different streams get
-    different workspaces. A workspace is allocated on the stream that uses
-    it, so that when a larger one replaces it, the allocator reuses its memory
-    only after the work already queued on that stream."""
+    different workspaces. A workspace is allocated, zero-filled (its arrival
+    counters start at zero), on the stream that uses it, so that when a
+    larger one replaces it, the allocator reuses its memory only after the
+    work already queued on that stream."""
     dev = torch.device(device)
     key = (dev, int(stream_handle))
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
         with torch.cuda.stream(torch.cuda.ExternalStream(int(stream_handle), device=dev)):
-            ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+            ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
         _workspaces[key] = ws
     return ws
 

@@ -14,8 +14,10 @@
 
 namespace {
 
-constexpr int kAbiVersion = 6;
+constexpr int kAbiVersion = 7;
 constexpr size_t kAlign = 256;
+constexpr size_t kCounterBytes = (size_t)pa::kArrivalSlots * sizeof(int32_t);
+static_assert(kCounterBytes == PA_WORKSPACE_COUNTER_BYTES, "counter region of the header");
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 bool valid_dtype(int d) { return d == PA_F32 || d == PA_F16 || d == PA_BF16; }
@@ -84,17 +86,18 @@ Plan make_plan(int num_seqs, int num_kv_heads, int max_context_len, int partitio
 }
 
 struct WorkspaceLayout {
-  size_t meta, items, wrec, links, ml, acc, total;
+  size_t ctr, meta, items, wrec, links, ml, acc, total;
   int fam_base, fam_max;  // shared mode: first family slot, sub-slots per family slot
 };
 
-// Workspace: split records, then (shared mode) the plan's items, worker
-// records and prefix links, then (m, l) and the partial outputs of every
-// slot. Shared mode
-// adds a family region after the ordinary slots: family slot (worker +
-// family index) holds fam_max sub-slots, one per member.
+// Workspace: the arrival counters (the same fixed region in every mode, so
+// that no call's other regions ever overlap them; they hold zeros between
+// calls), split records, then (shared mode) the plan's items, worker records
+// and prefix links, then (m, l) and the partial outputs of every slot.
+// Shared mode adds a family region after the ordinary slots: family slot
+// (worker + family index) holds fam_max sub-slots, one per member.
 WorkspaceLayout layout(const Plan& pl, int num_seqs, int num_heads, int num_kv_heads, int head_dim) {
-  WorkspaceLayout w{0, 0, 0, 0, 0, 0, 0, 0, 0};
+  WorkspaceLayout w{0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
   if (pl.slots == 0) return w;
   const bool shared = pl.mode == pa::kModeShared;
   size_t slots = pl.slots;
@@ -109,9 +112,10 @@ WorkspaceLayout layout(const Plan& pl, int num_seqs, int num_heads, int num_kv_h
   const size_t links = shared ? round_up((size_t)num_seqs * sizeof(int32_t)) : 0;
   const size_t ml = round_up(slots * (size_t)num_heads * 2 * sizeof(float));
   const size_t acc = round_up(slots * (size_t)num_heads * head_dim * sizeof(float));
-  w.meta = 0;
-  w.items = meta;
-  w.wrec = meta + items;
+  w.ctr = 0;
+  w.meta = kCounterBytes;
+  w.items = w.meta + meta;
+  w.wrec = w.items + items;
   w.links = w.wrec + wrec;
   w.ml = w.links + links;
   w.acc = w.ml + ml;
@@ -349,6 +353,67 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapp
 
 }  // extern "C"
 
+// What a decode call with these sizes runs: kernel family and group bucket,
+// split plan, workspace layout, workers per KV head (the grid's x), and
+// whether the balanced split merges inside the decode kernel. Shared by the
+// call and pa_decode_launches.
+struct DecodeChoice {
+  int kernel_algo, G, elem;
+  Plan pl;
+  WorkspaceLayout wl;
+  long long workers;
+  size_t lds_per_workgroup;
+  bool in_kernel;
+};
+
+static pa_status choose_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t max_context_len, int32_t partition_size, pa_dtype dtype, pa_algo algo,
+                               DecodeChoice* c) {
+  const int group = num_heads / num_kv_heads;
+  if (algo == PA_ALGO_MFMA) {
+    if (dtype == PA_F32) return PA_ERR_UNSUPPORTED;
+    c->kernel_algo = pa::kAlgoMfma;
+  } else if (algo == PA_ALGO_VECTOR) {
+    c->kernel_algo = pa::kAlgoVector;
+  } else {
+    // measured on MI355X: the MFMA engine leads at every group size, MHA included
+    c->kernel_algo = dtype != PA_F32 ? pa::kAlgoMfma : pa::kAlgoVector;
+  }
+  c->G = c->kernel_algo == pa::kAlgoMfma ? 0 : (group <= 1 ? 1 : group <= 2 ? 2 : group <= 4 ? 4 : 8);
+  c->pl = make_plan(num_seqs, num_kv_heads, max_context_len, partition_size);
+  if (c->pl.mode == pa::kModeShared) {
+    if (c->kernel_algo == pa::kAlgoMfma) c->kernel_algo = pa::kAlgoMfmaShared;
+    else c->pl = make_plan(num_seqs, num_kv_heads, max_context_len, PA_PARTITION_AUTO);  // vector engine: balanced
+  }
+  const Plan& pl = c->pl;
+  c->wl = layout(pl, num_seqs, num_heads, num_kv_heads, head_dim);
+  c->elem = dtype == PA_F32 ? pa::kF32 : (dtype == PA_F16 ? pa::kF16 : pa::kBF16);
+  c->lds_per_workgroup = 0;
+  const int target = workers_target(c->elem, head_dim, c->kernel_algo, c->G, &c->lds_per_workgroup);
+  if (pl.mode == pa::kModeBalanced || pl.mode == pa::kModeFixedStream || pl.mode == pa::kModeShared) {
+    // rounded down: every worker of the grid must be resident at once, or
+    // the ones left over start only when others finish
+    c->workers = target / num_kv_heads;
+    const long long cap = pl.mode == pa::kModeFixedStream ? (long long)num_seqs * pl.max_parts : pl.max_workers;
+    if (c->workers > cap) c->workers = cap;
+    if (c->workers < 1) c->workers = 1;
+  } else {
+    c->workers = (long long)num_seqs * pl.max_parts;
+    if (c->workers > INT_MAX) return PA_ERR_UNSUPPORTED;
+  }
+  // The balanced split merges inside the decode kernel when there are at
+  // least half as many sequences as workers per KV head, so that a split
+  // sequence has few pieces (one wave merges them, a round trip per eight);
+  // fewer sequences spread over many workers leave up to one piece per
+  // worker, which the closing launch merges with many waves per sequence.
+  // Every counter index and partial-result byte offset must fit (always, at
+  // the sizes the workspace is laid out for).
+  const WorkspaceLayout& wl = c->wl;
+  c->in_kernel = pl.mode == pa::kModeBalanced && wl.total > 0 && 2LL * num_seqs >= c->workers &&
+                 c->workers * num_kv_heads <= pa::kArrivalSlots && wl.total - wl.ml < ((size_t)1 << 31);
+  return PA_OK;
+}
+
 static pa_status decode_impl(void* out, const void* q, const void* k_new, const void* v_new, const void* k_cache,
                              const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
                              int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -377,24 +442,12 @@ static pa_status decode_impl(void* out, const void* q, const void* k_new, const 
       !aligned(block_tables, 4) || !aligned(context_lens, 4))
     return PA_ERR_INVALID_ARG;
 
-  int kernel_algo;
-  if (algo == PA_ALGO_MFMA) {
-    if (dtype == PA_F32) return PA_ERR_UNSUPPORTED;
-    kernel_algo = pa::kAlgoMfma;
-  } else if (algo == PA_ALGO_VECTOR) {
-    kernel_algo = pa::kAlgoVector;
-  } else {
-    // measured on MI355X: the MFMA engine leads at every group size, MHA included
-    kernel_algo = dtype != PA_F32 ? pa::kAlgoMfma : pa::kAlgoVector;
-  }
-  const int G = kernel_algo == pa::kAlgoMfma ? 0 : (group <= 1 ? 1 : group <= 2 ? 2 : group <= 4 ? 4 : 8);
-
-  Plan pl = make_plan(num_seqs, num_kv_heads, max_context_len, partition_size);
-  if (pl.mode == pa::kModeShared) {
-    if (kernel_algo == pa::kAlgoMfma) kernel_algo = pa::kAlgoMfmaShared;
-    else pl = make_plan(num_seqs, num_kv_heads, max_context_len, PA_PARTITION_AUTO);  // vector engine: balanced
-  }
-  const WorkspaceLayout wl = layout(pl, num_seqs, num_heads, num_kv_heads, head_dim);
+  DecodeChoice dc;
+  const pa_status st = choose_decode(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, partition_size,
+                                     dtype, algo, &dc);
+  if (st != PA_OK) return st;
+  const Plan& pl = dc.pl;
+  const WorkspaceLayout& wl = dc.wl;
   if (static_workspace) {
     // the library's fixed per-device array; looked up after every argument
     // check, so a rejected call touches no device
@@ -427,6 +480,7 @@ static pa_status decode_impl(void* out, const void* q, const void* k_new, const 
   p.fam_base = wl.fam_base;
   p.fam_max = wl.fam_max;
   p.meta_stride = shared ? 4 : 2;
+  p.ctr = dc.in_kernel ? reinterpret_cast<int32_t*>(ws + wl.ctr) : nullptr;
   p.max_len = max_context_len;
   p.num_seqs = num_seqs;
   p.num_heads = num_heads;
@@ -442,31 +496,31 @@ static pa_status decode_impl(void* out, const void* q, const void* k_new, const 
   p.max_parts = pl.max_parts;
   p.out_dtype = out_dtype;
 
-  const int elem = dtype == PA_F32 ? pa::kF32 : (dtype == PA_F16 ? pa::kF16 : pa::kBF16);
-  long long workers;
-  size_t lds_per_workgroup = 0;
-  const int target = workers_target(elem, head_dim, kernel_algo, G, &lds_per_workgroup);
-  if (pl.mode == pa::kModeBalanced || pl.mode == pa::kModeFixedStream || shared) {
-    // rounded down: every worker of the grid must be resident at once, or
-    // the ones left over start only when others finish
-    workers = target / num_kv_heads;
-    const long long cap = pl.mode == pa::kModeFixedStream ? (long long)num_seqs * pl.max_parts : pl.max_workers;
-    if (workers > cap) workers = cap;
-    if (workers < 1) workers = 1;
-  } else {
-    workers = (long long)num_seqs * pl.max_parts;
-    if (workers > INT_MAX) return PA_ERR_UNSUPPORTED;
-  }
   if (shared) {
-    const hipError_t e = pa::launch_plan(p, (unsigned)workers, static_cast<hipStream_t>(stream));
+    const hipError_t e = pa::launch_plan(p, (unsigned)dc.workers, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return PA_ERR_LAUNCH;
   }
-  const hipError_t e = pa::launch_decode(p, elem, head_dim, kernel_algo, G, (unsigned)workers, pl.slots > 0,
-                                         lds_per_workgroup, static_cast<hipStream_t>(stream));
+  const hipError_t e = pa::launch_decode(p, dc.elem, head_dim, dc.kernel_algo, dc.G, (unsigned)dc.workers,
+                                         pl.slots > 0, dc.lds_per_workgroup, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
 extern "C" {
+
+int32_t pa_decode_launches(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t max_context_len, int32_t partition_size, pa_dtype dtype, pa_algo algo,
+                           int32_t fused) {
+  if (!valid_dtype(dtype) || (algo != PA_ALGO_AUTO && algo != PA_ALGO_VECTOR && algo != PA_ALGO_MFMA)) return 0;
+  if (!decode_shape_ok(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, partition_size)) return 0;
+  if (num_kv_heads > 65535 || num_heads / num_kv_heads > pa::kMaxGroup || num_seqs == 0) return 0;
+  DecodeChoice dc;
+  if (choose_decode(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, partition_size, dtype, algo, &dc) !=
+      PA_OK)
+    return 0;
+  const int planning = dc.pl.mode == pa::kModeShared ? 2 : 0;
+  const int closing = !dc.in_kernel && (dc.pl.slots > 0 || fused) ? 1 : 0;
+  return planning + 1 + closing;
+}
 
 pa_status pa_decode_ex(void* out, const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,

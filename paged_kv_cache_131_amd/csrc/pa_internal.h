@@ -13,6 +13,10 @@ namespace pa {
 constexpr int kChunk = 32;
 // Upper bound on balanced-split workers summed over KV heads; sizes workspaces.
 constexpr int kMaxWorkersTotal = 8192;
+// Arrival counters of the balanced split's in-kernel merge: one per (KV
+// head, worker), at the start of every decode workspace (a fixed region, so
+// calls of any shape and mode leave each other's counters alone).
+constexpr int kArrivalSlots = kMaxWorkersTotal;
 // Largest query-head group (num_heads / num_kv_heads) any kernel handles.
 constexpr int kMaxGroup = 8;
 // Balanced splits scan every sequence length in every worker; above this
@@ -86,6 +90,12 @@ struct DecodeParams {
   int32_t fam_base;     // first partial-result slot of the family region
   int32_t fam_max;      // most members of a family (sub-slots per family slot)
   int32_t meta_stride;  // ints per sequence in ws_meta: 2, or 4 in shared mode
+  // balanced split merged inside the decode kernel (no closing launch): the
+  // workspace's arrival counters, indexed kv_head * workers + the worker
+  // holding a split sequence's first chunk; zero before the launch, and the
+  // worker that completes a count sets it back to zero. Null: the closing
+  // launch merges and stores the new tokens.
+  int32_t* ctr;
 };
 
 // Most finished segments a decode workgroup keeps in LDS before storing them.
@@ -100,9 +110,10 @@ hipError_t static_scratch(void** ptr);
 
 // Launch the decode kernel for (elem, head_dim, algo, group bucket G),
 // grid = (workers per KV head, num_kv_heads), 64 threads per workgroup, then,
-// when `merge` is set or the call brings new tokens (k_new), the closing
-// kernel (grid = (num_seqs, num_kv_heads)) that combines the partial results
-// of split sequences and stores the new tokens into the cache.
+// unless the decode kernel merges itself (ctr set), when `merge` is set or
+// the call brings new tokens (k_new), the closing kernel (grid = (num_seqs,
+// num_kv_heads)) that combines the partial results of split sequences and
+// stores the new tokens into the cache.
 // lds_per_workgroup: the share of a CU's LDS one decode workgroup may take
 // (the CU's LDS over the resident workgroups per CU the worker count assumes).
 hipError_t launch_decode(const DecodeParams& p, int elem, int head_dim, int algo, int G,

@@ -29,7 +29,9 @@
 // Decode workspace of pa_decode_noalloc: a fixed array per device, so that
 // callers that cannot allocate still get the split path. Host code never
 // passes this name to a kernel (on the host it is only a stand-in for the
-// symbol); it uses the device address static_scratch() looks up.
+// symbol); it uses the device address static_scratch() looks up. Static
+// storage: zero when the code object is loaded, as the arrival counters at
+// the start of every decode workspace must be before their first use.
 static __device__ __align__(256) unsigned char scratch[pa::kStaticScratchBytes];
 
 namespace pa {
@@ -431,7 +433,9 @@ struct MfmaEngine {
   // consumed it is refilled with the next step (K after the last QK, V after
   // the last PV), so one step's loads are always in flight behind the math.
   // Column groups run one after the other: group cg's QK, softmax and PV
-  // (the K refill waits for the last group's QK).
+  // (the K refill waits for the last group's QK). The stream's last step
+  // (REFILL false) loads nothing.
+  template <bool REFILL>
   __device__ __forceinline__ void step(Frag& f, const DecodeParams& p, Smem& sm, int kvh, int lane, int cs, const Segment& cur,
                        int cs_next, const ChunkIds* ids_next, const Segment& nxt) {
     const int col = lane & 15, grp = lane >> 4, g = p.group;
@@ -442,10 +446,11 @@ struct MfmaEngine {
     const int part = kDistinct ? 0 : column_part(g, col);
     float sv[SUB][8];
     scores(f, p, qop[0], grp, cs, t1, partial, sv);
-    if (NCG == 1) {
-      // unconditional refill (at the end of the stream the last step re-reads
-      // itself from L2) keeps the count of loads in flight the same on every
-      // path, so the PV wait below never has to drain the next step's K loads
+    if (NCG == 1 && REFILL) {
+      // the refill of every step but the last (a separate copy of the step)
+      // is unconditional: the count of loads in flight is the same on every
+      // path of this code, so the PV wait below never has to drain the next
+      // step's K loads
       load_k(f, p, kvh, lane, cs_next, ids_next, nxt);
     }
     // V of tokens past the segment's end is selected out (never multiplied),
@@ -474,8 +479,10 @@ struct MfmaEngine {
         }
       }
     }
-    if (NCG > 1) load_k(f, p, kvh, lane, cs_next, ids_next, nxt);
-    load_v(f, p, kvh, lane, cs_next, ids_next, nxt);
+    if (REFILL) {
+      if (NCG > 1) load_k(f, p, kvh, lane, cs_next, ids_next, nxt);
+      load_v(f, p, kvh, lane, cs_next, ids_next, nxt);
+    }
   }
 
   // Column group cg's results into sm: o[head slot][dd], (m, l) per slot.
@@ -623,8 +630,10 @@ struct VecEngine {
     for (int st = 0; st < VSTEPS; ++st) f.vr[st] = load16_stream(vb + (size_t)st * DPS * Bs);
   }
 
-  __device__ void step(Frag& f, const DecodeParams& p, Smem& sm, int kvh, int lane, int cs, const Segment& cur,
-                       int cs_next, const ChunkIds* ids_next, const Segment& nxt) {
+  // REFILL false: the stream's last step, which loads nothing.
+  template <bool REFILL>
+  __device__ __forceinline__ void step(Frag& f, const DecodeParams& p, Smem& sm, int kvh, int lane, int cs,
+                                       const Segment& cur, int cs_next, const ChunkIds* ids_next, const Segment& nxt) {
     const int t1 = cur.t1;
     const bool has_new = cur.tnew >= cs && cur.tnew < cs + kChunk;
     const int piece = lane % LPR;
@@ -646,7 +655,7 @@ struct VecEngine {
         if (piece == 0) sm.sc[h][st * RPS + lane / LPR] = d;
       }
     }
-    load_k(f, p, kvh, lane, cs_next, ids_next, nxt);
+    if (REFILL) load_k(f, p, kvh, lane, cs_next, ids_next, nxt);
     __syncthreads();
 
     // softmax over the chunk's 32 tokens
@@ -690,7 +699,7 @@ struct VecEngine {
         acc[h][st] = a;
       }
     }
-    load_v(f, p, kvh, lane, cs_next, ids_next, nxt);
+    if (REFILL) load_v(f, p, kvh, lane, cs_next, ids_next, nxt);
     __syncthreads();  // sc/pl are rewritten by the next chunk
   }
 
@@ -730,7 +739,7 @@ struct VecEngine {
 // Segment driver, epilogue and merge (shared by both engines)
 // ---------------------------------------------------------------------------
 template <class Eng, int D>
-__device__ void write_zero_rows(const DecodeParams& p, int s, int kvh, int lane) {
+__device__ __forceinline__ void write_zero_rows(const DecodeParams& p, int s, int kvh, int lane) {
   const int g = p.group;
   const size_t base = ((size_t)s * p.num_heads + (size_t)kvh * g) * D;
   for (int idx = lane; idx < g * D; idx += 64) store_out(p.out, base + idx, 0.f, p.out_dtype);
@@ -966,11 +975,20 @@ __device__ __forceinline__ void store16(f32x4* dst, f32x4 v) {
   }
 }
 
+// The pieces of split sequences a worker of the in-kernel merge stored (at
+// most two: only the first and the last segment of a worker's chunk range
+// can be part of a sequence): sequence, pieces, worker holding the first.
+struct Arrival {
+  int s, np, first;
+};
+
 struct ResultBuf {
   float* vals;
   float* ml;
   int* rec;
   int n;
+  int narr;
+  Arrival arr0, arr1;
 };
 
 __device__ __forceinline__ ResultBuf result_buffer(const DecodeParams& p, int D) {
@@ -979,7 +997,34 @@ __device__ __forceinline__ ResultBuf result_buffer(const DecodeParams& p, int D)
   rb.ml = rb.vals + (size_t)p.res_slots * p.group * D;
   rb.rec = reinterpret_cast<int*>(rb.ml + (size_t)p.res_slots * p.group * 2);
   rb.n = 0;
+  rb.narr = 0;
+  rb.arr0 = rb.arr1 = Arrival{0, 0, 0};
   return rb;
+}
+
+// Partial results of the in-kernel merge are written and read by waves on
+// different XCDs within one launch, and each XCD has its own L2: they go
+// through agent-scope coherent (sc1) buffer accesses, which neither leave a
+// line behind in this XCD's L2 nor read a stale one from it. Byte offsets
+// from the region's base fit 31 bits (checked by the host).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ws_rsrc(const float* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, -1, 0x00020000);
+}
+constexpr int kCohSc1 = 16;  // cache-policy operand: sc1
+__device__ __forceinline__ void coh_store16(__amdgpu_buffer_rsrc_t r, size_t off, f32x4 v) {
+  const u32x4 u = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
+  __builtin_amdgcn_raw_buffer_store_b128(u, r, (int)off, 0, kCohSc1);
+}
+__device__ __forceinline__ void coh_store4(__amdgpu_buffer_rsrc_t r, size_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)off, 0, kCohSc1);
+}
+__device__ __forceinline__ f32x4 coh_load16(__amdgpu_buffer_rsrc_t r, size_t off) {
+  const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCohSc1);
+  return f32x4{__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w)};
+}
+__device__ __forceinline__ f32x2 coh_load8(__amdgpu_buffer_rsrc_t r, size_t off) {
+  const auto u = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kCohSc1);
+  return f32x2{__uint_as_float(u[0]), __uint_as_float(u[1])};
 }
 
 // Store every buffered result: whole sequences to `out`, pieces of split
@@ -989,18 +1034,19 @@ __device__ __forceinline__ ResultBuf result_buffer(const DecodeParams& p, int D)
 // partitions at the long-context shape 939 -> 913 us); at the stream's end
 // ordinary stores.
 template <int D, int MAXG, bool NT, bool SHARED>
-__device__ void flush_results(const DecodeParams& p, ResultBuf& rb, int kvh, int lane) {
+__device__ __forceinline__ void flush_results(const DecodeParams& p, ResultBuf& rb, int kvh, int lane) {
   constexpr int kStride = SHARED ? 4 : 2;  // ints per sequence in ws_meta
   constexpr int kV4 = (MAXG * D / 4 + 63) / 64;  // 16-byte pieces per lane and result
   const int gq = p.group, Hq = p.num_heads, n4 = gq * D / 4;
   const size_t head0 = (size_t)kvh * gq;
   const bool out_vec = (reinterpret_cast<uintptr_t>(p.out) & (p.out_dtype == kF32 ? 15 : 7)) == 0;
+  const bool coh = !SHARED && p.ctr != nullptr;  // pieces merged in this launch
   for (int k = 0; k < rb.n; ++k) {
     const int* r = rb.rec + kResRec * k;
     const int s = __builtin_amdgcn_readfirstlane(r[0]), np = __builtin_amdgcn_readfirstlane(r[1]);
     const int slot = __builtin_amdgcn_readfirstlane(r[2]);
     const float* v = rb.vals + (size_t)k * gq * D;
-    const int kind = r[4];
+    const int kind = coh ? 0 : r[4];
     if (kind && lane == 0) {
       // split record of sequence s: {own first slot, own pieces}, or in
       // shared mode {family first slot, family pieces, own first, own pieces}
@@ -1044,6 +1090,15 @@ __device__ void flush_results(const DecodeParams& p, ResultBuf& rb, int kvh, int
         for (int u = 0; u < kV4; ++u)
           if (lane + 64 * u < n4) store_out4(p.out, base + 4 * (size_t)(lane + 64 * u), t[u], dt, false);
       }
+    } else if (coh) {
+      const size_t row0 = (size_t)slot * Hq + head0;
+      const __amdgpu_buffer_rsrc_t ra = ws_rsrc(p.ws_acc), rm = ws_rsrc(p.ws_ml);
+#pragma unroll
+      for (int u = 0; u < kV4; ++u) {
+        const int i = lane + 64 * u;
+        if (i < n4) coh_store16(ra, (row0 * D + 4 * (size_t)i) * 4, t[u]);
+      }
+      for (int i = lane; i < 2 * gq; i += 64) coh_store4(rm, (row0 * 2 + i) * 4, rb.ml[(size_t)k * gq * 2 + i]);
     } else {
       const size_t row0 = (size_t)slot * Hq + head0;
 #pragma unroll
@@ -1103,6 +1158,12 @@ __device__ void segment_epilogue(const DecodeParams& p, const typename Eng::Smem
     r[4] = kvh == 0 ? seg_kind<kShared>(p, g) : 0;
     r[5] = direct;
   }
+  if (!kShared && !direct && p.ctr != nullptr) {
+    const Arrival a{g.s, g.npieces, g.first_slot - g.s};
+    if (rb.narr == 0) rb.arr0 = a;
+    else rb.arr1 = a;
+    rb.narr = min(rb.narr + 1, 2);
+  }
   rb.n = k + 1;
   __syncthreads();
 }
@@ -1129,8 +1190,8 @@ __device__ void finish_segment(const DecodeParams& p, Eng& eng, typename Eng::Sm
 // same time; block ids are read two chunks ahead. A segment's epilogue
 // therefore overlaps the next segment's first loads.
 template <class Eng, int D>
-__device__ void run_stream(const DecodeParams& p, typename Eng::Smem& sm, SegmentSource<(Eng::kGroups > 1)>& src,
-                           int kvh, int lane) {
+__device__ __forceinline__ void run_stream(const DecodeParams& p, typename Eng::Smem& sm, SegmentSource<(Eng::kGroups > 1)>& src,
+                           int kvh, int lane, ResultBuf& rb) {
   static_assert(Eng::kSub == 1, "the chunk stream assumes one 32-token chunk per step");
   Segment A = src.next(p);
   if (!A.valid) return;
@@ -1141,7 +1202,6 @@ __device__ void run_stream(const DecodeParams& p, typename Eng::Smem& sm, Segmen
   Eng eng;
   typename Eng::Q q, qn;
   eng.load_q(q, p, A, kvh, lane);
-  ResultBuf rb = result_buffer(p, D);
   Segment B = src.next(p);
   Segment C = B.valid ? src.next(p) : invalid_segment();
   Pos p1 = advance(p0, A, B, C);
@@ -1157,10 +1217,16 @@ __device__ void run_stream(const DecodeParams& p, typename Eng::Smem& sm, Segmen
     const bool at_end = !leaving && p1.cs == p0.cs;         // and there is no next segment
     const Segment n1 = seg_at(p1.rel, A, B, C);
     if (leaving) eng.load_q(qn, p, n1, kvh, lane);
-    eng.step(f, p, sm, kvh, lane, p0.cs, A, p1.cs, &ids1, n1);
-    if (leaving || at_end) {
+    if (at_end) {
+      // the last step issues no refill: nothing of the stream is left in
+      // flight behind its results
+      eng.template step<false>(f, p, sm, kvh, lane, p0.cs, A, p1.cs, &ids1, n1);
       finish_segment<Eng, D>(p, eng, sm, A, kvh, lane, rb);
-      if (at_end) break;
+      break;
+    }
+    eng.template step<true>(f, p, sm, kvh, lane, p0.cs, A, p1.cs, &ids1, n1);
+    if (leaving) {
+      finish_segment<Eng, D>(p, eng, sm, A, kvh, lane, rb);
       A = B;
       B = C;
       C = B.valid ? src.next(p) : invalid_segment();
@@ -1173,7 +1239,208 @@ __device__ void run_stream(const DecodeParams& p, typename Eng::Smem& sm, Segmen
     p2 = advance(p2, A, B, C);
     ids1 = ids2;
   }
-  flush_results<D, Eng::kMaxGroup, false, (Eng::kGroups > 1)>(p, rb, kvh, lane);
+  // a launch that merges itself flushes in settle(), with the new tokens'
+  // loads in flight
+  if ((Eng::kGroups > 1) || p.ctr == nullptr) flush_results<D, Eng::kMaxGroup, false, (Eng::kGroups > 1)>(p, rb, kvh, lane);
+}
+
+// The in-kernel merge, run by the worker whose piece completed the count of
+// a split sequence, for up to two sequences at once (a worker's first and
+// last segment; their pieces' loads go out together): pieces first ..
+// first + np - 1 of each, in piece order, folded with a running maximum.
+// The weights are those of the closing launch's merge -- piece k of head h
+// weighs 2^(m_k - M) over M = max_j m_j, and out = sum_k 2^(m_k - M) acc_k /
+// sum_k 2^(m_k - M) l_k -- rescaled as M grows. Lane l covers 4 channels of
+// every (64 / (D/4))-th head; each piece's (m, l) pair and 16-byte share of
+// acc are read with agent-scope loads, kIn pieces in flight.
+template <int D, int MAXG>
+struct MergeAcc {
+  static constexpr int RPI = 64 / (D / 4);         // head rows per wave instruction
+  static constexpr int HPL = (MAXG + RPI - 1) / RPI;  // heads per lane
+  float M[HPL], den[HPL];
+  f32x4 num[HPL];
+  __device__ void init() {
+#pragma unroll
+    for (int j = 0; j < HPL; ++j) {
+      M[j] = kNegInf;
+      den[j] = 0.f;
+      num[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  __device__ void fold(int j, f32x2 ml, f32x4 a) {
+    const float m = ml.x, Mn = fmaxf(M[j], m);
+    if (Mn != kNegInf) {
+      const float c = fast_exp2(M[j] - Mn), e = fast_exp2(m - Mn);
+      den[j] = fmaf(den[j], c, e * ml.y);
+      num[j] = num[j] * c + e * a;
+      M[j] = Mn;
+    }
+  }
+};
+
+template <int D, int MAXG>
+__device__ __forceinline__ void merge_arrived(const DecodeParams& p, int kvh, int lane, const Arrival& a0, bool m0,
+                                              const Arrival& a1, bool m1) {
+  using Acc = MergeAcc<D, MAXG>;
+  constexpr int LPR = D / 4, RPI = Acc::RPI, HPL = Acc::HPL;
+  constexpr int kIn = 8;
+  const int gq = p.group, Hq = p.num_heads;
+  const int r = lane / LPR, d4 = (lane % LPR) * 4;
+  const int head0 = kvh * gq;
+  const __amdgpu_buffer_rsrc_t ra = ws_rsrc(p.ws_acc), rm = ws_rsrc(p.ws_ml);
+  const int n0 = m0 ? a0.np : 0, total = n0 + (m1 ? a1.np : 0);
+  Acc acc0, acc1;
+  acc0.init();
+  acc1.init();
+  for (int k0 = 0; k0 < total; k0 += kIn) {
+    // every load of the batch unconditional (past the last piece or head:
+    // the last one again), so that they all go out before the first wait
+    f32x2 ml[kIn][HPL];
+    f32x4 v[kIn][HPL];
+#pragma unroll
+    for (int i = 0; i < kIn; ++i) {
+      const int k = min(k0 + i, total - 1);
+      const int slot = k < n0 ? a0.first + a0.s + k : a1.first + a1.s + (k - n0);
+#pragma unroll
+      for (int j = 0; j < HPL; ++j) {
+        const int h = min(r + j * RPI, gq - 1);
+        const size_t row = (size_t)slot * Hq + head0 + h;
+        ml[i][j] = coh_load8(rm, row * 2 * 4);
+        v[i][j] = coh_load16(ra, (row * D + d4) * 4);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kIn; ++i) {
+      const int k = k0 + i;
+      if (k >= total) continue;
+#pragma unroll
+      for (int j = 0; j < HPL; ++j) {
+        if (r + j * RPI >= gq) continue;
+        if (k < n0) acc0.fold(j, ml[i][j], v[i][j]);
+        else acc1.fold(j, ml[i][j], v[i][j]);
+      }
+    }
+  }
+  const bool out_vec = (reinterpret_cast<uintptr_t>(p.out) & (p.out_dtype == kF32 ? 15 : 7)) == 0;
+#pragma unroll
+  for (int j = 0; j < HPL; ++j) {
+    const int h = r + j * RPI;
+    if (h >= gq) continue;
+    if (m0) store_out4(p.out, ((size_t)a0.s * Hq + head0 + h) * D + d4, acc0.num[j] * (1.f / acc0.den[j]),
+                       p.out_dtype, out_vec);
+    if (m1) store_out4(p.out, ((size_t)a1.s * Hq + head0 + h) * D + d4, acc1.num[j] * (1.f / acc1.den[j]),
+                       p.out_dtype, out_vec);
+  }
+}
+
+// The fused write of a launch that merges itself: worker w of W stores the
+// new tokens of sequences w, w + W, ... for its KV head (the slot of
+// position L-1, when the length was not cut and the table entry lies inside
+// the pool). It may overlap the other workers' reads of the cache: the one
+// worker that reads the slot's chunk takes that token's K row and V
+// elements from k_new/v_new, never from the slot, and the store changes no
+// other byte. Non-temporal: a V column dirties one cache line per element,
+// which left in the cache is written back during the next decode's stream.
+// kBatch sequences per round trip: loads, then stores.
+template <typename U, int D>
+struct NewTokens {
+  static constexpr int kBatch = 8;
+  static constexpr int NE = D / 64;
+  int phys[kBatch], off[kBatch];
+  U kv[kBatch][NE], vv[kBatch][NE];
+
+  // s0 < num_seqs and max_blocks_per_seq >= 1. Every load unconditional
+  // (for a sequence without a write: an in-bounds row, unused), so that they
+  // all go out before the first wait.
+  __device__ void load(const DecodeParams& p, int s0, int W, int kvh, int lane) {
+    const int S = p.num_seqs, Hkv = p.num_kv_heads;
+    const U* kn = static_cast<const U*>(p.k_new);
+    const U* vn = static_cast<const U*>(p.v_new);
+    const const_i32* tables = (const const_i32*)p.block_tables;
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int s = s0 + i * W;
+      const int sc = min(s, S - 1);
+      const int L = lds_len(sc);
+      const bool ok = s < S && L > 0 && capped_len(p, L) == L;
+      const int t = ok ? L - 1 : 0;
+      const int ph = tables[(size_t)sc * p.max_blocks_per_seq + (t >> p.log2_block)];
+      phys[i] = ok ? ph : -1;
+      off[i] = t & (p.block_size - 1);
+      const size_t src = ((size_t)sc * Hkv + kvh) * D;
+#pragma unroll
+      for (int j = 0; j < NE; ++j) {
+        kv[i][j] = kn[src + lane + 64 * j];
+        vv[i][j] = vn[src + lane + 64 * j];
+      }
+    }
+  }
+
+  __device__ void store(const DecodeParams& p, int kvh, int lane) const {
+    const int Hkv = p.num_kv_heads, B = p.block_size, Bs = v_subtile(B);
+    U* kc = const_cast<U*>(static_cast<const U*>(p.k_cache));
+    U* vc = const_cast<U*>(static_cast<const U*>(p.v_cache));
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (phys[i] < 0 || phys[i] >= p.num_blocks) continue;
+      U* kd = kc + (((size_t)phys[i] * Hkv + kvh) * B + off[i]) * D;
+      U* vd = vc + v_elem(phys[i], Hkv, kvh, D, B, Bs, 0, off[i]);
+#pragma unroll
+      for (int j = 0; j < NE; ++j) {
+        const int e = lane + 64 * j;
+        __builtin_nontemporal_store(kv[i][j], kd + e);
+        __builtin_nontemporal_store(vv[i][j], vd + (size_t)e * Bs);
+      }
+    }
+  }
+};
+
+// End of a balanced-split worker whose launch merges itself. The buffered
+// results are stored (the pieces with agent-scope stores, so nothing of them
+// waits in this XCD's L2); once every store is acknowledged, each piece
+// counts its arrival, and the worker whose add completes a sequence's count
+// merges it, reading every piece with agent-scope loads, and sets the
+// counter back to zero for the next launch. No worker waits for another.
+// The new tokens' loads go out with the merge's, their stores last: issued
+// before the flush, the scalar table loads would hold up its LDS reads (one
+// counter covers both), and stores ahead of the merge's loads would hold
+// those up in the in-order vector-memory count.
+template <class Eng, int D>
+__device__ __forceinline__ void settle(const DecodeParams& p, ResultBuf& rb, int w, int W, int kvh, int lane) {
+  using NT = NewTokens<typename Eng::raw, D>;
+  const bool writes = p.k_new != nullptr && w < p.num_seqs && p.max_blocks_per_seq > 0;
+  flush_results<D, Eng::kMaxGroup, false, false>(p, rb, kvh, lane);
+  int* c0 = p.ctr + (size_t)kvh * W + rb.arr0.first;
+  int* c1 = p.ctr + (size_t)kvh * W + rb.arr1.first;
+  int old0 = 0, old1 = 0;
+  if (rb.narr > 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (lane == 0) {
+      old0 = __hip_atomic_fetch_add(c0, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (rb.narr > 1) old1 = __hip_atomic_fetch_add(c1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  NT nt;
+  if (writes) nt.load(p, w, W, kvh, lane);
+  if (rb.narr > 0) {
+    old0 = __builtin_amdgcn_readfirstlane(old0);
+    old1 = __builtin_amdgcn_readfirstlane(old1);
+    asm volatile("" ::: "memory");
+    const bool m0 = old0 == rb.arr0.np - 1, m1 = rb.narr > 1 && old1 == rb.arr1.np - 1;
+    if (lane == 0) {
+      if (m0) __hip_atomic_store(c0, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (m1) __hip_atomic_store(c1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (m0 || m1) merge_arrived<D, Eng::kMaxGroup>(p, kvh, lane, rb.arr0, m0, rb.arr1, m1);
+  }
+  if (writes) {
+    nt.store(p, kvh, lane);
+    for (int s0 = w + NT::kBatch * W; s0 < p.num_seqs; s0 += NT::kBatch * W) {
+      NT more;
+      more.load(p, s0, W, kvh, lane);
+      more.store(p, kvh, lane);
+    }
+  }
 }
 
 // Workgroups are handed to the 8 XCDs (each with its own L2) in turn by
@@ -1218,7 +1485,8 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
     src.first = first;
     src.first_item = make_item(wr + 8);
     src.fixed = invalid_segment();
-    run_stream<Eng, D>(p, sm, src, kvh, lane);
+    ResultBuf rb = result_buffer(p, D);
+    run_stream<Eng, D>(p, sm, src, kvh, lane, rb);
     return;
   } else {
   if (p.mode == kModeFixed) {
@@ -1244,7 +1512,8 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
     g.tnew = new_token_pos(p, g.t1, L, L_raw);
     g.valid = 1;
     src.fixed = uniform(g);
-    run_stream<Eng, D>(p, sm, src, kvh, lane);
+    ResultBuf rb = result_buffer(p, D);
+    run_stream<Eng, D>(p, sm, src, kvh, lane, rb);
     return;
   }
 
@@ -1285,35 +1554,37 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
   // with no more workers than chunks every range is non-empty, so the pieces
   // of a sequence are exactly the workers owner_of(first chunk)..owner_of(last)
   const long long Wn = (long long)W < T ? (long long)W : T;
-  if (w >= Wn) return;
-  const long long start = (long long)w * T / Wn, end = (long long)(w + 1) * T / Wn;
-
-  const unsigned long long ball = __ballot(start >= excl && start < incl);
-  if (ball == 0ull) return;  // unreachable while 0 <= start < T
-  const int owner = __builtin_ctzll(ball);
-  int s_first = 0;
-  long long c_first = 0;
-  if (lane == owner) {
-    long long c = excl;
-    for (int s = s_lo; s < s_hi; ++s) {
-      const int n = num_chunks(capped_len(p, g_lens[s]));
-      if (start < c + n) {
-        s_first = s;
-        c_first = c;
-        break;
+  ResultBuf rb = result_buffer(p, D);
+  if (w < Wn) {
+    const long long start = (long long)w * T / Wn, end = (long long)(w + 1) * T / Wn;
+    // never empty while 0 <= start < T
+    const unsigned long long ball = __ballot(start >= excl && start < incl);
+    const int owner = ball ? __builtin_ctzll(ball) : 0;
+    int s_first = 0;
+    long long c_first = 0;
+    if (lane == owner) {
+      long long c = excl;
+      for (int s = s_lo; s < s_hi; ++s) {
+        const int n = num_chunks(capped_len(p, g_lens[s]));
+        if (start < c + n) {
+          s_first = s;
+          c_first = c;
+          break;
+        }
+        c += n;
       }
-      c += n;
     }
+    src.s = __builtin_amdgcn_readfirstlane(__shfl(s_first, owner));
+    src.c = __shfl(c_first, owner);
+    src.k = 0;
+    src.start = start;
+    src.end = ball ? end : start;
+    src.W = Wn;
+    src.T = T;
+    src.fixed = invalid_segment();
+    run_stream<Eng, D>(p, sm, src, kvh, lane, rb);
   }
-  src.s = __builtin_amdgcn_readfirstlane(__shfl(s_first, owner));
-  src.c = __shfl(c_first, owner);
-  src.k = 0;
-  src.start = start;
-  src.end = end;
-  src.W = Wn;
-  src.T = T;
-  src.fixed = invalid_segment();
-  run_stream<Eng, D>(p, sm, src, kvh, lane);
+  if (p.ctr != nullptr) settle<Eng, D>(p, rb, w, W, kvh, lane);
   }
 }
 
@@ -2105,7 +2376,8 @@ hipError_t launch_decode(const DecodeParams& p, int elem, int head_dim, int algo
   hipError_t e = hipLaunchKernel(fn, dim3(workers, (unsigned)p.num_kv_heads, 1), dim3(64, 1, 1), kargs,
                                  lens_bytes + slots * slot_bytes, stream);
   // the closing launch merges split sequences and stores the fused write
-  if (e != hipSuccess || (!merge && !p.k_new)) return e;
+  // (both done by the decode kernel itself when it has arrival counters)
+  if (e != hipSuccess || p.ctr != nullptr || (!merge && !p.k_new)) return e;
   // few pieces per sequence: one wave per (sequence, KV head); many (fixed
   // partitions, or a balanced split of few sequences over many workers):
   // four waves per (sequence, query head)

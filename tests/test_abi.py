@@ -31,6 +31,14 @@ def lib():
     return pb.load_library()
 
 
+def test_header_sizes_match_binding():
+    text = open(HEADER).read()
+    sizes = {m.group(1): int(m.group(2)) << int(m.group(3) or 0)
+             for m in re.finditer(r"#define (PA_\w+_BYTES) \(\(size_t\)(\d+)(?: << (\d+))?\)", text)}
+    assert sizes["PA_WORKSPACE_COUNTER_BYTES"] == pb.WORKSPACE_COUNTER_BYTES == 8192 * 4  # one int per worker
+    assert sizes["PA_NOALLOC_SCRATCH_BYTES"] == pb.NOALLOC_SCRATCH_BYTES
+
+
 def test_exports_match_header(lib):
     declared = declared_functions()
     assert declared == sorted(pb.SIGNATURES), "binding signatures out of sync with the header"
@@ -43,7 +51,7 @@ def test_exports_match_header(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.pa_abi_version() == 6
+    assert lib.pa_abi_version() == 7
     assert lib.pa_status_string(OK) == b"ok"
     assert lib.pa_status_string(WORKSPACE) == b"workspace missing or too small"
     assert lib.pa_status_string(123) == b"unknown status"
@@ -116,11 +124,25 @@ def test_decode_workspace_sizes(lib):
     assert f(4, 32, 8, 128, 1024, 0) == 0                  # single pass never splits
     assert f(4, 32, 8, 128, 512, 512) == 0                 # one partition per sequence
     two = f(4, 32, 8, 128, 1024, 512)                      # 2 partitions x 4 seqs = 8 slots
-    assert two == 256 + 8 * 32 * 2 * 4 + 8 * 32 * 128 * 4   # split records, (m, l), partial outputs
+    # arrival counters, split records, (m, l), partial outputs
+    assert two == 32768 + 256 + 8 * 32 * 2 * 4 + 8 * 32 * 128 * 4
     auto = f(256, 32, 8, 128, 8192, -1)
-    assert auto >= (1024 + 256) * 32 * 130 * 4             # balanced: workers + sequences slots
+    assert auto >= 32768 + (1024 + 256) * 32 * 130 * 4     # balanced: workers + sequences slots
     assert f(4, 30, 8, 128, 1024, -1) == 0                 # rejected shape
     assert f(4, 32, 8, 128, 1024, 40) == 0
+
+
+def test_decode_launch_count_rejections(lib):
+    # argument checks come before any device query: 0 for what pa_decode rejects or for no sequences
+    f = lib.pa_decode_launches
+    BF16 = 2
+    assert f(0, 32, 8, 128, 1024, -1, BF16, 0, 1) == 0     # no sequences
+    assert f(4, 32, 8, 96, 1024, -1, BF16, 0, 1) == 0      # head_dim
+    assert f(4, 30, 8, 128, 1024, -1, BF16, 0, 1) == 0     # heads not a multiple of KV heads
+    assert f(4, 72, 8, 128, 1024, -1, BF16, 0, 1) == 0     # group 9
+    assert f(4, 32, 8, 128, 1024, 40, BF16, 0, 1) == 0     # partition not a multiple of 32
+    assert f(4, 32, 8, 128, 1024, -1, 7, 0, 1) == 0        # dtype
+    assert f(4, 32, 8, 128, 1024, -1, BF16, 5, 1) == 0     # algo
 
 
 def test_decode_workspace_sizes_shared_mode(lib):
@@ -129,7 +151,8 @@ def test_decode_workspace_sizes_shared_mode(lib):
     workers = 2048 // Hkv                                  # worker waves per KV head
     fam_max = 2 * (16 // (Hq // Hkv))                      # members per family
     slots = workers + 2 * S + (workers + S // 2 + 1) * fam_max
-    need = (S * 4 * 4                                      # split records, four ints
+    need = (32768                                          # arrival counters
+            + S * 4 * 4                                    # split records, four ints
             + S * 2 * 8 * 4                                # work items, eight ints
             + workers * 16 * 4                             # worker records, sixteen ints
             + S * 4                                        # prefix links

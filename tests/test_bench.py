@@ -69,14 +69,22 @@ def test_counter_summary_scaling_and_hash(bench, tmp_path, monkeypatch):
     # per launch: mean over dispatches, fetch x2, write x1, KiB -> bytes
     assert entry["kernels"]["decode_kernel"]["traffic_bytes"] == (200.0 * 2 + 40.0) * 1024
     assert entry["kernels"]["merge_kernel"]["traffic_bytes"] == (10.0 * 2 + 6.0) * 1024
-    assert entry["decode_kernel+merge_kernel"] == (440.0 + 26.0) * 1024
     assert json.loads(traffic.read_text())["llama3_8b"]["kernel_hash"] == bench.kernel_hash("llama3_8b")
     assert bench.traffic_for("decode_kernel+merge_kernel", "llama3_8b") == (440.0 + 26.0) * 1024
+    assert bench.traffic_for("decode_kernel", "llama3_8b") == 440.0 * 1024
+    assert bench.traffic_for("write_kv_kernel+decode_kernel", "llama3_8b") is None  # not in the record
     # a record taken on other kernel sources is not used
     rec = json.loads(traffic.read_text())
     rec["llama3_8b"]["kernel_hash"] = "0" * 16
     traffic.write_text(json.dumps(rec))
     assert bench.traffic_for("decode_kernel+merge_kernel", "llama3_8b") is None
+
+
+def test_step_kernels_from_launch_counts(bench):
+    assert bench.step_kernels(1, True) == "decode_kernel"
+    assert bench.step_kernels(2, True) == "decode_kernel+merge_kernel"
+    assert bench.step_kernels(4, True) == "link_kernel+plan_kernel+decode_kernel+merge_kernel"
+    assert bench.step_kernels(1, False) == "write_kv_kernel+decode_kernel"
 
 
 def test_more_than_one_gpu_is_refused():

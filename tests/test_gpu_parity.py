@@ -333,23 +333,27 @@ def test_zero_length_context_writes_zeros():
         check(out[keep], ref[keep], 2e-3, f"others part={part} {algo}")
 
 
-def test_workspace_contents_do_not_matter():
+def test_workspace_contents_past_the_counters_do_not_matter():
     # a workspace full of garbage (stale records of another call included)
-    # gives the same, correct result
+    # past its zeroed arrival counters gives the same, correct result, and
+    # the call leaves the counters zero
     cfg = small_cfg("llama3_8b", num_seqs=16)
     w = wl.make_decode_workload(cfg)
     dv = Dev(w)
     dv.write()
     kr, vr = host_after_write(w)
     ref = oracle.decode(w.q, kr, vr, w.block_tables, w.context_lens, cfg.scale, 16, "bf16")
+    nc = pb.WORKSPACE_COUNTER_BYTES
     for part in (-1, 64):
         need = pb.pa_decode_workspace_bytes(16, 32, 8, 128, w.max_context_len, part)
         for fill in (0, 0x7F, 0xFF):
             ws = torch.full((need,), fill, dtype=torch.uint8, device=DEV)
+            ws[:nc].zero_()
             out = torch.empty(dv.q.shape, dtype=torch.float32, device=DEV)
             pb.pa_decode(out, dv.q, dv.kc, dv.vc, dv.bt, dv.cl, cfg.scale, w.max_context_len, partition_size=part,
                          workspace=ws)
             check(out, ref, 2e-3, f"workspace filled with {fill:#x}, part={part}")
+            assert int(ws[:nc].count_nonzero()) == 0, "arrival counters not left at zero"
 
 
 def test_calls_on_two_streams_get_their_own_workspaces():

@@ -36,7 +36,7 @@ def run_case(w, part):
     NB, Hkv, B, _ = kc.shape
     need = pb.pa_decode_workspace_bytes(S, Hq, Hkv, d, w.max_context_len, part)
     assert 0 < need <= pb.NOALLOC_SCRATCH_BYTES
-    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
     ref_out = torch.empty(q.shape, dtype=torch.float32, device=DEV)
     pb.pa_decode(ref_out, q, kc, vc, bt, cl, cfg.scale, w.max_context_len, partition_size=part, workspace=ws)
     got = torch.full(q.shape, float("nan"), dtype=torch.float32, device=DEV)
