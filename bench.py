@@ -399,7 +399,10 @@ def shape_sweep(torch, pb, wl, reps: int) -> list:
     """pa_write_decode over a grid of batch sizes and equal context lengths
     (Llama-3-8B head shape: 32 query / 8 KV heads, head_dim 128, block 16,
     bf16, shuffled pool, balanced split), up to 4.2 M context tokens per step.
-    K/V values are seeded normal draws on the device (timing only)."""
+    K/V values are seeded normal draws on the device (timing only). Each
+    shape is timed twice: calls issued one by one from Python (where small
+    steps wait on the host's issue rate), and the same calls replayed from
+    a HIP graph (the GPU's time)."""
     import dataclasses
 
     dev = torch.device("cuda:0")
@@ -421,9 +424,11 @@ def shape_sweep(torch, pb, wl, reps: int) -> list:
             vn = torch.randn((S, Hkv, d), device=dev, dtype=torch.bfloat16, generator=g)
             bt, cl = pb.int32_to_device(w.block_tables, dev), pb.int32_to_device(w.context_lens, dev)
             out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+            need = pb.pa_decode_workspace_bytes(S, cfg.num_heads, cfg.num_kv_heads, d, w.max_context_len, -1)
+            ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
 
             def step():
-                pb.pa_write_decode(out, q, kn, vn, kc, vc, bt, cl, cfg.scale, w.max_context_len)
+                pb.pa_write_decode(out, q, kn, vn, kc, vc, bt, cl, cfg.scale, w.max_context_len, workspace=ws)
 
             for _ in range(10):
                 step()
@@ -435,9 +440,33 @@ def shape_sweep(torch, pb, wl, reps: int) -> list:
             e1.record()
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) / reps * 1000
+            # the same steps replayed from a HIP graph: the GPU's own time per
+            # step, without the host's cost of issuing each call
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                step()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for _ in range(reps):
+                    step()
+            graph.replay()
+            torch.cuda.synchronize()
+            e0.record()
+            graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            gus = e0.elapsed_time(e1) / reps * 1000
+            del graph
             nbytes = decode_bytes(cfg, w.context_lens)["total"] + write_bytes(cfg, S, True)
-            rows.append({"num_seqs": S, "context_len": L, "step_us": round(us, 1), "bytes": nbytes,
-                         "GBps": round(nbytes / us / 1e3), "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 3)})
+            rows.append({"num_seqs": S, "context_len": L, "step_us": round(us, 1), "graph_step_us": round(gus, 1),
+                         "bytes": nbytes, "GBps": round(nbytes / us / 1e3),
+                         "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 3),
+                         "graph_frac": round(nbytes / gus / 1e3 / HBM_PEAK_GBS, 3),
+                         "launches": pb.pa_decode_launches(S, cfg.num_heads, cfg.num_kv_heads, d, w.max_context_len,
+                                                           -1, q.dtype, "auto", True)})
             print(json.dumps(rows[-1]), flush=True)
             del kc, vc
             torch.cuda.empty_cache()

@@ -15,8 +15,12 @@
 // limit as a per-column mask. P enters PV as a rounded 16-bit part plus its
 // rounding residual (two MFMAs), which keeps the products fp32-accurate.
 //
-// LDS layout of one stage, in 16-byte units (swizzled so that the 16 lanes of
-// an MFMA operand read fall in distinct banks):
+// LDS layout of one stage, in 16-byte units, swizzled for conflict-free
+// operand reads. A 16-byte LDS read of 64 lanes is served in four passes of
+// 16 lanes, grouped by lane bit 5 and the parity of lane bits 2-4 (measured on
+// gfx950 with SQ_LDS_BANK_CONFLICT over patterns that tell the groupings
+// apart); a pass costs one cycle when its 16 lanes fall in distinct 16-byte
+// bank groups (64 four-byte banks), one more per extra lane in a group.
 //   K: token t of the chunk, head-dim segment s (8 elements) at unit
 //      t * D/8 + (s ^ fk(t));
 //   V, after K's 32*D/8 units: channel c, token group u (8 tokens) at unit
@@ -72,7 +76,11 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
 }
 
 __device__ __forceinline__ int k_swizzle(int t, int D) { return ((t & 3) | ((t >> 1) & 12)) & (D / 8 - 1); }
-__device__ __forceinline__ int v_swizzle(int c) { return (c >> 2) & 3; }
+// V: the four 8-token groups of channel c are permuted by bit 2 of c. With the
+// previous (c >> 2) & 3, two lanes of every pass shared a bank group (57M
+// conflict cycles per launch of the 32-prompt batch; 5M now, all in the
+// output staging, which has since been fixed too).
+__device__ __forceinline__ int v_swizzle(int c) { return (c >> 1) & 2; }
 
 // Wait until at most N of this wave's vector memory operations are in flight,
 // then meet the other waves; LDS accesses are not moved across it.
@@ -423,9 +431,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(PrefillPara
   // contiguous outputs, so each wave stages its rows, group by group, in its
   // own half of a ring stage (free once every wave is past the last chunk's
   // reads) and stores them 16 bytes per lane; element dd of row r sits at
-  // r*D + (dd ^ ((r & 3) << 4)), which spreads the four rows one write
-  // instruction touches over the banks. An output not 16-byte aligned takes
-  // the per-element stores.
+  // r*D + (dd ^ ((r >> 2) << 4)): the 64 lanes of a write instruction (rows
+  // 4*grp + i, elements 16j + col) then fall in 64 distinct banks, and a
+  // 16-byte unit of the read-back stays contiguous. An output not 16-byte
+  // aligned takes the per-element stores.
   __syncthreads();
   const bool vec_out = (reinterpret_cast<uintptr_t>(p.out) & 15) == 0;
   const int es = p.out_dtype == kF32 ? 4 : 2;
@@ -442,7 +451,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(PrefillPara
         const int r = 4 * grp + i;
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
-          const int e = r * D + ((16 * j + col) ^ ((r & 3) << 4));
+          const int e = r * D + ((16 * j + col) ^ ((r >> 2) << 4));
           const float v = T.o[gi][j][i] * inv[i];
           if (es == 4) reinterpret_cast<float*>(stg)[e] = v;
           else
@@ -457,7 +466,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(PrefillPara
         const int r = u / upr, c = u - r * upr;
         const int qr = r / g, jq = gi * qt + qr;
         if (jq < nq_w) {
-          const int e0 = (c * 16 / es) ^ ((r & 3) << 4);  // the unit's first element, as staged
+          const int e0 = (c * 16 / es) ^ ((r >> 2) << 4);  // the unit's first element, as staged
           const u32x4 val = *reinterpret_cast<const u32x4*>(stg + (size_t)(r * D + e0) * es);
           const size_t base = ((size_t)(q0 + j0 + wave * qw + jq) * Hq + T.kvh * g + (r - qr * g)) * D;
           *reinterpret_cast<u32x4*>(static_cast<char*>(p.out) + (base + (size_t)c * 16 / es) * es) = val;
