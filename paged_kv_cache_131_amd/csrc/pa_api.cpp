@@ -402,14 +402,17 @@ static pa_status choose_decode(int32_t num_seqs, int32_t num_heads, int32_t num_
     if (c->workers > INT_MAX) return PA_ERR_UNSUPPORTED;
   }
   // The balanced split merges inside the decode kernel when there are at
-  // least half as many sequences as workers per KV head, so that a split
-  // sequence has few pieces (one wave merges them, a round trip per eight);
-  // fewer sequences spread over many workers leave up to one piece per
-  // worker, which the closing launch merges with many waves per sequence.
+  // least a quarter as many sequences as workers per KV head, so that a
+  // split sequence has few pieces (one wave merges them, a round trip per
+  // eight); fewer sequences spread over many workers leave up to one piece
+  // per worker, which the closing launch merges with many waves per sequence
+  // (measured on MI355X, graph replay: 32 x 2,048 tokens 51.3 -> 50.5 us
+  // merged in-kernel; 16 x 256 12.9 -> 15.5 us, 16 sequences of the long-
+  // context shape 815 -> 822 us, so those keep the closing launch).
   // Every counter index and partial-result byte offset must fit (always, at
   // the sizes the workspace is laid out for).
   const WorkspaceLayout& wl = c->wl;
-  c->in_kernel = pl.mode == pa::kModeBalanced && wl.total > 0 && 2LL * num_seqs >= c->workers &&
+  c->in_kernel = pl.mode == pa::kModeBalanced && wl.total > 0 && 4LL * num_seqs >= c->workers &&
                  c->workers * num_kv_heads <= pa::kArrivalSlots && wl.total - wl.ml < ((size_t)1 << 31);
   return PA_OK;
 }

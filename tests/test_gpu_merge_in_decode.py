@@ -81,8 +81,8 @@ def mixed_lengths(S, seed):
     ("bf16", 64, 8, 8, 64, "vector", False),    # the vector engine, g = 1, 64-token blocks
 ])
 def test_in_kernel_merge_many_sequences(etype, d, Hq, Hkv, B, algo, fused):
-    """1,024 sequences (at least half as many as any launch has workers per
-    KV head, so the decode kernel merges itself): every output against the
+    """1,024 sequences (at least a quarter as many as any launch has workers
+    per KV head, so the decode kernel merges itself): every output against the
     oracle, for both engines, with and without the fused write, and the
     arrival counters left zero."""
     S = 1024
@@ -180,17 +180,54 @@ def test_graph_replay_matches_eager():
 
 def test_launch_counts():
     """pa_decode_launches: one launch where the balanced split merges in the
-    decode kernel (at least half as many sequences as workers per KV head),
-    two with the closing merge, four with the shared split's planning."""
+    decode kernel (at least a quarter as many sequences as workers per KV
+    head), two with the closing merge, four with the shared split's
+    planning."""
     W = torch.cuda.get_device_properties(0).multi_processor_count * 4 // 8  # MFMA workers per KV head, 8 KV heads
     f = pb.pa_decode_launches
     bf16 = torch.bfloat16
     assert f(256, 32, 8, 128, 8192, -1, bf16, "auto", True) == (1 if 2 * 256 >= W else 2)
-    assert f(W // 2, 32, 8, 128, 8192, -1, bf16, "auto", False) == 1
-    assert f(W // 2 - 1, 32, 8, 128, 8192, -1, bf16, "auto", True) == 2
+    assert f(W // 4, 32, 8, 128, 8192, -1, bf16, "auto", False) == 1
+    assert f(W // 4 - 1, 32, 8, 128, 8192, -1, bf16, "auto", True) == 2
     assert f(1, 32, 8, 128, 8192, -1, bf16, "auto", False) == 2
     assert f(256, 32, 8, 128, 8192, -2, bf16, "auto", True) == 4                 # shared split
     assert f(256, 32, 8, 128, 8192, -2, torch.float32, "auto", True) == 1        # fp32 runs it as AUTO
     assert f(256, 32, 8, 128, 8192, 512, bf16, "auto", False) == 2               # fixed partitions
     assert f(256, 32, 8, 128, 8192, 0, bf16, "auto", False) == 1                 # no split
     assert f(256, 32, 8, 128, 8192, 0, bf16, "auto", True) == 2                  # no split, fused write
+
+
+def test_in_kernel_merge_cut_and_empty_contexts():
+    """The in-kernel path with max_context_len below the longest contexts
+    (they are cut to it and their new tokens are not stored) and with
+    zero-length contexts (zeros written, nothing stored): 600 sequences."""
+    S, B, cut = 600, 16, 2000
+    lens = mixed_lengths(S, 91)
+    cfg = wl.DecodeConfig("mixed-cut", 91, S, 32, 8, 128, B, "bf16", 0.088,
+                          ("fixed", tuple(int(x) for x in lens)), int(lens.max()))
+    w = wl.make_decode_workload(cfg, lengths=lens)
+    assert (lens > cut).sum() >= 3
+    dv = device_case(w)
+    empty = [5, 77, 300]
+    lens_dev = lens.copy()
+    lens_dev[empty] = 0
+    dv["cl"] = pb.int32_to_device(lens_dev, DEV)
+    need = pb.pa_decode_workspace_bytes(S, 32, 8, 128, cut, -1)
+    assert pb.pa_decode_launches(S, 32, 8, 128, cut, -1, torch.bfloat16, "auto", True) == 1
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    out = torch.full(dv["q"].shape, float("nan"), dtype=torch.float32, device=DEV)
+    pb.pa_write_decode(out, dv["q"], dv["kn"], dv["vn"], dv["kc"], dv["vc"], dv["bt"], dv["cl"], cfg.scale, cut,
+                       workspace=ws)
+    torch.cuda.synchronize()
+    say(f"in-kernel merge: {int((lens > cut).sum())} contexts cut to {cut}, {len(empty)} empty")
+    keep = (lens_dev > 0) & (lens_dev <= cut)
+    kr, vr = oracle.write_kv(w.k_cache, w.v_cache, w.k_new[keep], w.v_new[keep], w.slot_mapping[keep], B)
+    np.testing.assert_array_equal(pb.to_host(dv["kc"], "bf16").view(np.uint16), kr.view(np.uint16))
+    np.testing.assert_array_equal(pb.to_host(dv["vc"], "bf16").view(np.uint16), vr.view(np.uint16))
+    g = out.cpu().numpy()
+    assert (g[empty] == 0).all()
+    seqs = [s for s in range(S) if lens_dev[s] > 0]
+    ref = oracle.decode(w.q, kr, vr, w.block_tables, np.minimum(lens_dev, cut).astype(np.int32), cfg.scale, B,
+                        "bf16", seqs=seqs)
+    check(out, ref, "cut and empty contexts", seqs=seqs)
+    assert int(ws[:pb.WORKSPACE_COUNTER_BYTES].count_nonzero()) == 0
