@@ -2062,7 +2062,7 @@ __device__ void merge_heads_one_wave(const DecodeParams& p, MergeSmem<1>& sm, in
     for (int h = 0; h < kMaxGroup; ++h)
 #pragma unroll
       for (int i = 0; i < PER; ++i)
-        pre[j][h][i] = (h < nh && j < npieces) ? acc0[(size_t)h * D + (size_t)pm.slot(j) * step + 64 * i] : 0.f;
+        pre[j][h][i] = acc0[(size_t)min(h, nh - 1) * D + (size_t)pm.slot(min(j, npieces - 1)) * step + 64 * i];
   // (m, l) of every (head, piece): m into wgt, l kept in the same slot's pair
   for (int i = tid; i < nh * npieces; i += 64) {
     const int h = i / npieces, k = i % npieces;
@@ -2103,15 +2103,32 @@ __device__ void merge_heads_one_wave(const DecodeParams& p, MergeSmem<1>& sm, in
       }
     }
   }
-#pragma unroll 2
-  for (int k = kPre; k < npieces; ++k) {
-    const size_t off = (size_t)pm.slot(k) * step;
+  // the remaining pieces kBatch at a time, every load of a batch
+  // unconditional (past the last piece or head: the last one again) so that
+  // they all go out before the first wait; loads under per-head conditions
+  // were each put behind a vmcnt(0) wait, a round trip per (piece, head)
+  constexpr int kBatch = 4;
+  for (int k0 = kPre; k0 < npieces; k0 += kBatch) {
+    float x[kBatch][kMaxGroup][PER];
 #pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h) {
-      if (h < nh) {
-        const float w = sm.wgt[h][k];
+    for (int b = 0; b < kBatch; ++b) {
+      const size_t off = (size_t)pm.slot(min(k0 + b, npieces - 1)) * step;
 #pragma unroll
-        for (int i = 0; i < PER; ++i) acc[h][i] = fmaf(w, acc0[(size_t)h * D + off + 64 * i], acc[h][i]);
+      for (int h = 0; h < kMaxGroup; ++h)
+#pragma unroll
+        for (int i = 0; i < PER; ++i) x[b][h][i] = acc0[(size_t)min(h, nh - 1) * D + off + 64 * i];
+    }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      if (k0 + b < npieces) {
+#pragma unroll
+        for (int h = 0; h < kMaxGroup; ++h) {
+          if (h < nh) {
+            const float w = sm.wgt[h][k0 + b];
+#pragma unroll
+            for (int i = 0; i < PER; ++i) acc[h][i] = fmaf(w, x[b][h][i], acc[h][i]);
+          }
+        }
       }
     }
   }
