@@ -623,6 +623,11 @@ def prefill_main(args, torch, pb, wl, dev) -> int:
     return 0
 
 
+def pool_name(args) -> str:
+    """How the decode workload's blocks are placed in the pool."""
+    return "reserved" if args.reserved else "contiguous" if args.contiguous else "shuffled"
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -635,6 +640,9 @@ def main() -> int:
     ap.add_argument("--block-size", type=int, default=None, help="tokens per block (default: the workload's)")
     ap.add_argument("--contiguous", action="store_true",
                     help="hand out the pool's blocks in order instead of the seeded shuffled order")
+    ap.add_argument("--reserved", action="store_true",
+                    help="decode: give every sequence a max_len region of its own (logical block i of sequence "
+                         "s at block s * max_blocks + i), the reservation that paging replaces")
     ap.add_argument("--two-calls", action="store_true", help="time pa_write_kv + pa_decode instead of the fused call")
     ap.add_argument("--prefix-len", type=int, default=1024,
                     help="shared_prefix: tokens of the shared prefix (not a multiple of 16: copy-on-write of its "
@@ -666,6 +674,10 @@ def main() -> int:
     from paged_kv_cache_131_amd import workloads as wl
 
     dev = torch.device("cuda:0")
+    if args.contiguous and args.reserved:
+        raise SystemExit("--contiguous and --reserved are two different pool layouts")
+    if args.reserved and args.workload == "prefill":
+        raise SystemExit("--reserved applies to the decode workloads")
     if args.workload == "prefill" and not (args.swap_sweep or args.shape_sweep):
         return prefill_main(args, torch, pb, wl, dev)
     # a drawn workload is generated first and the oracle's baseline timed on
@@ -680,7 +692,7 @@ def main() -> int:
             cfg0 = wl.CONFIGS[args.workload]
             if args.block_size:
                 cfg0 = dataclasses.replace(cfg0, block_size=args.block_size)
-            w0 = wl.make_decode_workload(cfg0, contiguous=args.contiguous)
+            w0 = wl.make_decode_workload(cfg0, contiguous=args.contiguous, reserved=args.reserved)
         gen_s = time.perf_counter() - t0
         if not args.no_cpu_baseline:
             cpu = cpu_baseline(w0, args.cpu_budget)
@@ -691,8 +703,9 @@ def main() -> int:
     if args.shape_sweep:
         print(json.dumps({"shape_sweep": shape_sweep(torch, pb, wl, 50)}), flush=True)
         return 0
-    if args.workload in ("parallel_sampling", "beam_search", "shared_prefix") and (args.block_size or args.contiguous):
-        raise SystemExit("--block-size/--contiguous apply to the drawn-length workloads")
+    if args.workload in ("parallel_sampling", "beam_search", "shared_prefix") and (
+            args.block_size or args.contiguous or args.reserved):
+        raise SystemExit("--block-size/--contiguous/--reserved apply to the drawn-length workloads")
     if args.workload == "parallel_sampling":
         c = loop_case(wl.ParallelSamplingWorkload(prompt_len=1016), 256, pb, dev, torch, max(args.steps, 10))
     elif args.workload == "beam_search":
@@ -778,7 +791,7 @@ def main() -> int:
             "max_context_len": max_len,
             "partition_size": part,
             "block_size": cfg.block_size,
-            "pool": "contiguous" if args.contiguous else "shuffled",
+            "pool": pool_name(args),
             "algo": args.algo,
             "step": ("copy blocks (0 pairs) + fused write 1 token/seq and decode" if fused
                      else "copy blocks (0 pairs) + write 1 token/seq + decode"),

@@ -206,11 +206,17 @@ class DecodeWorkload:
 
 
 def make_decode_workload(cfg: DecodeConfig, lengths=None, poison: bool = True,
-                         values: bool = True, contiguous: bool = False) -> DecodeWorkload:
+                         values: bool = True, contiguous: bool = False, reserved: bool = False) -> DecodeWorkload:
     """Draw one decode step's inputs. With values=False only the integer
     inputs (lengths, block tables, slot mapping) are produced. contiguous=True
     hands the pool's blocks out in order (sequence s's blocks adjacent, after
-    those of s-1) instead of in the seeded shuffled order."""
+    those of s-1) instead of in the seeded shuffled order. reserved=True gives
+    every sequence a region of max_blocks blocks of its own (sequence s's
+    logical block i is block s * max_blocks + i), the maximum-length
+    reservation that paging replaces; the pool then holds num_seqs *
+    max_blocks blocks plus one never handed out."""
+    if contiguous and reserved:
+        raise ValueError("contiguous and reserved are two different layouts")
     seqs = np.random.SeedSequence(1000 + cfg.index).spawn(6)
     rng_len, rng_pool = np.random.default_rng(seqs[0]), np.random.default_rng(seqs[1])
     ss_q, ss_k, ss_v, ss_new = seqs[2:]
@@ -220,22 +226,34 @@ def make_decode_workload(cfg: DecodeConfig, lengths=None, poison: bool = True,
     B = cfg.block_size
     nblk = -(-lens.astype(np.int64) // B)
     need = int(nblk.sum())
-    num_blocks = cfg.pool_blocks if cfg.pool_blocks else math.ceil(1.1 * need)
-    if num_blocks <= need:
-        raise ValueError("pool too small to leave a spare block for poisoned padding")
-    perm = rng_pool.permutation(num_blocks).astype(np.int32)
-    if contiguous:
-        perm = np.arange(num_blocks, dtype=np.int32)
     max_blocks = max(-(-cfg.max_len // B), int(nblk.max()))
-    poison_block = int(perm[need])             # first block never handed out
-    tables = np.full((cfg.num_seqs, max_blocks), poison_block, dtype=np.int32)
-    pos = 0
-    for s in range(cfg.num_seqs):
-        tables[s, :nblk[s]] = perm[pos:pos + nblk[s]]
-        pos += int(nblk[s])
+    if reserved:
+        num_blocks = cfg.num_seqs * max_blocks + 1
+        poison_block = num_blocks - 1
+        tables = np.full((cfg.num_seqs, max_blocks), poison_block, dtype=np.int32)
+        for s in range(cfg.num_seqs):
+            tables[s, :nblk[s]] = s * max_blocks + np.arange(nblk[s], dtype=np.int32)
+        used = np.concatenate([tables[s, :nblk[s]] for s in range(cfg.num_seqs)])
+        handed = np.zeros(num_blocks, dtype=bool)
+        handed[used] = True
+        unused = np.flatnonzero(~handed).astype(np.int32)
+    else:
+        num_blocks = cfg.pool_blocks if cfg.pool_blocks else math.ceil(1.1 * need)
+        if num_blocks <= need:
+            raise ValueError("pool too small to leave a spare block for poisoned padding")
+        perm = rng_pool.permutation(num_blocks).astype(np.int32)
+        if contiguous:
+            perm = np.arange(num_blocks, dtype=np.int32)
+        poison_block = int(perm[need])             # first block never handed out
+        tables = np.full((cfg.num_seqs, max_blocks), poison_block, dtype=np.int32)
+        pos = 0
+        for s in range(cfg.num_seqs):
+            tables[s, :nblk[s]] = perm[pos:pos + nblk[s]]
+            pos += int(nblk[s])
+        used = perm[:need]
+        unused = perm[need:]
 
     Hkv, d = cfg.num_kv_heads, cfg.head_dim
-    used = perm[:need]
     last_pos = lens.astype(np.int64) - 1
     slots = (tables[np.arange(cfg.num_seqs), last_pos // B].astype(np.int64) * B + last_pos % B).astype(np.int32)
     if not values:
@@ -250,7 +268,6 @@ def make_decode_workload(cfg: DecodeConfig, lengths=None, poison: bool = True,
 
     if poison:
         pv = poison_value(cfg.etype)
-        unused = perm[need:]
         k_cache[unused] = pv
         v_cache[unused] = pv
         for s in range(cfg.num_seqs):

@@ -285,6 +285,23 @@ def test_decode_grid(etype, d, B, Hq, Hkv, algo, part):
     check(dv.decode(partition_size=part, algo=algo), ref, TOL[etype], f"{cfg.name} {algo} part={part}")
 
 
+@pytest.mark.parametrize("layout", ["contiguous", "reserved"])
+@pytest.mark.parametrize("B", [16, 64])
+def test_decode_pool_layouts(layout, B):
+    # blocks handed out in order, and a max-length region per sequence (the
+    # reservation paging replaces), against the definition
+    lens = (1, 2, 31, 32, 33, 64, 65, 100, 257, 700)
+    cfg = wl.DecodeConfig(f"layout-{layout}-{B}", 9, len(lens), 32, 8, 128, B, "bf16", 1.0, ("fixed", lens), 768)
+    say(f"pool layout {layout} B={B}")
+    w = wl.make_decode_workload(cfg, **{layout: True})
+    dv = Dev(w)
+    dv.write()
+    kr, vr = host_after_write(w)
+    ref = oracle.decode(w.q, kr, vr, w.block_tables, w.context_lens, cfg.scale, B, "bf16")
+    for part in (-1, 0):
+        check(dv.decode(partition_size=part), ref, TOL["bf16"], f"{cfg.name} part={part}")
+
+
 @pytest.mark.parametrize("B,part", [(8, 32), (16, 32), (32, 32), (64, 64), (128, 128)])
 @pytest.mark.parametrize("algo", ["mfma", "vector"])
 def test_split_partition_of_one_block_or_one_chunk(B, part, algo):

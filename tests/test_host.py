@@ -1,5 +1,6 @@
 """Host logic: block manager, seeded workload generators, rounding helpers. CPU only."""
 
+import dataclasses
 import math
 
 import numpy as np
@@ -121,6 +122,21 @@ def test_tiny_workload_values_and_poison():
     assert np.isnan(w.k_cache[w.poison_block]).all()
     bits = w.k_cache[w.poison_block].view(np.uint32)
     assert (bits == wl.POISON_BITS["f32"]).all()
+
+
+def test_reserved_layout_gives_each_sequence_its_own_region():
+    cfg = dataclasses.replace(wl.CONFIGS["llama3_8b"], num_seqs=6, lengths=("fixed", (1, 16, 17, 40, 100, 128)),
+                              max_len=128, value_scale=1.0)
+    w = wl.make_decode_workload(cfg, reserved=True, values=False)
+    B, mb = cfg.block_size, w.block_tables.shape[1]
+    assert mb == 8 and w.num_blocks == 6 * mb + 1 and w.poison_block == w.num_blocks - 1
+    for s, L in enumerate(w.context_lens):
+        n = -(-int(L) // B)
+        assert list(w.block_tables[s, :n]) == [s * mb + i for i in range(n)]
+        assert (w.block_tables[s, n:] == w.poison_block).all()
+        assert w.slot_mapping[s] == (s * mb + (int(L) - 1) // B) * B + (int(L) - 1) % B
+    with pytest.raises(ValueError):
+        wl.make_decode_workload(cfg, reserved=True, contiguous=True, values=False)
 
 
 def test_bf16_rounding_matches_torch():
