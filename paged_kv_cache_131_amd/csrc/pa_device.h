@@ -48,6 +48,37 @@ __device__ __forceinline__ float sum_over_column(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// x of the lane picked by a DPP control within the lane's row of 16.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// x combined (sum, or max when MAX) over aligned groups of N consecutive
+// lanes, N = 4, 8, 16, 32 or 64; every lane of a group gets the group's value,
+// bit-identical across the group (each step adds the two halves in either
+// order). Within a row of 16: quad_perm [1,0,3,2] and [2,3,0,1] (lane ^ 1,
+// lane ^ 2), row_half_mirror (the other quad of the eight) and row_mirror
+// (the other eight); across rows the lane-swap instructions. No LDS.
+template <int N, bool MAX = false>
+__device__ __forceinline__ float reduce_lanes(float x) {
+  static_assert(N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "group of 4 to 64 lanes");
+  const auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+  x = op(x, dpp_f<0xB1>(x));
+  x = op(x, dpp_f<0x4E>(x));
+  if constexpr (N >= 8) x = op(x, dpp_f<0x141>(x));
+  if constexpr (N >= 16) x = op(x, dpp_f<0x140>(x));
+  if constexpr (N >= 32) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  }
+  if constexpr (N >= 64) {
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = op(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  }
+  return x;
+}
+
 // V tiles are stored as sub-tiles [block_size/Bs][head_dim][Bs]: Bs = 32 for
 // a block_size that is a multiple of 32 above 32, else Bs = block_size (a
 // plain [head_dim][block_size] tile). The element of channel c and in-block

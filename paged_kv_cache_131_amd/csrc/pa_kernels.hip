@@ -525,8 +525,8 @@ struct MfmaEngine {
 // Vector engine (any element type, group bucket G >= g).
 //
 // QK: 16-byte coalesced loads of token rows, LPR lanes per row, partial dot
-// products reduced across those lanes. Softmax over the chunk's 32 scores
-// through LDS. PV: 16-byte loads of VEC consecutive tokens at one dd from the
+// products reduced across those lanes by DPP moves. Softmax over the chunk's
+// 32 scores through LDS (its maximum by DPP moves and lane swaps). PV: 16-byte loads of VEC consecutive tokens at one dd from the
 // token-minor V tile, fp32 FMAs, accumulators reduced across lanes at the end.
 // ---------------------------------------------------------------------------
 template <int E, int D, int G>
@@ -650,8 +650,7 @@ struct VecEngine {
         float d = 0.f;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) d = fmaf(qv[h][e], kf[e], d);
-#pragma unroll
-        for (int off = LPR / 2; off >= 1; off >>= 1) d += __shfl_xor(d, off);
+        d = reduce_lanes<LPR>(d);
         if (piece == 0) sm.sc[h][st * RPS + lane / LPR] = d;
       }
     }
@@ -665,9 +664,7 @@ struct VecEngine {
     for (int h = 0; h < G; ++h) {
       const bool valid = lane < kChunk && cs + lane < t1;
       const float sv = valid ? sm.sc[h][lane] * p.scale_log2 : kNegInf;
-      float cmax = sv;
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) cmax = fmaxf(cmax, __shfl_xor(cmax, off));
+      const float cmax = reduce_lanes<64, true>(sv);
       const float m_new = fmaxf(m_run[h], cmax);
       alpha[h] = fast_exp2(m_run[h] - m_new);
       const float pv = fast_exp2(sv - m_new);
@@ -709,14 +706,10 @@ struct VecEngine {
     for (int h = 0; h < G; ++h) {
 #pragma unroll
       for (int st = 0; st < VSTEPS; ++st) {
-        float v = acc[h][st];
-#pragma unroll
-        for (int off = LPD / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+        const float v = reduce_lanes<LPD>(acc[h][st]);
         if (tg == 0) sm.o[h][st * DPS + ddl] = v;
       }
-      float l = l_run[h];
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
+      const float l = reduce_lanes<64>(l_run[h]);
       if (lane == 0) {
         sm.ml[h][0] = m_run[h];
         sm.ml[h][1] = l;
