@@ -17,6 +17,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_inff();
@@ -135,6 +136,19 @@ struct ElemT<kF16> {
     }
     return w;
   }
+  // c + the dot product of the 8 elements of a and b: four two-element dot
+  // instructions (16-bit products are exact in fp32, accumulated in fp32).
+  // Each pair is copied out of the vector before the bit cast: a bit cast
+  // of the subscripted element itself was compiled as a cast of element 0
+  // for every i (hipcc of ROCm 7.2).
+  __device__ static float dot8(u32x4 a, u32x4 b, float c) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t x = a[i], y = b[i];
+      c = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x), __builtin_bit_cast(f16x2, y), c, false);
+    }
+    return c;
+  }
   // p = hi + lo: hi the nearest 16-bit values, lo the residuals rounded
   __device__ static void split(const float* p, op8& hi, op8& lo) {
 #pragma unroll
@@ -160,6 +174,15 @@ struct ElemT<kBF16> {
     }
   }
   __device__ static u32x4 keep_first(u32x4 w, int nvalid) { return ElemT<kF16>::keep_first(w, nvalid); }
+  // as ElemT<kF16>::dot8
+  __device__ static float dot8(u32x4 a, u32x4 b, float c) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t x = a[i], y = b[i];
+      c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, y), c, false);
+    }
+    return c;
+  }
   // p = hi + lo: hi the nearest bf16 values (one packed conversion per pair,
   // unpacked by shifts), lo the residuals rounded
   __device__ static void split(const float* p, op8& hi, op8& lo) {

@@ -524,37 +524,58 @@ struct MfmaEngine {
 // ---------------------------------------------------------------------------
 // Vector engine (any element type, group bucket G >= g).
 //
-// QK: 16-byte coalesced loads of token rows, LPR lanes per row, partial dot
-// products reduced across those lanes by DPP moves. Softmax over the chunk's
-// 32 scores through LDS (its maximum by DPP moves and lane swaps). PV: 16-byte loads of VEC consecutive tokens at one dd from the
-// token-minor V tile, fp32 FMAs, accumulators reduced across lanes at the end.
+// QK: 16-byte coalesced loads of token rows, LPR lanes per row (a K group),
+// partial dot products (two-element dot instructions on 16-bit elements, fp32
+// FMAs on fp32 ones) reduced across those lanes by DPP moves, so that every
+// lane of K group q holds the scores of its tokens q*KSTEPS .. +KSTEPS-1.
+// PV: 16-byte loads of VEC consecutive tokens at one dd from the token-minor
+// V tile, taken from the lane's own K group's tokens, so the lane forms their
+// weights itself; the chunk maximum crosses the groups by lane swaps. No LDS
+// inside the chunk loop; accumulators are reduced across lanes at the end.
 // ---------------------------------------------------------------------------
 template <int E, int D, int G>
 struct VecEngine {
   using Tr = ElemT<E>;
   using raw = typename Tr::raw;
   static constexpr int VEC = Tr::kVec;
-  static constexpr int LPR = D / VEC;           // lanes per K row
-  static constexpr int RPS = 64 / LPR;          // K rows per load step
-  static constexpr int KSTEPS = kChunk / RPS;   // K load steps per chunk
-  static constexpr int LPD = kChunk / VEC;      // lanes per V dd-row of a chunk
-  static constexpr int DPS = 64 / LPD;          // dd rows per V load step
+  static constexpr int LPR = D / VEC;           // lanes per K row (one K group)
+  static constexpr int RPS = 64 / LPR;          // K groups: rows per load step
+  static constexpr int KSTEPS = kChunk / RPS;   // K load steps per chunk = tokens per K group
+  // A V lane takes VEC consecutive tokens of its own K group (NTG token
+  // groups per K group), or, when a K group holds fewer than VEC tokens
+  // (16-bit elements, head_dim 64), of two neighbouring K groups (kPair).
+  static constexpr bool kPair = KSTEPS < VEC;
+  static constexpr int NTG = kPair ? 1 : KSTEPS / VEC;
+  static constexpr int VLANES = kPair ? 2 * LPR : LPR;  // lanes of one V group
+  static constexpr int DPS = VLANES / NTG;      // dd rows per V load step
   static constexpr int VSTEPS = D / DPS;        // V load steps per chunk
+  static_assert(kPair ? (VLANES == 16 && KSTEPS * 2 == VEC) : (KSTEPS % VEC == 0), "lane layout");
+  // QK by two-element dot instructions (16-bit elements), except bf16 with
+  // one query head per KV head, where widening is two bit operations per
+  // pair and FMAs measured faster (OPT-13B shape 205.8 vs 209.8 us); fp16
+  // widening takes a conversion per element (209.3 vs 211.1 us with dot2)
+  static constexpr bool kDot = E == kF16 || (E == kBF16 && G > 1);
   static constexpr int kSub = 1;
   static constexpr int kGroups = 1;
   static constexpr int kMaxGroup = G;
   struct alignas(16) Smem {
-    float sc[G][kChunk];
-    float pl[G][kChunk];
     float o[G][D];
     float ml[G][2];
   };
 
-  float qv[G][VEC];
+  u32x4 qr[G];  // this lane's piece of q, as stored
   float acc[G][VSTEPS];
   float m_run[G];
   float l_run[G];
-  uint32_t vn[VSTEPS];  // the segment's new token's V at this lane's rows st*DPS + lane/LPD
+  uint32_t vn[VSTEPS];  // the segment's new token's V at this lane's dd rows
+
+  // lane roles: K group kq (token rows kq * KSTEPS + st), piece of the row;
+  // V group, its first token (relative to the chunk) and the lane's dd row
+  __device__ static int kq(int lane) { return lane / LPR; }
+  __device__ static int v_tok(int lane) {
+    return kPair ? (lane / VLANES) * VEC : kq(lane) * KSTEPS + (lane % LPR) % NTG * VEC;
+  }
+  __device__ static int v_row(int lane) { return kPair ? lane % VLANES : (lane % LPR) / NTG; }
 
   struct Q {
     u32x4 w[G];
@@ -574,7 +595,7 @@ struct VecEngine {
     // read unconditionally (from q when the call brings no new token: an
     // in-bounds row, never used) so every segment issues the same loads
     const raw* vb = static_cast<const raw*>(p.v_new ? p.v_new : p.q) + ((size_t)s * p.num_kv_heads + kvh) * D +
-                    lane / LPD;
+                    v_row(lane);
 #pragma unroll
     for (int st = 0; st < VSTEPS; ++st) q.vn[st] = vb[st * DPS];
   }
@@ -582,7 +603,7 @@ struct VecEngine {
   __device__ void reset(const Q& q, const DecodeParams&, const Segment&, int, int, Smem&) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      Tr::widen(q.w[h], qv[h]);
+      qr[h] = q.w[h];
 #pragma unroll
       for (int st = 0; st < VSTEPS; ++st) acc[h][st] = 0.f;
       m_run[h] = kNegInf;
@@ -608,7 +629,7 @@ struct VecEngine {
     const raw* kn = static_cast<const raw*>(p.k_new) + ((size_t)g.s * Hkv + kvh) * D + piece * VEC;
 #pragma unroll
     for (int st = 0; st < KSTEPS; ++st) {
-      const int tok = cs + st * RPS + lane / LPR;
+      const int tok = cs + kq(lane) * KSTEPS + st;
       const int phys = pick_block(ids, tok, lg, g.lbl, p.num_blocks);
       const raw* row = kc + (((size_t)phys * Hkv + kvh) * B + (tok & (B - 1))) * D + piece * VEC;
       f.kr[st] = load16_stream(tok == g.tnew ? kn : row);
@@ -621,66 +642,89 @@ struct VecEngine {
     const ChunkIds ids = idp[0];
     const int B = p.block_size, lg = p.log2_block, Hkv = p.num_kv_heads;
     const raw* __restrict__ vc = static_cast<const raw*>(p.v_cache);
-    const int tg = lane % LPD, ddl = lane / LPD;
-    const int tv = cs + tg * VEC;
+    const int tv = cs + v_tok(lane);
     const int physv = pick_block(ids, tv, lg, lbl, p.num_blocks);
     const int Bs = v_subtile(B);
-    const raw* vb = vc + v_elem(physv, Hkv, kvh, D, B, Bs, ddl, tv & (B - 1));
+    const raw* vb = vc + v_elem(physv, Hkv, kvh, D, B, Bs, v_row(lane), tv & (B - 1));
 #pragma unroll
     for (int st = 0; st < VSTEPS; ++st) f.vr[st] = load16_stream(vb + (size_t)st * DPS * Bs);
   }
 
   // REFILL false: the stream's last step, which loads nothing.
+  // Every lane of K group kq ends QK with the scores of that group's KSTEPS
+  // tokens; the chunk maximum combines the groups by lane swaps, and the P of
+  // a lane's own VEC V tokens is formed where it is used: no LDS round trip.
   template <bool REFILL>
-  __device__ __forceinline__ void step(Frag& f, const DecodeParams& p, Smem& sm, int kvh, int lane, int cs,
+  __device__ __forceinline__ void step(Frag& f, const DecodeParams& p, Smem&, int kvh, int lane, int cs,
                                        const Segment& cur, int cs_next, const ChunkIds* ids_next, const Segment& nxt) {
     const int t1 = cur.t1;
     const bool has_new = cur.tnew >= cs && cur.tnew < cs + kChunk;
-    const int piece = lane % LPR;
-    const int tg = lane % LPD;
-    const int tv = cs + tg * VEC;
+    const int k0 = cs + kq(lane) * KSTEPS;  // this lane's first K token
+    const int tv = cs + v_tok(lane);        // this lane's first V token
 
-    // QK
+    // QK of every head; then the refill of K, whose registers are free
+    float sv[G][KSTEPS];
 #pragma unroll
-    for (int st = 0; st < KSTEPS; ++st) {
-      float kf[VEC];
-      Tr::widen(f.kr[st], kf);
+    for (int h = 0; h < G; ++h) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
+      for (int st = 0; st < KSTEPS; ++st) {
         float d = 0.f;
+        if constexpr (kDot) {
+          d = Tr::dot8(qr[h], f.kr[st], d);
+        } else {
+          float qf[VEC], kf[VEC];
+          Tr::widen(qr[h], qf);
+          Tr::widen(f.kr[st], kf);
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) d = fmaf(qv[h][e], kf[e], d);
+          for (int e = 0; e < VEC; ++e) d = fmaf(qf[e], kf[e], d);
+        }
         d = reduce_lanes<LPR>(d);
-        if (piece == 0) sm.sc[h][st * RPS + lane / LPR] = d;
+        sv[h][st] = k0 + st < t1 ? d * p.scale_log2 : kNegInf;
       }
     }
     if (REFILL) load_k(f, p, kvh, lane, cs_next, ids_next, nxt);
-    __syncthreads();
 
-    // softmax over the chunk's 32 tokens
-    const bool partial = cs + kChunk > t1;
+    // the chunk maximum and P of the lane's V tokens, head by head
+    float pw[G][VEC];
     float alpha[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const bool valid = lane < kChunk && cs + lane < t1;
-      const float sv = valid ? sm.sc[h][lane] * p.scale_log2 : kNegInf;
-      const float cmax = reduce_lanes<64, true>(sv);
+      float cmax = sv[h][0];
+#pragma unroll
+      for (int st = 1; st < KSTEPS; ++st) cmax = fmaxf(cmax, sv[h][st]);
+      cmax = reduce_groups<true>(cmax);
       const float m_new = fmaxf(m_run[h], cmax);
       alpha[h] = fast_exp2(m_run[h] - m_new);
-      const float pv = fast_exp2(sv - m_new);
-      l_run[h] = l_run[h] * alpha[h] + pv;
       m_run[h] = m_new;
-      if (lane < kChunk) sm.pl[h][lane] = pv;
+      float psum = 0.f;
+      if constexpr (kPair) {
+        // tokens 0..KSTEPS-1 of the pair are the even group's, the rest the
+        // odd group's: the other group's scores come from lane ^ 8
+        const bool odd = (lane & 8) != 0;
+#pragma unroll
+        for (int e = 0; e < KSTEPS; ++e) {
+          const float other = dpp_f<0x128>(sv[h][e]);  // row_ror:8
+          pw[h][e] = fast_exp2((odd ? other : sv[h][e]) - m_new);
+          pw[h][KSTEPS + e] = fast_exp2((odd ? sv[h][e] : other) - m_new);
+        }
+      } else {
+        const int base = (lane % LPR) % NTG * VEC;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          float x = sv[h][e];
+#pragma unroll
+          for (int k = 1; k < NTG; ++k) x = base == k * VEC ? sv[h][k * VEC + e] : x;
+          pw[h][e] = fast_exp2(x - m_new);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) psum += pw[h][e];
+      l_run[h] = l_run[h] * alpha[h] + psum;
     }
-    __syncthreads();
 
     // PV
+    const bool partial = cs + kChunk > t1;
     const int enew = has_new && cur.tnew >= tv && cur.tnew < tv + VEC ? cur.tnew - tv : -1;
-    float pw[G][VEC];
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) pw[h][e] = sm.pl[h][tg * VEC + e];
 #pragma unroll
     for (int st = 0; st < VSTEPS; ++st) {
       u32x4 w = f.vr[st];
@@ -697,19 +741,45 @@ struct VecEngine {
       }
     }
     if (REFILL) load_v(f, p, kvh, lane, cs_next, ids_next, nxt);
-    __syncthreads();  // sc/pl are rewritten by the next chunk
+  }
+
+  // x combined over the K groups (lanes l, l + LPR, ...): the two groups of a
+  // row of 16 by a rotation of 8, then rows by lane swaps
+  template <bool MAX>
+  __device__ static float reduce_groups(float x) {
+    const auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+    if constexpr (LPR <= 8) x = op(x, dpp_f<0x128>(x));
+    if constexpr (LPR <= 16) {
+      const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+      x = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    }
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return op(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  }
+
+  // x summed over the lanes sharing this lane's dd row (all V groups and
+  // token groups): every chunk token once
+  __device__ static float sum_over_row(float x) {
+    if constexpr (NTG >= 2) x += dpp_f<0xB1>(x);
+    if constexpr (NTG >= 4) x += dpp_f<0x4E>(x);
+    if constexpr (VLANES <= 16) {
+      const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+      x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    }
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
   }
 
   __device__ void finish(Smem& sm, int lane, int) {
-    const int tg = lane % LPD, ddl = lane / LPD;
+    const bool writer = lane < VLANES && (kPair || (lane % LPR) % NTG == 0);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
 #pragma unroll
       for (int st = 0; st < VSTEPS; ++st) {
-        const float v = reduce_lanes<LPD>(acc[h][st]);
-        if (tg == 0) sm.o[h][st * DPS + ddl] = v;
+        const float v = sum_over_row(acc[h][st]);
+        if (writer) sm.o[h][st * DPS + v_row(lane)] = v;
       }
-      const float l = reduce_lanes<64>(l_run[h]);
+      const float l = sum_over_row(l_run[h]);
       if (lane == 0) {
         sm.ml[h][0] = m_run[h];
         sm.ml[h][1] = l;
