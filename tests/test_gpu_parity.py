@@ -248,6 +248,7 @@ GRID = [
     ("bf16", 128, 16, 32, 8, "mfma", 0),
     ("bf16", 128, 16, 32, 8, "mfma", 64),
     ("f16", 128, 16, 8, 8, "vector", -1),
+    ("bf16", 128, 16, 8, 8, "vector", -1),    # g = 1 bf16: the vector engine's FMA form of QK
     ("f16", 128, 16, 8, 8, "mfma", -1),
     ("f16", 128, 16, 16, 2, "mfma", 32),
     ("bf16", 64, 8, 12, 4, "mfma", -1),       # g = 3
