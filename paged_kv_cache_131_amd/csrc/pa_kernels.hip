@@ -528,8 +528,9 @@ struct MfmaEngine {
 // partial dot products (two-element dot instructions on 16-bit elements, fp32
 // FMAs on fp32 ones) reduced across those lanes by DPP moves, so that every
 // lane of K group q holds the scores of its tokens q*KSTEPS .. +KSTEPS-1.
-// PV: 16-byte loads of VEC consecutive tokens at one dd from the token-minor
-// V tile, taken from the lane's own K group's tokens, so the lane forms their
+// PV: 8 consecutive tokens at one dd per lane (one 16-byte load of 16-bit
+// elements, two of fp32) from the token-minor V tile, taken from the lane's
+// own K group's tokens, so the lane forms their
 // weights itself; the chunk maximum crosses the groups by lane swaps. No LDS
 // inside the chunk loop; accumulators are reduced across lanes at the end.
 // ---------------------------------------------------------------------------
@@ -541,20 +542,30 @@ struct VecEngine {
   static constexpr int LPR = D / VEC;           // lanes per K row (one K group)
   static constexpr int RPS = 64 / LPR;          // K groups: rows per load step
   static constexpr int KSTEPS = kChunk / RPS;   // K load steps per chunk = tokens per K group
-  // A V lane takes VEC consecutive tokens of its own K group (NTG token
-  // groups per K group), or, when a K group holds fewer than VEC tokens
+  // A V lane takes TV = 8 consecutive tokens (VPL 16-byte loads per dd row;
+  // always inside one row of the token-minor V tile) of its own K group (NTG
+  // token groups per K group), or, when a K group holds fewer than TV tokens
   // (16-bit elements, head_dim 64), of two neighbouring K groups (kPair).
-  static constexpr bool kPair = KSTEPS < VEC;
-  static constexpr int NTG = kPair ? 1 : KSTEPS / VEC;
+  // Eight tokens rather than one load's worth for fp32: half the partial
+  // sums per lane (fp32, head_dim 128, four heads: 482 registers and no
+  // spill, against 512 and 116 bytes of scratch).
+  static constexpr int TV = 8;
+  static constexpr int VPL = TV / VEC;
+  static constexpr bool kPair = KSTEPS < TV;
+  static constexpr int NTG = kPair ? 1 : KSTEPS / TV;
   static constexpr int VLANES = kPair ? 2 * LPR : LPR;  // lanes of one V group
   static constexpr int DPS = VLANES / NTG;      // dd rows per V load step
   static constexpr int VSTEPS = D / DPS;        // V load steps per chunk
-  static_assert(kPair ? (VLANES == 16 && KSTEPS * 2 == VEC) : (KSTEPS % VEC == 0), "lane layout");
+  static_assert(kPair ? (VLANES == 16 && KSTEPS * 2 == TV) : (KSTEPS % TV == 0), "lane layout");
   // QK by two-element dot instructions (16-bit elements), except bf16 with
   // one query head per KV head, where widening is two bit operations per
   // pair and FMAs measured faster (OPT-13B shape 205.8 vs 209.8 us); fp16
   // widening takes a conversion per element (209.3 vs 211.1 us with dot2)
   static constexpr bool kDot = E == kF16 || (E == kBF16 && G > 1);
+  // Scores of every head held at once (the K refill issued before the
+  // softmax) unless they take more than 64 registers (fp32, head_dim 128,
+  // eight heads: spilled 728 bytes per lane); then head by head.
+  static constexpr bool kPerHead = G * KSTEPS > 64;
   static constexpr int kSub = 1;
   static constexpr int kGroups = 1;
   static constexpr int kMaxGroup = G;
@@ -573,7 +584,7 @@ struct VecEngine {
   // V group, its first token (relative to the chunk) and the lane's dd row
   __device__ static int kq(int lane) { return lane / LPR; }
   __device__ static int v_tok(int lane) {
-    return kPair ? (lane / VLANES) * VEC : kq(lane) * KSTEPS + (lane % LPR) % NTG * VEC;
+    return kPair ? (lane / VLANES) * TV : kq(lane) * KSTEPS + (lane % LPR) % NTG * TV;
   }
   __device__ static int v_row(int lane) { return kPair ? lane % VLANES : (lane % LPR) / NTG; }
 
@@ -615,7 +626,7 @@ struct VecEngine {
 
   struct Frag {
     u32x4 kr[KSTEPS];
-    u32x4 vr[VSTEPS];
+    u32x4 vr[VSTEPS][VPL];
   };
 
   // The row of the segment's new token (g.tnew) comes from the caller's
@@ -647,13 +658,73 @@ struct VecEngine {
     const int Bs = v_subtile(B);
     const raw* vb = vc + v_elem(physv, Hkv, kvh, D, B, Bs, v_row(lane), tv & (B - 1));
 #pragma unroll
-    for (int st = 0; st < VSTEPS; ++st) f.vr[st] = load16_stream(vb + (size_t)st * DPS * Bs);
+    for (int st = 0; st < VSTEPS; ++st)
+#pragma unroll
+      for (int u = 0; u < VPL; ++u) f.vr[st][u] = load16_stream(vb + (size_t)st * DPS * Bs + u * VEC);
+  }
+
+  // Scores (log2 units, -inf past t1) of head h for this lane's K group's
+  // KSTEPS tokens, k0 the group's first.
+  __device__ __forceinline__ void qk_head(const Frag& f, const DecodeParams& p, int h, int k0, int t1,
+                                          float (&sv)[KSTEPS]) const {
+#pragma unroll
+    for (int st = 0; st < KSTEPS; ++st) {
+      float d = 0.f;
+      if constexpr (kDot) {
+        d = Tr::dot8(qr[h], f.kr[st], d);
+      } else {
+        float qf[VEC], kf[VEC];
+        Tr::widen(qr[h], qf);
+        Tr::widen(f.kr[st], kf);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) d = fmaf(qf[e], kf[e], d);
+      }
+      d = reduce_lanes<LPR>(d);
+      sv[st] = k0 + st < t1 ? d * p.scale_log2 : kNegInf;
+    }
+  }
+
+  // The chunk maximum of head h across the K groups, its rescale factor, and
+  // P of the lane's TV V tokens; m and l of the head move on.
+  __device__ __forceinline__ void softmax_head(int h, int lane, const float (&sv)[KSTEPS], float (&pw)[TV],
+                                               float& alpha) {
+    float cmax = sv[0];
+#pragma unroll
+    for (int st = 1; st < KSTEPS; ++st) cmax = fmaxf(cmax, sv[st]);
+    cmax = reduce_groups<true>(cmax);
+    const float m_new = fmaxf(m_run[h], cmax);
+    alpha = fast_exp2(m_run[h] - m_new);
+    m_run[h] = m_new;
+    if constexpr (kPair) {
+      // tokens 0..KSTEPS-1 of the pair are the even group's, the rest the
+      // odd group's: the other group's scores come from lane ^ 8
+      const bool odd = (lane & 8) != 0;
+#pragma unroll
+      for (int e = 0; e < KSTEPS; ++e) {
+        const float other = dpp_f<0x128>(sv[e]);  // row_ror:8
+        pw[e] = fast_exp2((odd ? other : sv[e]) - m_new);
+        pw[KSTEPS + e] = fast_exp2((odd ? sv[e] : other) - m_new);
+      }
+    } else {
+      const int base = (lane % LPR) % NTG * TV;
+#pragma unroll
+      for (int e = 0; e < TV; ++e) {
+        float x = sv[e];
+#pragma unroll
+        for (int k = 1; k < NTG; ++k) x = base == k * TV ? sv[k * TV + e] : x;
+        pw[e] = fast_exp2(x - m_new);
+      }
+    }
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < TV; ++e) psum += pw[e];
+    l_run[h] = l_run[h] * alpha + psum;
   }
 
   // REFILL false: the stream's last step, which loads nothing.
   // Every lane of K group kq ends QK with the scores of that group's KSTEPS
   // tokens; the chunk maximum combines the groups by lane swaps, and the P of
-  // a lane's own VEC V tokens is formed where it is used: no LDS round trip.
+  // a lane's own TV V tokens is formed where it is used: no LDS round trip.
   template <bool REFILL>
   __device__ __forceinline__ void step(Frag& f, const DecodeParams& p, Smem&, int kvh, int lane, int cs,
                                        const Segment& cur, int cs_next, const ChunkIds* ids_next, const Segment& nxt) {
@@ -662,83 +733,53 @@ struct VecEngine {
     const int k0 = cs + kq(lane) * KSTEPS;  // this lane's first K token
     const int tv = cs + v_tok(lane);        // this lane's first V token
 
-    // QK of every head; then the refill of K, whose registers are free
-    float sv[G][KSTEPS];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-#pragma unroll
-      for (int st = 0; st < KSTEPS; ++st) {
-        float d = 0.f;
-        if constexpr (kDot) {
-          d = Tr::dot8(qr[h], f.kr[st], d);
-        } else {
-          float qf[VEC], kf[VEC];
-          Tr::widen(qr[h], qf);
-          Tr::widen(f.kr[st], kf);
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) d = fmaf(qf[e], kf[e], d);
-        }
-        d = reduce_lanes<LPR>(d);
-        sv[h][st] = k0 + st < t1 ? d * p.scale_log2 : kNegInf;
-      }
-    }
-    if (REFILL) load_k(f, p, kvh, lane, cs_next, ids_next, nxt);
-
-    // the chunk maximum and P of the lane's V tokens, head by head
-    float pw[G][VEC];
+    float pw[G][TV];
     float alpha[G];
+    if constexpr (kPerHead) {
+      // QK and P head by head, then the refill of K
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float cmax = sv[h][0];
-#pragma unroll
-      for (int st = 1; st < KSTEPS; ++st) cmax = fmaxf(cmax, sv[h][st]);
-      cmax = reduce_groups<true>(cmax);
-      const float m_new = fmaxf(m_run[h], cmax);
-      alpha[h] = fast_exp2(m_run[h] - m_new);
-      m_run[h] = m_new;
-      float psum = 0.f;
-      if constexpr (kPair) {
-        // tokens 0..KSTEPS-1 of the pair are the even group's, the rest the
-        // odd group's: the other group's scores come from lane ^ 8
-        const bool odd = (lane & 8) != 0;
-#pragma unroll
-        for (int e = 0; e < KSTEPS; ++e) {
-          const float other = dpp_f<0x128>(sv[h][e]);  // row_ror:8
-          pw[h][e] = fast_exp2((odd ? other : sv[h][e]) - m_new);
-          pw[h][KSTEPS + e] = fast_exp2((odd ? sv[h][e] : other) - m_new);
-        }
-      } else {
-        const int base = (lane % LPR) % NTG * VEC;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          float x = sv[h][e];
-#pragma unroll
-          for (int k = 1; k < NTG; ++k) x = base == k * VEC ? sv[h][k * VEC + e] : x;
-          pw[h][e] = fast_exp2(x - m_new);
-        }
+      for (int h = 0; h < G; ++h) {
+        float sv[KSTEPS];
+        qk_head(f, p, h, k0, t1, sv);
+        softmax_head(h, lane, sv, pw[h], alpha[h]);
       }
+      if (REFILL) load_k(f, p, kvh, lane, cs_next, ids_next, nxt);
+    } else {
+      // QK of every head; then the refill of K, whose registers are free;
+      // then the chunk maximum and P of the lane's V tokens, head by head
+      float sv[G][KSTEPS];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) psum += pw[h][e];
-      l_run[h] = l_run[h] * alpha[h] + psum;
+      for (int h = 0; h < G; ++h) qk_head(f, p, h, k0, t1, sv[h]);
+      if (REFILL) load_k(f, p, kvh, lane, cs_next, ids_next, nxt);
+#pragma unroll
+      for (int h = 0; h < G; ++h) softmax_head(h, lane, sv[h], pw[h], alpha[h]);
     }
 
     // PV
     const bool partial = cs + kChunk > t1;
-    const int enew = has_new && cur.tnew >= tv && cur.tnew < tv + VEC ? cur.tnew - tv : -1;
+    const int enew = has_new && cur.tnew >= tv && cur.tnew < tv + TV ? cur.tnew - tv : -1;
 #pragma unroll
     for (int st = 0; st < VSTEPS; ++st) {
-      u32x4 w = f.vr[st];
-      if (partial) w = Tr::keep_first(w, t1 - tv);
-      if (has_new) w = put_elem<raw>(w, enew, vn[st]);  // the new token's V, not its slot's old value
-      float vf[VEC];
-      Tr::widen(w, vf);
+      float a[G];
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float a = acc[h][st] * alpha[h];
+      for (int h = 0; h < G; ++h) a[h] = acc[h][st] * alpha[h];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) a = fmaf(pw[h][e], vf[e], a);
-        acc[h][st] = a;
+      for (int u = 0; u < VPL; ++u) {
+        u32x4 w = f.vr[st][u];
+        if (partial) w = Tr::keep_first(w, t1 - tv - u * VEC);
+        if (has_new) {  // the new token's V, not its slot's old value
+          const int en = enew >= u * VEC && enew < (u + 1) * VEC ? enew - u * VEC : -1;
+          w = put_elem<raw>(w, en, vn[st]);
+        }
+        float vf[VEC];
+        Tr::widen(w, vf);
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) a[h] = fmaf(pw[h][u * VEC + e], vf[e], a[h]);
       }
+#pragma unroll
+      for (int h = 0; h < G; ++h) acc[h][st] = a[h];
     }
     if (REFILL) load_v(f, p, kvh, lane, cs_next, ids_next, nxt);
   }
