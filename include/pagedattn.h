@@ -206,9 +206,11 @@ pa_status pa_decode_ex(void* out, const void* q, const void* k_cache, const void
  * are bit-identical to that pair of calls ([notes-zh] §5.3: the new token's
  * KV goes into the last logical block, then attention reads the blocks).
  * The attention kernel takes position L-1 from k_new/v_new and never uses
- * what the slot holds, so the store may overlap it: under
- * PA_PARTITION_AUTO the decode kernel stores the new tokens itself, in the
- * other modes the launch after it (which also merges split sequences) does.
+ * what the slot holds, so the store may overlap it: the decode kernel
+ * stores the new tokens itself under PA_PARTITION_SHARED and when the
+ * balanced split merges inside it (at least a quarter as many sequences as
+ * workers per KV head); otherwise the launch after it (which also merges
+ * split sequences) does.
  * The block of position L-1 must not be shared with another sequence of the
  * call (copy-on-write has already made it private, [notes-zh] §6.1). No
  * write is made for a sequence with L <= 0, with L beyond

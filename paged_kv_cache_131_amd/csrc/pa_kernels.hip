@@ -1455,7 +1455,9 @@ struct NewTokens {
 
   // s0 < num_seqs and max_blocks_per_seq >= 1. Every load unconditional
   // (for a sequence without a write: an in-bounds row, unused), so that they
-  // all go out before the first wait.
+  // all go out before the first wait. LDS_LENS: the lengths are in LDS (the
+  // balanced split's copy), else read from memory.
+  template <bool LDS_LENS = true>
   __device__ void load(const DecodeParams& p, int s0, int W, int kvh, int lane) {
     const int S = p.num_seqs, Hkv = p.num_kv_heads;
     const U* kn = static_cast<const U*>(p.k_new);
@@ -1465,7 +1467,7 @@ struct NewTokens {
     for (int i = 0; i < kBatch; ++i) {
       const int s = s0 + i * W;
       const int sc = min(s, S - 1);
-      const int L = lds_len(sc);
+      const int L = LDS_LENS ? lds_len(sc) : len_uniform(p, sc);
       const bool ok = s < S && L > 0 && capped_len(p, L) == L;
       const int t = ok ? L - 1 : 0;
       const int ph = tables[(size_t)sc * p.max_blocks_per_seq + (t >> p.log2_block)];
@@ -1498,6 +1500,22 @@ struct NewTokens {
     }
   }
 };
+
+// The new tokens of sequences w, w + W, ... for KV head kvh, stored by
+// worker w of the family kernel when its stream has ended (or at once when
+// it has none). The attention takes position L-1 from k_new/v_new and never
+// reads the slot, so the stores may overlap other workers' reads of the
+// same blocks; they are the last thing a worker does, after its results.
+template <class Eng, int D>
+__device__ __forceinline__ void store_new_tokens(const DecodeParams& p, int w, int W, int kvh, int lane) {
+  using NT = NewTokens<typename Eng::raw, D>;
+  if (p.k_new == nullptr || p.max_blocks_per_seq <= 0) return;
+  for (int s0 = w; s0 < p.num_seqs; s0 += NT::kBatch * W) {
+    NT nt;
+    nt.template load<false>(p, s0, W, kvh, lane);
+    nt.store(p, kvh, lane);
+  }
+}
 
 // End of a balanced-split worker whose launch merges itself. The buffered
 // results are stored (the pieces with agent-scope stores, so nothing of them
@@ -1577,7 +1595,11 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
       if (capped_len(p, len_uniform(p, s)) <= 0) write_zero_rows<Eng, D>(p, s, kvh, lane);
     const const_i32* wr = (const const_i32*)p.wrec + (size_t)w * kWorkerInts;
     const int start = wr[0], end = wr[1], first = wr[2], T = wr[3];
-    if (p.mode != kModeShared || start >= end) return;
+    if (p.mode != kModeShared) return;
+    if (start >= end) {
+      store_new_tokens<Eng, D>(p, w, W, kvh, lane);
+      return;
+    }
     src.s = first;
     src.c = start;
     src.k = 0;
@@ -1591,6 +1613,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
     src.fixed = invalid_segment();
     ResultBuf rb = result_buffer(p, D);
     run_stream<Eng, D>(p, sm, src, kvh, lane, rb);
+    store_new_tokens<Eng, D>(p, w, W, kvh, lane);
     return;
   } else {
   if (p.mode == kModeFixed) {
@@ -2291,11 +2314,11 @@ __device__ __forceinline__ int new_token_slot(const DecodeParams& p, int s, int 
 
 // The launch after the attention kernel: workgroups of W waves, grid
 // (sequences, KV heads, head split Z) with g / Z query heads each. It merges
-// the sequence's pieces when it was split and, for pa_write_decode, the
-// z = 0 workgroup stores the new token into the cache. That store follows
-// every read of the cache by the attention kernel, which took the new token
-// from k_new/v_new; its values are read first and stored last, so its round
-// trips overlap the merge's.
+// the sequence's pieces when it was split and, for pa_write_decode outside
+// the shared mode (whose decode kernel stores them), the z = 0 workgroup
+// stores the new token into the cache. The attention kernel took the new
+// token from k_new/v_new; its values are read first and stored last, so
+// their round trips overlap the merge's.
 template <int D, typename U, int W, bool SHARED>
 __global__ __launch_bounds__(64 * W) void merge_kernel(DecodeParams p) {
   __shared__ MergeSmem<W> sm;
@@ -2318,8 +2341,8 @@ __global__ __launch_bounds__(64 * W) void merge_kernel(DecodeParams p) {
   // (from q without one: an in-bounds row, never stored) and widened, so
   // nothing waits for them before the merge
   constexpr int NE = (D + 64 * W - 1) / (64 * W);
-  uint32_t kn[NE], vn[NE];
-  {
+  uint32_t kn[NE] = {}, vn[NE] = {};
+  if constexpr (!SHARED) {
     const size_t src = ((size_t)s * Hkv + kvh) * D;
     const U* ks = static_cast<const U*>(p.k_new ? p.k_new : p.q) + src;
     const U* vs = static_cast<const U*>(p.v_new ? p.v_new : p.q) + src;
@@ -2331,7 +2354,7 @@ __global__ __launch_bounds__(64 * W) void merge_kernel(DecodeParams p) {
     }
   }
   // the slot's block-table entry is requested before the merge's loads
-  const int slot = (p.k_new && blockIdx.z == 0) ? new_token_slot(p, s, L) : -1;
+  const int slot = (!SHARED && p.k_new && blockIdx.z == 0) ? new_token_slot(p, s, L) : -1;
   if (p.merge) merge_sequence<D, W, SHARED>(p, sm, s, head0, nh, tid, L, meta);
   if (slot >= 0) {
     const int B = p.block_size, phys = slot / B, off = slot % B, Bs = v_subtile(B);
@@ -2497,7 +2520,9 @@ hipError_t launch_decode(const DecodeParams& p, int elem, int head_dim, int algo
   hipError_t e = hipLaunchKernel(fn, dim3(workers, (unsigned)p.num_kv_heads, 1), dim3(64, 1, 1), kargs,
                                  lens_bytes + slots * slot_bytes, stream);
   // the closing launch merges split sequences and stores the fused write
-  // (both done by the decode kernel itself when it has arrival counters)
+  // (both done by the decode kernel itself when it has arrival counters; in
+  // the shared mode the decode kernel stores the new tokens and this launch
+  // only merges)
   if (e != hipSuccess || p.ctr != nullptr || (!merge && !p.k_new)) return e;
   // few pieces per sequence: one wave per (sequence, KV head); many (fixed
   // partitions, or a balanced split of few sequences over many workers):
