@@ -87,8 +87,8 @@ _ORACLE_JOB = None
 
 
 def host_cores() -> int:
-    """Cores this process may run on, capped at 16 (one GPU's share of the
-    host on the GPU machines)."""
+    """Cores this process may run on, capped at 16 (one GPU's share of an
+    eight-GPU host's cores)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
