@@ -53,7 +53,7 @@ typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
 typedef enum pa_status {
   PA_OK = 0,
   PA_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, negative or inconsistent size */
-  PA_ERR_UNSUPPORTED = -2,  /* valid request this build does not implement */
+  PA_ERR_UNSUPPORTED = -2,  /* valid request this library does not implement */
   PA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required */
   PA_ERR_LAUNCH = -4        /* the HIP runtime reported an error at launch */
 } pa_status;

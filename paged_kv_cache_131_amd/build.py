@@ -91,8 +91,8 @@ def m0_violations(disassembly: str) -> list:
 
 
 def check_m0(obj: str, tmpdir: str) -> int:
-    """Disassemble the gfx950 code object inside `obj` (this build's
-    prompt-phase kernel) and raise if any instruction besides the inline
+    """Disassemble the gfx950 code object inside `obj` (the prompt-phase
+    kernel just compiled) and raise if any instruction besides the inline
     assembly's own M0 setting and direct-to-LDS loads touches M0. Returns
     the number of direct-to-LDS loads seen."""
     fatbin = os.path.join(tmpdir, "prefill.fatbin")
