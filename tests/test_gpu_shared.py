@@ -118,6 +118,50 @@ def test_shared_mode_fused_write_and_permutation():
         assert torch.equal(d2.decode(), first), f"permutation {seed}"
 
 
+def test_shared_mode_graph_replay_matches_eager():
+    """Three fused steps in shared mode (planning launches, the family decode
+    kernel storing the new tokens, the closing merge) captured in one graph
+    replay three times, with eager work and synchronizations between the
+    replays, to the eager steps' output and pools bit for bit."""
+    w = wl.make_forked_workload(cfg_of("bf16", 32, 8, 128, 16, index=54), GROUPS)
+    say("shared mode graph replay")
+    need = pb.pa_decode_workspace_bytes(len(w.context_lens), 32, 8, 128, w.max_context_len, SHARED)
+    eager, graphed, other = Dev(w), Dev(w), Dev(w)
+    ws_e, ws_g, ws_o = (torch.zeros(need, dtype=torch.uint8, device=DEV) for _ in range(3))
+    out_e = torch.empty(eager.q.shape, dtype=torch.float32, device=DEV)
+    out_g = torch.empty(eager.q.shape, dtype=torch.float32, device=DEV)
+
+    def step(d, ws, out):
+        pb.pa_write_decode(out, d.q, d.k_new, d.v_new, d.kc, d.vc, d.bt, d.cl, w.cfg.scale, w.max_context_len,
+                           partition_size=SHARED, workspace=ws)
+
+    for _ in range(3):
+        step(eager, ws_e, out_e)
+    torch.cuda.synchronize()
+    kr, vr = oracle.write_kv(w.k_cache, w.v_cache, w.k_new, w.v_new, w.slot_mapping, 16)
+    check(out_e, oracle.decode(w.q, kr, vr, w.block_tables, w.context_lens, w.cfg.scale, 16, "bf16"), "eager")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(graphed, ws_g, out_g)  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(3):
+            step(graphed, ws_g, out_g)
+    for r in range(3):
+        out_g.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        say(f"  replay {r}")
+        assert torch.equal(out_g, out_e), f"replay {r} differs from the eager steps"
+        for a, b in ((graphed.kc, eager.kc), (graphed.vc, eager.vc)):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"replay {r}: pools differ"
+        step(other, ws_o, torch.empty_like(out_e))  # eager work of the program between replays
+        torch.cuda.synchronize()
+
+
 def test_shared_mode_workspace_contents_do_not_matter():
     B = 16
     w = wl.make_forked_workload(cfg_of("bf16", 32, 8, 128, B, index=53), GROUPS)
