@@ -178,7 +178,9 @@ def test_prefill_full_size_sampled():
     assert np.all(np.isfinite(g))
     rng = np.random.default_rng(3)
     longest = int(np.argmax(w.context_lens))
-    rows = [(longest, 0), (longest, int(w.context_lens[longest]) - 1), (0, 0)]
+    rows = [(longest, int(w.context_lens[longest]) // 2)]
+    for s in range(w.cfg.num_seqs):  # every prompt's first and last query
+        rows += [(s, 0), (s, int(w.queries[s]) - 1)]
     for s in rng.choice(w.cfg.num_seqs, size=13, replace=False):
         n = int(w.queries[s])
         rows.append((int(s), int(rng.integers(0, n))))
@@ -191,6 +193,18 @@ def test_prefill_full_size_sampled():
                             np.array([p + 1], np.int32), w.cfg.scale, B, "bf16")
         check(got[row:row + 1], ref, f"seq {s} query {j} (position {p})", "bf16")
         check(got32[row:row + 1], ref, f"seq {s} query {j} (position {p}), fp32 out", "f32", pin=PIN)
+
+
+def test_prefill_full_size_unit_values():
+    """The full 32-prompt batch with V = 1 at every stored token (poison kept
+    in the padding): every output of every query and head is 1, which checks
+    the causal limit, the normalisation and the ring over all 40,920 rows."""
+    w = wl.make_prefill_workload()
+    ones = np.where(np.isnan(oracle.to_float64(w.v_cache, "bf16")), w.v_cache, np.uint16(0x3F80)).astype(np.uint16)
+    out = run_prefill(dataclasses.replace(w, v_cache=ones), "f32")
+    err = float((out - 1.0).abs().max())
+    say(f"prefill full size, unit values: max |o - 1| = {err:.3e} over {out.numel()} values")
+    assert err <= 2e-3 and err <= PIN
 
 
 @pytest.mark.parametrize("scale", [-0.3, 0.0, 2.5])
